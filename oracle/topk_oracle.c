@@ -1,0 +1,196 @@
+/*
+ * CPU oracle for exact per-row top-k selection.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct
+ * definition that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark may build, load
+ * or call it.  It shares no code, header or constant with the GPU library.
+ *
+ * What it computes (the plain definition of the selection the pages
+ * describe):
+ *   - "The Secret GPU Kernel Behind DeepSeek V4.1 Flash", transcript
+ *     2:40-3:05: keep the 512 biggest numbers of a list of up to a million
+ *     scores, by comparing and moving only (no arithmetic on the values).
+ *   - same transcript, 3:55-4:08: the selection keeps "the best 512"; the
+ *     threshold filter in front of it loses nothing, so the result is the
+ *     exact top-k of the row.
+ *   - kernelbench.com "DeepSeek V4.1 Flash", bitonic-selection paragraph:
+ *     values come back bit-exact and indices never repeat.
+ *
+ * Readings taken where the pages are silent (each is also listed in the
+ * design notes):
+ *   - Order of values: IEEE-754 total order restricted to non-NaN numbers,
+ *     i.e. -inf < negative finites < -0.0 < +0.0 < positive finites < +inf.
+ *     Plain float '>' calls -0.0 and +0.0 equal, so the zero pair is broken
+ *     by the sign bit explicitly.
+ *   - Ties (identical values): the lower index comes first.
+ *   - Row r holds positions [0, L) with L = clamp(lengths[r], 0, n), or
+ *     L = n when no lengths are given.  Positions >= L are never returned.
+ *   - Output row r has k slots: the first min(k, L) hold the selected
+ *     (value bits, index) pairs in the order above; the remaining slots hold
+ *     value -inf and index -1.
+ *   - NaN inside [0, L) is outside the contract: the oracle refuses the
+ *     input (returns ORACLE_ENAN) instead of inventing an order.
+ *
+ * Method: copy each row's (value, index) pairs, sort them with qsort under
+ * the comparator below (a strict total order, so the result does not depend
+ * on qsort's stability), emit the first min(k, L).  Rows are spread over
+ * POSIX threads; each row is sorted by exactly one thread.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+#define ORACLE_ENAN (-2)
+#define ORACLE_ENOMEM (-3)
+
+typedef struct {
+    float v;
+    int32_t i;
+} pair_t;
+
+/* 1 when a comes strictly before b in the value order (descending). */
+static int value_greater(float a, float b) {
+    if (a > b) return 1;
+    if (a < b) return 0;
+    /* a == b under float compare: only the zero pair is ordered by sign */
+    if (a == 0.0f && !signbit(a) && signbit(b)) return 1;
+    return 0;
+}
+
+/* qsort comparator: value descending, then index ascending. */
+static int pair_cmp(const void *pa, const void *pb) {
+    const pair_t *a = (const pair_t *)pa;
+    const pair_t *b = (const pair_t *)pb;
+    if (value_greater(a->v, b->v)) return -1;
+    if (value_greater(b->v, a->v)) return 1;
+    if (a->i < b->i) return -1;
+    if (a->i > b->i) return 1;
+    return 0;
+}
+
+static int64_t row_length(const int32_t *lengths, int64_t r, int64_t n) {
+    if (!lengths) return n;
+    int64_t L = lengths[r];
+    if (L < 0) L = 0;
+    if (L > n) L = n;
+    return L;
+}
+
+/* Selects one row; `work` has room for n pairs. */
+static int select_row(const float *row, int64_t L, int64_t k, float *out_v,
+                      int32_t *out_i, pair_t *work) {
+    for (int64_t j = 0; j < L; ++j) {
+        if (isnan(row[j])) return ORACLE_ENAN;
+        work[j].v = row[j];
+        work[j].i = (int32_t)j;
+    }
+    qsort(work, (size_t)L, sizeof(pair_t), pair_cmp);
+    int64_t m = L < k ? L : k;
+    for (int64_t j = 0; j < m; ++j) {
+        out_v[j] = work[j].v; /* a copy of the stored float: bits unchanged */
+        out_i[j] = work[j].i;
+    }
+    for (int64_t j = m; j < k; ++j) {
+        out_v[j] = -INFINITY;
+        out_i[j] = -1;
+    }
+    return ORACLE_OK;
+}
+
+typedef struct {
+    const float *scores;
+    const int32_t *lengths;
+    int64_t rows, n, k;
+    float *out_vals;
+    int32_t *out_idx;
+    int64_t r_begin, r_end;
+    int status;
+    int64_t bad_row;
+} job_t;
+
+static void *run_job(void *arg) {
+    job_t *jb = (job_t *)arg;
+    jb->status = ORACLE_OK;
+    jb->bad_row = -1;
+    if (jb->r_begin >= jb->r_end) return NULL;
+    pair_t *work = (pair_t *)malloc(sizeof(pair_t) * (size_t)(jb->n > 0 ? jb->n : 1));
+    if (!work) {
+        jb->status = ORACLE_ENOMEM;
+        return NULL;
+    }
+    for (int64_t r = jb->r_begin; r < jb->r_end; ++r) {
+        int64_t L = row_length(jb->lengths, r, jb->n);
+        int st = select_row(jb->scores + r * jb->n, L, jb->k, jb->out_vals + r * jb->k,
+                            jb->out_idx + r * jb->k, work);
+        if (st != ORACLE_OK) {
+            jb->status = st;
+            jb->bad_row = r;
+            break;
+        }
+    }
+    free(work);
+    return NULL;
+}
+
+/*
+ * scores:   host array [rows][n] (row stride n)
+ * lengths:  host array [rows] or NULL (then every row has length n)
+ * out_vals: host array [rows][k];  out_idx: host array [rows][k]
+ * nthreads: worker threads (<= 0 means 1)
+ * bad_row:  optional; receives the first row that held a NaN
+ * Returns ORACLE_OK, ORACLE_EINVAL, ORACLE_ENAN or ORACLE_ENOMEM.
+ */
+int oracle_topk(const float *scores, const int32_t *lengths, int64_t rows, int64_t n,
+                int64_t k, float *out_vals, int32_t *out_idx, int nthreads,
+                int64_t *bad_row) {
+    if (bad_row) *bad_row = -1;
+    if (rows < 0 || n < 0 || k < 1 || n > INT32_MAX) return ORACLE_EINVAL;
+    if (rows == 0) return ORACLE_OK;
+    if (!scores || !out_vals || !out_idx) return ORACLE_EINVAL;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > rows) nthreads = (int)rows;
+
+    job_t *jobs = (job_t *)calloc((size_t)nthreads, sizeof(job_t));
+    pthread_t *tids = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !tids) {
+        free(jobs);
+        free(tids);
+        return ORACLE_ENOMEM;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].scores = scores;
+        jobs[t].lengths = lengths;
+        jobs[t].rows = rows;
+        jobs[t].n = n;
+        jobs[t].k = k;
+        jobs[t].out_vals = out_vals;
+        jobs[t].out_idx = out_idx;
+        jobs[t].r_begin = rows * t / nthreads;
+        jobs[t].r_end = rows * (t + 1) / nthreads;
+    }
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&tids[t], NULL, run_job, &jobs[t]) != 0) break;
+        started = t;
+    }
+    run_job(&jobs[0]);
+    /* rows of threads that failed to start are done here, in order */
+    for (int t = started + 1; t < nthreads; ++t) run_job(&jobs[t]);
+    for (int t = 1; t <= started; ++t) pthread_join(tids[t], NULL);
+
+    int status = ORACLE_OK;
+    for (int t = 0; t < nthreads && status == ORACLE_OK; ++t) {
+        if (jobs[t].status != ORACLE_OK) {
+            status = jobs[t].status;
+            if (bad_row) *bad_row = jobs[t].bad_row;
+        }
+    }
+    free(jobs);
+    free(tids);
+    return status;
+}

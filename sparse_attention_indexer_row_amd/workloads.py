@@ -1,0 +1,138 @@
+"""Seeded synthetic score rows shaped like the indexer's selection workload.
+
+This module only draws random numbers.  It holds none of the selection
+arithmetic, imports neither the GPU binding nor the oracle, and is the one
+piece of code both sides' callers share.
+
+The rows stand in for indexer scores over a 16K-1M token context ("The Secret
+GPU Kernel Behind DeepSeek V4.1 Flash", transcript 1:48-3:05: each indexer
+query scores every cached position and 512 are kept; the built-in selection
+is measured from 16,000 to a million scores).  No public dataset or trained
+weights are involved.  Every array is drawn in float64 with numpy's PCG64 and
+rounded once to float32.
+
+Named workloads (rows x n, k):
+  small     4 x 16,384,   k=512   N(0,1)
+  outlier   64 x 131,072, k=512   N(0,1), 1% of positions per row from N(4,1)
+  one_row   1 x 1,048,576, k=512  N(0,1)  (one row: must be split over CUs)
+  adverse   128 x 1,048,576, k=512  even rows strictly ascending by position,
+                                    odd rows quantized to 256 levels
+  ragged    256 x 262,144, k=2048 lengths uniform in [1, 262,144], scores
+                                    N(0,1) + 0.5*log1p(position), -inf padding
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass
+class Workload:
+    name: str
+    scores: np.ndarray            # float32 [rows][n], C-contiguous
+    lengths: np.ndarray | None    # int32 [rows] or None (all rows full)
+    k: int
+    seed: int
+    description: str
+
+    @property
+    def rows(self) -> int:
+        return self.scores.shape[0]
+
+    @property
+    def n(self) -> int:
+        return self.scores.shape[1]
+
+    def valid_elements(self) -> int:
+        """Number of scores the selection must read: sum of row lengths."""
+        if self.lengths is None:
+            return self.rows * self.n
+        return int(np.clip(self.lengths.astype(np.int64), 0, self.n).sum())
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def normal_rows(rows: int, n: int, seed: int) -> np.ndarray:
+    return _rng(seed).standard_normal((rows, n)).astype(np.float32)
+
+
+def strictly_ascending(v: np.ndarray) -> np.ndarray:
+    """Sorted float32 row made strictly increasing by nudging repeats up one ulp."""
+    v = np.sort(v.astype(np.float32))
+    while True:
+        bad = np.nonzero(v[1:] <= v[:-1])[0]
+        if bad.size == 0:
+            return v
+        v[bad + 1] = np.nextafter(v[bad], np.float32(np.inf))
+
+
+def quantized_levels(x: np.ndarray) -> np.ndarray:
+    """256 levels q/32 with q = clip(floor(32 x), -128, 127) (no -0.0 possible)."""
+    q = np.clip(np.floor(32.0 * x), -128, 127).astype(np.int64)
+    return (q.astype(np.float64) / 32.0).astype(np.float32)
+
+
+def small(seed: int = 101) -> Workload:
+    return Workload("small", normal_rows(4, 16384, seed), None, 512, seed,
+                    "4 rows x 16,384 fp32 N(0,1), k=512")
+
+
+def outlier(seed: int = 102, rows: int = 64, n: int = 131072) -> Workload:
+    g = _rng(seed)
+    x = g.standard_normal((rows, n))
+    m = int(round(0.01 * n))
+    for r in range(rows):
+        pos = g.choice(n, size=m, replace=False)
+        x[r, pos] = g.normal(4.0, 1.0, size=m)
+    return Workload("outlier", x.astype(np.float32), None, 512, seed,
+                    f"{rows} rows x {n:,} fp32 N(0,1) with {m} positions/row from N(4,1), k=512")
+
+
+def one_row(seed: int = 103, n: int = 1 << 20) -> Workload:
+    return Workload("one_row", normal_rows(1, n, seed), None, 512, seed,
+                    f"1 row x {n:,} fp32 N(0,1), k=512")
+
+
+def adverse(seed: int = 104, rows: int = 128, n: int = 1 << 20) -> Workload:
+    g = _rng(seed)
+    out = np.empty((rows, n), dtype=np.float32)
+    for r in range(rows):
+        x = g.standard_normal(n)
+        if r % 2 == 0:
+            out[r] = strictly_ascending(x.astype(np.float32))
+        else:
+            out[r] = quantized_levels(x)
+    return Workload("adverse", out, None, 512, seed,
+                    f"{rows} rows x {n:,} fp32, k=512; even rows strictly ascending, "
+                    "odd rows quantized to 256 levels")
+
+
+def ragged(seed: int = 105, rows: int = 256, n: int = 262144, k: int = 2048) -> Workload:
+    g = _rng(seed)
+    lengths = g.integers(1, n, size=rows, endpoint=True).astype(np.int32)
+    out = np.full((rows, n), -np.inf, dtype=np.float32)
+    pos = np.arange(n, dtype=np.float64)
+    trend = 0.5 * np.log1p(pos)
+    for r in range(rows):
+        L = int(lengths[r])
+        out[r, :L] = (g.standard_normal(L) + trend[:L]).astype(np.float32)
+    return Workload("ragged", out, lengths, k, seed,
+                    f"{rows} ragged rows, lengths uniform in [1, {n:,}], padded to {n:,} "
+                    f"with -inf, scores N(0,1)+0.5*log1p(position), k={k}")
+
+
+WORKLOADS = {
+    "small": small,
+    "outlier": outlier,
+    "one_row": one_row,
+    "adverse": adverse,
+    "ragged": ragged,
+}
+
+
+def make(name: str, **kw) -> Workload:
+    return WORKLOADS[name](**kw)

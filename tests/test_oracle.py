@@ -1,0 +1,157 @@
+"""Pins the CPU oracle to facts that do not come from the oracle itself.
+
+Runs on the CPU only.  See ``oracle_pins`` for the sources of truth.
+"""
+
+import os
+import subprocess
+import sys
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+from sparse_attention_indexer_row_amd import workloads
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _topk(scores, k, lengths):
+    return oracle.topk(scores, k, lengths, threads=4)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(_topk)
+
+
+def _check_invariants(scores, lengths, k, vals, idx):
+    """Properties every correct top-k output has, checked without re-sorting."""
+    rows, n = scores.shape
+    key_all = oracle_pins.total_order_key(scores)
+    for r in range(rows):
+        L = n if lengths is None else int(np.clip(lengths[r], 0, n))
+        m = min(k, L)
+        assert np.all(idx[r, m:] == -1)
+        assert np.all(np.isneginf(vals[r, m:]))
+        sel = idx[r, :m]
+        assert np.all((sel >= 0) & (sel < L)), "index outside the row's valid range"
+        assert np.unique(sel).size == m, "an index repeats"
+        assert np.array_equal(oracle_pins.bits_of(vals[r, :m]), oracle_pins.bits_of(scores[r, sel]))
+        key = key_all[r, sel].astype(np.int64)
+        # sorted: key descending, equal keys by index ascending
+        dk = np.diff(key)
+        assert np.all(dk <= 0)
+        assert np.all(np.diff(sel)[dk == 0] > 0)
+        if m < L:
+            mask = np.ones(L, dtype=bool)
+            mask[sel] = False
+            rest = key_all[r, :L][mask].astype(np.int64)
+            kmin = key[-1]
+            assert rest.max() <= kmin, "an excluded value beats the smallest kept one"
+            # an excluded value equal to the boundary value has a higher index
+            tied = np.nonzero(mask)[0][rest == kmin]
+            assert np.all(tied > sel[-1])
+
+
+@pytest.mark.parametrize("name", ["small", "outlier_small", "adverse_small", "ragged_small"])
+def test_invariants_on_workload_shapes(name):
+    if name == "small":
+        w = workloads.small()
+    elif name == "outlier_small":
+        w = workloads.outlier(rows=6, n=20000)
+    elif name == "adverse_small":
+        w = workloads.adverse(rows=6, n=30000)
+    else:
+        w = workloads.ragged(rows=12, n=9000, k=700)
+    vals, idx = oracle.topk(w.scores, w.k, w.lengths)
+    _check_invariants(w.scores, w.lengths, w.k, vals, idx)
+
+
+def test_thread_count_does_not_change_result():
+    w = workloads.ragged(rows=9, n=5000, k=300, seed=3)
+    a = oracle.topk(w.scores, w.k, w.lengths, threads=1)
+    b = oracle.topk(w.scores, w.k, w.lengths, threads=7)
+    assert np.array_equal(a[1], b[1])
+    assert np.array_equal(oracle_pins.bits_of(a[0]), oracle_pins.bits_of(b[0]))
+
+
+def test_quantized_rows_match_integer_key_route():
+    # many ties at the boundary level: checked against the independent key route
+    x = workloads.quantized_levels(np.random.default_rng(5).standard_normal((3, 4096)))
+    vals, idx = oracle.topk(x, 200)
+    for r in range(3):
+        ev, ei = oracle_pins.expected_by_key(x[r], 4096, 200)
+        assert np.array_equal(idx[r], ei)
+
+
+def test_nan_is_rejected():
+    x = np.zeros((3, 10), dtype=np.float32)
+    x[2, 4] = np.nan
+    with pytest.raises(oracle.OracleNaN):
+        oracle.topk(x, 3)
+    # NaN beyond a row's length is never looked at
+    vals, idx = oracle.topk(x, 3, np.array([10, 10, 4], dtype=np.int32))
+    assert idx[2].tolist() == [0, 1, 2]
+
+
+def test_bad_arguments():
+    lib = oracle._get()
+    assert lib.oracle_topk(None, None, 1, 4, 1, None, None, 1, None) == oracle.EINVAL
+    assert lib.oracle_topk(None, None, 0, 4, 1, None, None, 1, None) == oracle.OK
+    x = np.zeros((1, 4), dtype=np.float32)
+    o = np.zeros(4, dtype=np.float32)
+    i = np.zeros(4, dtype=np.int32)
+    assert lib.oracle_topk(x.ctypes.data, None, 1, 4, 0, o.ctypes.data, i.ctypes.data, 1,
+                           None) == oracle.EINVAL
+
+
+# Planted mistakes: each replaces one piece of the oracle's source; the pins
+# above must reject every one of them.
+MUTANTS = {
+    "ties_to_higher_index": (
+        "if (a->i < b->i) return -1;\n    if (a->i > b->i) return 1;",
+        "if (a->i < b->i) return 1;\n    if (a->i > b->i) return -1;"),
+    "zeros_unordered": (
+        "if (a == 0.0f && !signbit(a) && signbit(b)) return 1;", ""),
+    "zeros_reversed": (
+        "if (a == 0.0f && !signbit(a) && signbit(b)) return 1;",
+        "if (a == 0.0f && signbit(a) && !signbit(b)) return 1;"),
+    "ascending_values": (
+        "if (a > b) return 1;\n    if (a < b) return 0;",
+        "if (a < b) return 1;\n    if (a > b) return 0;"),
+    "filler_index_zero": ("out_i[j] = -1;", "out_i[j] = 0;"),
+    "filler_value_zero": ("out_v[j] = -INFINITY;", "out_v[j] = 0.0f;"),
+    "length_not_clamped_high": ("if (L > n) L = n;", ""),
+    "length_not_clamped_low": ("if (L < 0) L = 0;", ""),
+    "off_by_one_count": ("int64_t m = L < k ? L : k;", "int64_t m = L < k ? L : k - 1;"),
+    "wrong_index_recorded": ("work[j].i = (int32_t)j;", "work[j].i = (int32_t)(L - 1 - j);"),
+    "lengths_ignored": ("if (!lengths) return n;", "if (lengths || !lengths) return n;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    old, new = MUTANTS[name]
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib = os.path.join(d, "libmutant.so")
+        oracle.build(path, lib)
+        p = subprocess.run([sys.executable, os.path.join(HERE, "_oracle_mutant_runner.py"), lib],
+                           capture_output=True, text=True, timeout=300)
+    assert p.returncode != 0, f"mutant {name} passed every pin:\n{p.stdout}"
+
+
+def test_unmutated_oracle_passes_runner():
+    with tempfile.TemporaryDirectory() as d:
+        lib = os.path.join(d, "liboracle.so")
+        oracle.build(oracle._SRC, lib)
+        p = subprocess.run([sys.executable, os.path.join(HERE, "_oracle_mutant_runner.py"), lib],
+                           capture_output=True, text=True, timeout=300)
+    assert p.returncode == 0, p.stdout + p.stderr
