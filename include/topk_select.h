@@ -1,0 +1,171 @@
+/*
+ * topk_select.h -- exact per-row top-k selection on MI355X (gfx950).
+ *
+ * The operation ("The Secret GPU Kernel Behind DeepSeek V4.1 Flash",
+ * transcript 2:40-4:20): for each query row of indexer scores, keep the k
+ * largest of up to about a million fp32 scores and return their values and
+ * positions.  The row is read once, in 1,024-element blocks visited in a
+ * shuffled order drawn without looking at the data (3:30, 4:55-5:10); each
+ * score meets one comparison against a threshold that only rises (3:18-4:08);
+ * survivors go to a small tray that is sorted only when it passes its mark,
+ * keeping the best k (3:55-4:08).  When there are too few rows to fill the
+ * chip, one row is split across several compute units that each keep a local
+ * top-k and a leader merges them (5:22-5:33).  Values come back bit-exact and
+ * indices never repeat because every score travels as one 64-bit word holding
+ * an order-preserving key above its index (kernelbench.com "DeepSeek V4.1
+ * Flash", bitonic-selection paragraph).
+ *
+ * Result (identical for every schedule, seed and split):
+ *   Row r holds positions [0, L_r), L_r = clamp(lengths[r], 0, n), or n when
+ *   `lengths` is NULL.  Output row r has k slots.  The first min(k, L_r) hold
+ *   the selected scores and their positions, ordered by value descending in
+ *   IEEE-754 total order (-0.0 below +0.0), equal values by lower position.
+ *   The remaining slots hold value -inf and index -1.  Values are bit copies
+ *   of the input.  Positions >= L_r are never read or returned.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller.
+ *   - scores: fp32 [rows][n], row r starts at scores + r*n (any 4-byte
+ *     alignment).  out_vals: fp32 [rows][k].  out_idx: int32 [rows][k].
+ *     lengths: int32 [rows] or NULL.  Offsets are computed in 64 bits.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Calls are asynchronous and stream-ordered.
+ *   - Arguments are checked on the host before any HIP call.  On an argument
+ *     error the call returns a negative status, launches nothing and writes
+ *     nothing.  rows == 0 returns TOPK_OK and does nothing.
+ *   - Device data is never an error: lengths outside [0, n] are clamped.
+ *     NaN scores are a precondition violation: the output is then
+ *     unspecified, but the call stays memory-safe and terminates.
+ *   - A failed launch (hipGetLastError right after it) returns TOPK_ELAUNCH.
+ */
+#ifndef TOPK_SELECT_H
+#define TOPK_SELECT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define TOPK_OK 0
+#define TOPK_EINVAL (-1)     /* null pointer, rows < 0, n < 1, bad option    */
+#define TOPK_EK_RANGE (-2)   /* k < 1 or k > TOPK_MAX_K                       */
+#define TOPK_EWORKSPACE (-3) /* workspace missing, misaligned or too small    */
+#define TOPK_ESPLIT (-4)     /* split outside [0, TOPK_MAX_SPLIT]             */
+#define TOPK_ELAUNCH (-5)    /* the HIP launch failed                         */
+#define TOPK_EDEVICE (-6)    /* no usable gfx950 device / runtime query failed */
+#define TOPK_EALLOC (-7)     /* library-owned workspace allocation failed     */
+
+/* Largest supported k (the pages' own kernel stops near 4,000). */
+#define TOPK_MAX_K 2048
+/* Largest number of workgroups one row may be split across. */
+#define TOPK_MAX_SPLIT 1024
+
+/*
+ * topk_select -- top-k of every row, planned automatically.
+ *
+ * Chooses one workgroup per row or, when rows alone cannot fill the GPU,
+ * splits each row across several workgroups (transcript 5:22-5:33).  A split
+ * call uses a library-owned, grow-only workspace per device, allocated with
+ * hipMalloc on the first call that needs a larger one (so the first such call
+ * is not graph-capturable; use topk_select_split for capture).  Calls that
+ * share this internal workspace must be ordered on one stream.
+ */
+int topk_select(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
+                int32_t k, float *out_vals, int32_t *out_idx, void *stream);
+
+/*
+ * topk_split_workspace_bytes -- device bytes topk_select_split needs.
+ * `split` == 0 means the automatic choice.  Returns 0 for invalid arguments.
+ * The workspace holds per-row threshold and ticket words and one k-list per
+ * (row, split) pair.
+ */
+size_t topk_split_workspace_bytes(int32_t rows, int32_t n, int32_t k, int32_t split);
+
+/*
+ * topk_workspace_init -- zero a caller-owned workspace once, before its first
+ * use, with a fill kernel on `stream` (no memset node, so it can be captured).
+ * The split path leaves the workspace zeroed again at the end of every call.
+ * `workspace` must be 256-byte aligned.
+ */
+int topk_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * topk_select_split -- top-k with each row split across `split` workgroups
+ * (0 = automatic, 1 = no split).  Each workgroup keeps a local top-k of its
+ * share of the row's blocks; workgroups of a row share a rising threshold
+ * through the workspace; the last to finish (elected by an atomic ticket)
+ * merges the local lists and writes the row's output.  `workspace` is
+ * caller-owned device memory of at least topk_split_workspace_bytes(...),
+ * 256-byte aligned, zeroed once by topk_workspace_init.  Allocates nothing.
+ * Two calls that use one workspace must not run concurrently.
+ */
+int topk_select_split(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
+                      int32_t k, float *out_vals, int32_t *out_idx, int32_t split,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Tuning and instrumentation knobs.  Zero fields take the defaults. */
+typedef struct {
+    uint64_t seed;           /* visit-order seed; the result never depends on it */
+    int32_t split;           /* workgroups per row; 0 = automatic                */
+    int32_t waves;           /* waves per workgroup, 2..4: one sorts, the rest stream */
+    int32_t watermark;       /* tray words that trigger a sort; 0 = default      */
+    int32_t reserved;
+    /* Optional device array [rows][2] of uint64, accumulated into (zero it
+     * first): [0] scores that entered a tray (the only ones ever sorted),
+     * [1] sort passes run.  NULL turns the counters off. */
+    unsigned long long *stats;
+} topk_options;
+
+/*
+ * topk_select_ex -- topk_select_split with explicit options.  `workspace`
+ * may be NULL when the plan has split == 1.
+ */
+int topk_select_ex(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
+                   int32_t k, float *out_vals, int32_t *out_idx, const topk_options *opts,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* The plan a call would use (host only, no launch). */
+typedef struct {
+    int32_t split;           /* workgroups per row                      */
+    int32_t waves;           /* waves per workgroup                     */
+    int32_t list_words;      /* kept-list capacity: k rounded up to 64*2^j */
+    int32_t watermark;       /* tray words that trigger a sort          */
+    int32_t tray_words;      /* tray capacity per wave                  */
+    int32_t lds_bytes;       /* dynamic LDS per workgroup               */
+    int32_t compute_units;   /* compute units the plan assumed          */
+    int32_t reserved;
+    size_t workspace_bytes;  /* 0 when split == 1                       */
+} topk_plan_t;
+
+int topk_plan(int32_t rows, int32_t n, int32_t k, const topk_options *opts, topk_plan_t *out);
+
+/* Human-readable text for a status code (static storage). */
+const char *topk_strerror(int status);
+
+/*
+ * topk_visit_order -- host-side copy of the block visit order for row `row`
+ * of a row with `nblocks` 1,024-element blocks: out[p] = block visited at
+ * step p.  A diagnostic for tests; it is the same function the kernel uses.
+ */
+int topk_visit_order(uint64_t seed, int32_t row, int32_t nblocks, int32_t *out);
+
+/*
+ * Streaming probes used to measure the machine, not part of the selection:
+ * topk_probe_read reads `bytes` (multiple of 16) from `src` once with the
+ * selection kernel's load pattern and writes one word per workgroup into
+ * `sink` (at least topk_probe_sink_words(bytes) uint32 words), so the read
+ * cannot be elided.  topk_probe_copy copies `bytes` (multiple of 16) from src
+ * to dst.  Both return TOPK_OK or an error status.
+ */
+size_t topk_probe_sink_words(size_t bytes);
+int topk_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+int topk_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPK_SELECT_H */

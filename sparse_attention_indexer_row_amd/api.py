@@ -1,0 +1,179 @@
+"""Python binding of the C ABI, for PyTorch device tensors.
+
+Argument marshalling only: each function checks tensor placement, dtype and
+layout, passes raw device pointers and the current HIP stream to the library,
+and raises ``TopkError`` on a non-zero status.  Every step of the selection
+runs in the library's HIP kernels.  Names follow include/topk_select.h.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import TopkError, TopkOptions, TopkPlan  # noqa: F401
+
+
+def _stream_handle(stream, device) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return int(s.cuda_stream)
+
+
+def _check_scores(scores: torch.Tensor):
+    if not isinstance(scores, torch.Tensor) or scores.dim() != 2:
+        raise ValueError("scores must be a 2-D tensor [rows][n]")
+    if scores.dtype != torch.float32:
+        raise ValueError("scores must be float32")
+    if not scores.is_cuda:
+        raise ValueError("scores must be a GPU tensor")
+    if not scores.is_contiguous():
+        raise ValueError("scores must be contiguous (row stride n)")
+
+
+def _check_lengths(lengths, scores):
+    if lengths is None:
+        return None
+    if lengths.dtype != torch.int32 or lengths.device != scores.device:
+        raise ValueError("lengths must be int32 on the scores' device")
+    if lengths.shape != (scores.shape[0],) or not lengths.is_contiguous():
+        raise ValueError("lengths must be a contiguous [rows] tensor")
+    return lengths.data_ptr()
+
+
+def _outputs(scores, k, out):
+    rows = scores.shape[0]
+    if out is None:
+        vals = torch.empty((rows, k), dtype=torch.float32, device=scores.device)
+        idx = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+        return vals, idx
+    vals, idx = out
+    if vals.shape != (rows, k) or idx.shape != (rows, k):
+        raise ValueError("out tensors must be [rows][k]")
+    if vals.dtype != torch.float32 or idx.dtype != torch.int32:
+        raise ValueError("out tensors must be float32 and int32")
+    if vals.device != scores.device or idx.device != scores.device:
+        raise ValueError("out tensors must be on the scores' device")
+    if not (vals.is_contiguous() and idx.is_contiguous()):
+        raise ValueError("out tensors must be contiguous")
+    return vals, idx
+
+
+def topk_select(scores: torch.Tensor, k: int, lengths: torch.Tensor | None = None,
+                out=None, stream=None):
+    """Top-k (values, int32 indices) of every row of ``scores`` [rows][n]."""
+    _check_scores(scores)
+    lp = _check_lengths(lengths, scores)
+    vals, idx = _outputs(scores, k, out)
+    rows, n = scores.shape
+    st = _lib.load().topk_select(scores.data_ptr(), lp, rows, n, k, vals.data_ptr(),
+                                 idx.data_ptr(), _stream_handle(stream, scores.device))
+    _lib.check(st, "topk_select")
+    return vals, idx
+
+
+def topk_split_workspace_bytes(rows: int, n: int, k: int, split: int = 0) -> int:
+    return int(_lib.load().topk_split_workspace_bytes(rows, n, k, split))
+
+
+def topk_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size()
+    _lib.check(_lib.load().topk_workspace_init(workspace.data_ptr(), nbytes,
+                                               _stream_handle(stream, workspace.device)),
+               "topk_workspace_init")
+
+
+def new_workspace(rows: int, n: int, k: int, split: int = 0, device="cuda") -> torch.Tensor:
+    """Allocates and zeroes a workspace for topk_select_split (uint8 tensor)."""
+    nbytes = topk_split_workspace_bytes(rows, n, k, split)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("workspace allocation is not 256-byte aligned")
+    topk_workspace_init(ws)
+    return ws
+
+
+def topk_select_split(scores: torch.Tensor, k: int, split: int, workspace: torch.Tensor,
+                      lengths: torch.Tensor | None = None, out=None, stream=None):
+    _check_scores(scores)
+    lp = _check_lengths(lengths, scores)
+    vals, idx = _outputs(scores, k, out)
+    rows, n = scores.shape
+    st = _lib.load().topk_select_split(
+        scores.data_ptr(), lp, rows, n, k, vals.data_ptr(), idx.data_ptr(), split,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream, scores.device))
+    _lib.check(st, "topk_select_split")
+    return vals, idx
+
+
+def _options(seed=0, split=0, waves=0, watermark=0, stats=None) -> TopkOptions:
+    o = TopkOptions()
+    o.seed = seed
+    o.split = split
+    o.waves = waves
+    o.watermark = watermark
+    o.reserved = 0
+    o.stats = stats.data_ptr() if stats is not None else None
+    return o
+
+
+def topk_select_ex(scores: torch.Tensor, k: int, lengths: torch.Tensor | None = None, *,
+                   seed: int = 0, split: int = 0, waves: int = 0, watermark: int = 0,
+                   stats: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   out=None, stream=None):
+    """Selection with explicit options.  ``stats``: int64 [rows][2] to accumulate into."""
+    _check_scores(scores)
+    lp = _check_lengths(lengths, scores)
+    vals, idx = _outputs(scores, k, out)
+    rows, n = scores.shape
+    if stats is not None and (stats.dtype != torch.int64 or stats.shape != (rows, 2)
+                              or stats.device != scores.device or not stats.is_contiguous()):
+        raise ValueError("stats must be a contiguous int64 [rows][2] tensor on the device")
+    o = _options(seed, split, waves, watermark, stats)
+    wp = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.load().topk_select_ex(scores.data_ptr(), lp, rows, n, k, vals.data_ptr(),
+                                    idx.data_ptr(), ctypes.byref(o), wp, wb,
+                                    _stream_handle(stream, scores.device))
+    _lib.check(st, "topk_select_ex")
+    return vals, idx
+
+
+def topk_plan(rows: int, n: int, k: int, *, split: int = 0, waves: int = 0,
+              watermark: int = 0) -> dict:
+    o = _options(0, split, waves, watermark, None)
+    p = TopkPlan()
+    _lib.check(_lib.load().topk_plan(rows, n, k, ctypes.byref(o), ctypes.byref(p)), "topk_plan")
+    return {f: getattr(p, f) for f, _ in TopkPlan._fields_ if f != "reserved"}
+
+
+def topk_strerror(status: int) -> str:
+    return _lib.load().topk_strerror(status).decode()
+
+
+def topk_visit_order(seed: int, row: int, nblocks: int) -> np.ndarray:
+    out = np.empty(max(nblocks, 1), dtype=np.int32)
+    _lib.check(_lib.load().topk_visit_order(seed, row, nblocks, out.ctypes.data),
+               "topk_visit_order")
+    return out[:nblocks]
+
+
+def topk_probe_read(src: torch.Tensor, sink: torch.Tensor | None = None, stream=None):
+    nbytes = src.numel() * src.element_size()
+    words = int(_lib.load().topk_probe_sink_words(nbytes))
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=src.device)
+    _lib.check(_lib.load().topk_probe_read(src.data_ptr(), nbytes, sink.data_ptr(),
+                                           _stream_handle(stream, src.device)), "topk_probe_read")
+    return sink
+
+
+def topk_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    _lib.check(_lib.load().topk_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                                           _stream_handle(stream, src.device)), "topk_probe_copy")

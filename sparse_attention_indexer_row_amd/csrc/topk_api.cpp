@@ -1,0 +1,314 @@
+// C ABI of the selection library: argument checks, planning, workspace,
+// launch.  Every argument is checked before the first HIP call, so an
+// argument error never touches the device.
+#include "../../include/topk_select.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "common.h"
+#include "internal.h"
+
+namespace {
+
+using topk::kBlock;
+using topk::kWave;
+
+constexpr size_t kAlign = 256;
+constexpr int kDefaultWaves = 4;      // three streamer waves and one sorter wave
+constexpr int kDefaultWatermark = 512;
+constexpr int kMaxDevices = 64;
+constexpr int kAssumedCUs = 256;  // MI355X, used only when no device can be queried
+constexpr int64_t kMaxGroupsPerLaunch = (int64_t)1 << 22;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int list_multiplier(int32_t k) {  // E: list capacity 64*E >= k
+    int e = 1;
+    while (64 * e < k) e *= 2;
+    return e;
+}
+
+struct Plan {
+    int E, waves, split, watermark, tray, cus;
+    size_t lds, ws_bytes;
+    size_t off_lists;
+};
+
+// Workspace: per-row 16-byte control records (threshold word, ticket) at
+// the front, then the per-(row, split) kept lists.  Every call leaves all of
+// it zero again, so one zeroed buffer serves calls of any shape.
+size_t workspace_layout(int64_t rows, int split, int list_words, size_t *off_lists) {
+    const size_t ctrl = align_up((size_t)rows * 16, kAlign);
+    const size_t lists = (size_t)rows * (size_t)split * (size_t)list_words * 8;
+    if (off_lists) *off_lists = ctrl;
+    return ctrl + lists;
+}
+
+int device_cus(int *cus) {
+    static int cached[kMaxDevices] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TOPK_EDEVICE;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            return TOPK_EDEVICE;
+        cached[dev] = v;
+    }
+    *cus = cached[dev];
+    return TOPK_OK;
+}
+
+bool misaligned(const void *p, size_t a) { return ((uintptr_t)p % a) != 0; }
+
+// Argument checks shared by every selection entry point (no HIP calls).
+int check_args(const float *scores, int32_t rows, int32_t n, int32_t k, const float *out_vals,
+               const int32_t *out_idx, const int32_t *lengths) {
+    if (rows < 0 || n < 1) return TOPK_EINVAL;
+    if (k < 1 || k > TOPK_MAX_K) return TOPK_EK_RANGE;
+    if (rows == 0) return TOPK_OK;
+    if (!scores || !out_vals || !out_idx) return TOPK_EINVAL;
+    if (misaligned(scores, 4) || misaligned(out_vals, 4) || misaligned(out_idx, 4) ||
+        (lengths && misaligned(lengths, 4)))
+        return TOPK_EINVAL;
+    return TOPK_OK;
+}
+
+int check_options(const topk_options *o) {
+    if (!o) return TOPK_OK;
+    if (o->split < 0 || o->split > TOPK_MAX_SPLIT) return TOPK_ESPLIT;
+    if (o->waves != 0 && (o->waves < 2 || o->waves > topk::kMaxWaves)) return TOPK_EINVAL;
+    if (o->watermark < 0 || o->watermark > 4096) return TOPK_EINVAL;
+    return TOPK_OK;
+}
+
+// Plans a call.  `cus` is the compute-unit count to plan for.
+Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cus) {
+    Plan p{};
+    p.cus = cus;
+    p.E = list_multiplier(k);
+    const int list_words = 64 * p.E;
+    p.waves = (o && o->waves) ? o->waves : kDefaultWaves;
+    p.watermark = (o && o->watermark) ? o->watermark : kDefaultWatermark;
+    if (p.watermark < 64) p.watermark = 64;
+    p.tray = p.watermark + kBlock;  // a tray below the mark never overflows in one block
+    const int streamers = p.waves - 1;
+    p.lds = (size_t)8 * (size_t)(2 * streamers * p.tray);
+
+    if (o && o->split) {
+        p.split = o->split;
+    } else {
+        // Enough workgroups for about two per compute unit, but at least four
+        // blocks per wave so every stream does real work.
+        const int64_t nb = ((int64_t)n + 3 + kBlock - 1) / kBlock;
+        const int64_t target = 2 * (int64_t)cus;
+        int64_t s = rows > 0 ? (target + rows - 1) / rows : 1;
+        int64_t cap = nb / (4 * (int64_t)streamers);
+        if (cap < 1) cap = 1;
+        if (s > cap) s = cap;
+        if (s > TOPK_MAX_SPLIT) s = TOPK_MAX_SPLIT;
+        if (s < 1) s = 1;
+        p.split = (int)s;
+    }
+    p.ws_bytes = p.split > 1 ? workspace_layout(rows, p.split, list_words, &p.off_lists) : 0;
+    return p;
+}
+
+int run(const float *scores, const int32_t *lengths, int32_t rows, int32_t n, int32_t k,
+        float *out_vals, int32_t *out_idx, const Plan &pl, void *ws, uint64_t seed,
+        unsigned long long *stats, hipStream_t stream) {
+    topk::SelectArgs a{};
+    a.scores = scores;
+    a.lengths = lengths;
+    a.n = n;
+    a.k = k;
+    a.split = pl.split;
+    a.watermark = pl.watermark;
+    a.tray_words = pl.tray;
+    a.out_vals = out_vals;
+    a.out_idx = out_idx;
+    a.stats = stats;
+    a.seed = seed;
+    if (pl.split > 1) {
+        char *base = static_cast<char *>(ws);
+        a.ws_ctrl = reinterpret_cast<uint64_t *>(base);
+        a.ws_lists = reinterpret_cast<uint64_t *>(base + pl.off_lists);
+    }
+    // Keep each launch's work-item count well inside 32 bits.
+    const int64_t rows_per_launch = kMaxGroupsPerLaunch / pl.split > 0 ? kMaxGroupsPerLaunch / pl.split : 1;
+    for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
+        const int64_t nr = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
+        a.row0 = (int32_t)r0;
+        a.rows = (int32_t)nr;
+        if (topk::launch_select(a, pl.E, pl.waves, pl.lds, stream) != hipSuccess)
+            return TOPK_ELAUNCH;
+    }
+    return TOPK_OK;
+}
+
+// Library-owned workspace for topk_select: one grow-only buffer per device.
+std::mutex g_ws_mutex;
+void *g_ws[kMaxDevices] = {nullptr};
+size_t g_ws_bytes[kMaxDevices] = {0};
+
+int internal_workspace(size_t need, hipStream_t stream, void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TOPK_EDEVICE;
+    std::lock_guard<std::mutex> g(g_ws_mutex);
+    if (g_ws_bytes[dev] < need) {
+        if (g_ws[dev]) {
+            if (hipDeviceSynchronize() != hipSuccess) return TOPK_EDEVICE;
+            (void)hipFree(g_ws[dev]);
+            g_ws[dev] = nullptr;
+            g_ws_bytes[dev] = 0;
+        }
+        size_t bytes = align_up(need, (size_t)1 << 20);
+        void *p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess) return TOPK_EALLOC;
+        if (topk::launch_fill_zero(p, bytes, stream) != hipSuccess) {
+            (void)hipFree(p);
+            return TOPK_ELAUNCH;
+        }
+        g_ws[dev] = p;
+        g_ws_bytes[dev] = bytes;
+    }
+    *out = g_ws[dev];
+    return TOPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int topk_plan(int32_t rows, int32_t n, int32_t k, const topk_options *opts, topk_plan_t *out) {
+    if (!out) return TOPK_EINVAL;
+    if (rows < 0 || n < 1) return TOPK_EINVAL;
+    if (k < 1 || k > TOPK_MAX_K) return TOPK_EK_RANGE;
+    int st = check_options(opts);
+    if (st != TOPK_OK) return st;
+    int cus = kAssumedCUs;
+    int dev_cus = 0;
+    int count = 0;
+    if (hipGetDeviceCount(&count) == hipSuccess && count > 0 && device_cus(&dev_cus) == TOPK_OK)
+        cus = dev_cus;
+    Plan p = make_plan(rows, n, k, opts, cus);
+    out->split = p.split;
+    out->waves = p.waves;
+    out->list_words = 64 * p.E;
+    out->watermark = p.watermark;
+    out->tray_words = p.tray;
+    out->lds_bytes = (int32_t)p.lds;
+    out->compute_units = p.cus;
+    out->reserved = 0;
+    out->workspace_bytes = p.ws_bytes;
+    return TOPK_OK;
+}
+
+size_t topk_split_workspace_bytes(int32_t rows, int32_t n, int32_t k, int32_t split) {
+    if (rows < 0 || n < 1 || k < 1 || k > TOPK_MAX_K || split < 0 || split > TOPK_MAX_SPLIT)
+        return 0;
+    topk_options o{};
+    o.split = split;
+    topk_plan_t pl;
+    if (topk_plan(rows, n, k, &o, &pl) != TOPK_OK) return 0;
+    return pl.workspace_bytes;
+}
+
+int topk_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
+    if (!workspace || misaligned(workspace, kAlign)) return TOPK_EWORKSPACE;
+    if (workspace_bytes == 0) return TOPK_OK;
+    if (workspace_bytes % 16 != 0) return TOPK_EWORKSPACE;
+    return topk::launch_fill_zero(workspace, workspace_bytes, (hipStream_t)stream) == hipSuccess
+               ? TOPK_OK
+               : TOPK_ELAUNCH;
+}
+
+int topk_select_ex(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
+                   int32_t k, float *out_vals, int32_t *out_idx, const topk_options *opts,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    int st = check_args(scores, rows, n, k, out_vals, out_idx, lengths);
+    if (st != TOPK_OK) return st;
+    st = check_options(opts);
+    if (st != TOPK_OK) return st;
+    if (workspace && misaligned(workspace, kAlign)) return TOPK_EWORKSPACE;
+    if (rows == 0) return TOPK_OK;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != TOPK_OK) return st;
+    Plan pl = make_plan(rows, n, k, opts, cus);
+    if (pl.split > 1 && (!workspace || workspace_bytes < pl.ws_bytes)) return TOPK_EWORKSPACE;
+    return run(scores, lengths, rows, n, k, out_vals, out_idx, pl, workspace,
+               opts ? opts->seed : 0, opts ? opts->stats : nullptr, (hipStream_t)stream);
+}
+
+int topk_select_split(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
+                      int32_t k, float *out_vals, int32_t *out_idx, int32_t split,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    if (split < 0 || split > TOPK_MAX_SPLIT) return TOPK_ESPLIT;
+    topk_options o{};
+    o.split = split;
+    return topk_select_ex(scores, lengths, rows, n, k, out_vals, out_idx, &o, workspace,
+                          workspace_bytes, stream);
+}
+
+int topk_select(const float *scores, const int32_t *lengths, int32_t rows, int32_t n, int32_t k,
+                float *out_vals, int32_t *out_idx, void *stream) {
+    int st = check_args(scores, rows, n, k, out_vals, out_idx, lengths);
+    if (st != TOPK_OK) return st;
+    if (rows == 0) return TOPK_OK;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != TOPK_OK) return st;
+    Plan pl = make_plan(rows, n, k, nullptr, cus);
+    void *ws = nullptr;
+    if (pl.split > 1) {
+        st = internal_workspace(pl.ws_bytes, (hipStream_t)stream, &ws);
+        if (st != TOPK_OK) return st;
+    }
+    return run(scores, lengths, rows, n, k, out_vals, out_idx, pl, ws, 0, nullptr,
+               (hipStream_t)stream);
+}
+
+const char *topk_strerror(int status) {
+    switch (status) {
+        case TOPK_OK: return "ok";
+        case TOPK_EINVAL: return "invalid argument";
+        case TOPK_EK_RANGE: return "k out of range";
+        case TOPK_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case TOPK_ESPLIT: return "split out of range";
+        case TOPK_ELAUNCH: return "kernel launch failed";
+        case TOPK_EDEVICE: return "no usable device";
+        case TOPK_EALLOC: return "workspace allocation failed";
+        default: return "unknown status";
+    }
+}
+
+int topk_visit_order(uint64_t seed, int32_t row, int32_t nblocks, int32_t *out) {
+    if (nblocks < 0 || row < 0 || (nblocks > 0 && !out)) return TOPK_EINVAL;
+    const topk::VisitOrder o = topk::make_visit_order(seed, (uint32_t)row, (uint32_t)nblocks);
+    for (int32_t p = 0; p < nblocks; ++p) out[p] = (int32_t)topk::visit_block(o, (uint32_t)p);
+    return TOPK_OK;
+}
+
+size_t topk_probe_sink_words(size_t bytes) { return topk::probe_read_groups(bytes); }
+
+int topk_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+    if (bytes == 0) return TOPK_OK;
+    if (!src || !sink || bytes % 16 != 0 || misaligned(src, 16)) return TOPK_EINVAL;
+    return topk::launch_probe_read(src, bytes, sink, (hipStream_t)stream) == hipSuccess
+               ? TOPK_OK
+               : TOPK_ELAUNCH;
+}
+
+int topk_probe_copy(const void *src, void *dst, size_t bytes, void *stream) {
+    if (bytes == 0) return TOPK_OK;
+    if (!src || !dst || bytes % 16 != 0 || misaligned(src, 16) || misaligned(dst, 16))
+        return TOPK_EINVAL;
+    return topk::launch_probe_copy(src, dst, bytes, (hipStream_t)stream) == hipSuccess
+               ? TOPK_OK
+               : TOPK_ELAUNCH;
+}
+
+}  // extern "C"

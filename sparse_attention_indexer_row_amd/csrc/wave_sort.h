@@ -1,0 +1,130 @@
+// Wave-level bitonic sort and merge of 64*E packed words held in registers.
+//
+// Element i of a list lives in lane i / E, register i % E ("blocked" layout):
+// compare-exchange distances below E stay inside a lane's registers, larger
+// ones pair lane l with lane l ^ (distance / E) through a cross-lane permute.
+// No LDS traffic and no barrier: one wavefront sorts its own list.
+//
+// Keep-the-best merge (kernelbench.com "DeepSeek V4.1 Flash",
+// bitonic-selection paragraph: the second list is compared in reverse
+// where it lies, so the union is bitonic without a reversed copy): with A
+// sorted descending and B sorted ascending in the same layout,
+// max(A[i], B[i]) holds the best 64*E words of A and B and forms a bitonic
+// sequence, which one bitonic merge sorts.
+#pragma once
+
+#include "common.h"
+
+namespace topk {
+
+__device__ __forceinline__ uint32_t lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// Value of `v` in lane (lane ^ D).
+template <int D>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, uint32_t lane) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((lane ^ D) << 2), (int)v);
+}
+
+template <int D>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, uint32_t lane) {
+    uint32_t lo = xor_lane<D>((uint32_t)v, lane);
+    uint32_t hi = xor_lane<D>((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One compare-exchange stage at distance J inside sub-sequences of length
+// SIZE.  Sub-sequence direction: ascending when (i & SIZE) == 0 for the
+// ascending network (ASC), flipped for the descending one.  When SIZE equals
+// the whole list every sub-sequence runs in the final direction.
+template <int E, int SIZE, int J, bool ASC>
+__device__ __forceinline__ void bitonic_stage(uint64_t (&a)[E], uint32_t lane) {
+    constexpr int N = 64 * E;
+    if constexpr (J < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if ((e & J) != 0) continue;
+            const int e2 = e | J;
+            bool up;
+            if constexpr (SIZE >= N) {
+                up = ASC;
+            } else if constexpr (SIZE < E) {
+                up = (((e & SIZE) == 0) == ASC);
+            } else {
+                up = ((((lane * E) & SIZE) == 0) == ASC);
+            }
+            const uint64_t x = a[e], y = a[e2];
+            const uint64_t lo = umin64(x, y), hi = umax64(x, y);
+            a[e] = up ? lo : hi;
+            a[e2] = up ? hi : lo;
+        }
+    } else {
+        constexpr int D = J / E;
+        const bool lower = (lane & D) == 0;
+        bool up;
+        if constexpr (SIZE >= N) {
+            up = ASC;
+        } else {
+            up = ((((lane * E) & SIZE) == 0) == ASC);
+        }
+        const bool take_min = (lower == up);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint64_t x = a[e];
+            const uint64_t y = xor_lane64<D>(x, lane);
+            a[e] = take_min ? umin64(x, y) : umax64(x, y);
+        }
+    }
+}
+
+template <int E, int SIZE, int J, bool ASC>
+__device__ __forceinline__ void bitonic_stages_from(uint64_t (&a)[E], uint32_t lane) {
+    bitonic_stage<E, SIZE, J, ASC>(a, lane);
+    if constexpr (J > 1) bitonic_stages_from<E, SIZE, J / 2, ASC>(a, lane);
+}
+
+template <int E, int SIZE, bool ASC>
+__device__ __forceinline__ void bitonic_levels_from(uint64_t (&a)[E], uint32_t lane) {
+    bitonic_stages_from<E, SIZE, SIZE / 2, ASC>(a, lane);
+    if constexpr (SIZE < 64 * E) bitonic_levels_from<E, SIZE * 2, ASC>(a, lane);
+}
+
+// Full sort of the wave's 64*E words (ascending if ASC, else descending).
+template <int E, bool ASC>
+__device__ __forceinline__ void wave_sort(uint64_t (&a)[E], uint32_t lane) {
+    bitonic_levels_from<E, 2, ASC>(a, lane);
+}
+
+// Sorts a bitonic sequence of 64*E words.
+template <int E, bool ASC>
+__device__ __forceinline__ void wave_merge(uint64_t (&a)[E], uint32_t lane) {
+    bitonic_stages_from<E, 64 * E, 32 * E, ASC>(a, lane);
+}
+
+// acc (descending) := best 64*E words of acc and b (b ascending), descending.
+template <int E>
+__device__ __forceinline__ void keep_best(uint64_t (&acc)[E], const uint64_t (&b)[E],
+                                          uint32_t lane) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = umax64(acc[e], b[e]);
+    wave_merge<E, false>(acc, lane);
+}
+
+// Word at list position `pos` (any lane may ask; all get the same answer).
+template <int E>
+__device__ __forceinline__ uint64_t list_word_at(const uint64_t (&a)[E], uint32_t pos) {
+    const uint32_t e_sel = pos % E;
+    uint64_t v = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) v = (e == (int)e_sel) ? a[e] : v;
+    const int src = (int)(pos / E);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, src);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+}  // namespace topk

@@ -1,0 +1,173 @@
+"""The C-ABI library loads, exports what the header declares, and rejects bad
+arguments on the host.  CPU only: nothing here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_attention_indexer_row_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "topk_select.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(topk_\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_what_the_binding_declares():
+    assert tuple(declared_functions()) == _lib.EXPORTS
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_constants_match_header():
+    text = open(HEADER).read()
+    for cname in ("TOPK_OK", "TOPK_EINVAL", "TOPK_EK_RANGE", "TOPK_EWORKSPACE", "TOPK_ESPLIT",
+                  "TOPK_ELAUNCH", "TOPK_EDEVICE", "TOPK_EALLOC", "TOPK_MAX_K", "TOPK_MAX_SPLIT"):
+        m = re.search(rf"#define {cname} \(?(-?\d+)\)?", text)
+        assert m and int(m.group(1)) == getattr(_lib, cname), cname
+
+
+def test_options_and_plan_struct_sizes():
+    assert ctypes.sizeof(_lib.TopkOptions) == 32
+    assert ctypes.sizeof(_lib.TopkPlan) == 40
+
+
+FAKE = 0x10000  # a non-null, 256-aligned address that is never dereferenced
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, None, -1, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # rows < 0
+    ((FAKE, None, 1, 0, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),        # n < 1
+    ((FAKE, None, 1, 16, 0, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),     # k < 1
+    ((FAKE, None, 1, 16, 2049, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),  # k > max
+    ((None, None, 1, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),       # null scores
+    ((FAKE, None, 1, 16, 4, None, FAKE, None), _lib.TOPK_EINVAL),       # null out_vals
+    ((FAKE, None, 1, 16, 4, FAKE, None, None), _lib.TOPK_EINVAL),       # null out_idx
+    ((FAKE + 2, None, 1, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),   # misaligned scores
+    ((FAKE, FAKE + 1, 1, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),   # misaligned lengths
+    ((None, None, 0, 16, 4, None, None, None), _lib.TOPK_OK),           # rows == 0: no-op
+])
+def test_select_argument_errors(lib, args, status):
+    assert lib.topk_select(*args) == status
+
+
+def test_split_and_ex_argument_errors(lib):
+    a = (FAKE, None, 4, 4096, 8, FAKE, FAKE)
+    assert lib.topk_select_split(*a, -1, FAKE, 1 << 20, None) == _lib.TOPK_ESPLIT
+    assert lib.topk_select_split(*a, 1025, FAKE, 1 << 20, None) == _lib.TOPK_ESPLIT
+    assert lib.topk_select_split(*a, 2, FAKE + 8, 1 << 20, None) == _lib.TOPK_EWORKSPACE
+    o = _lib.TopkOptions()
+    o.waves = 1
+    assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_EINVAL
+    o.waves = 5
+    assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_EINVAL
+    o.waves, o.watermark = 4, -3
+    assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_EINVAL
+    o.watermark, o.split = 0, 2000
+    assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_ESPLIT
+
+
+def test_workspace_init_and_probe_argument_errors(lib):
+    assert lib.topk_workspace_init(None, 256, None) == _lib.TOPK_EWORKSPACE
+    assert lib.topk_workspace_init(FAKE + 16, 256, None) == _lib.TOPK_EWORKSPACE
+    assert lib.topk_workspace_init(FAKE, 100, None) == _lib.TOPK_EWORKSPACE
+    assert lib.topk_workspace_init(FAKE, 0, None) == _lib.TOPK_OK
+    assert lib.topk_probe_read(FAKE, 100, FAKE, None) == _lib.TOPK_EINVAL
+    assert lib.topk_probe_copy(FAKE, None, 256, None) == _lib.TOPK_EINVAL
+    assert lib.topk_probe_copy(FAKE, FAKE, 0, None) == _lib.TOPK_OK
+
+
+def test_strerror(lib):
+    assert lib.topk_strerror(0) == b"ok"
+    assert lib.topk_strerror(_lib.TOPK_EK_RANGE) == b"k out of range"
+    assert lib.topk_strerror(12345) == b"unknown status"
+
+
+def _plan(lib, rows, n, k, split=0, waves=0, watermark=0):
+    o = _lib.TopkOptions()
+    o.split, o.waves, o.watermark = split, waves, watermark
+    p = _lib.TopkPlan()
+    assert lib.topk_plan(rows, n, k, ctypes.byref(o), ctypes.byref(p)) == 0
+    return p
+
+
+def test_plan_list_sizes_and_lds(lib):
+    for k, words in [(1, 64), (64, 64), (65, 128), (512, 512), (513, 1024), (1000, 1024),
+                     (2048, 2048)]:
+        p = _plan(lib, 4, 1 << 16, k)
+        assert p.list_words == words
+        assert p.lds_bytes == 8 * 2 * (p.waves - 1) * p.tray_words
+        assert p.lds_bytes <= 160 * 1024
+        assert p.tray_words == p.watermark + 1024
+
+
+def test_plan_split_policy(lib):
+    cus = _plan(lib, 1, 1024, 1).compute_units
+    big = _plan(lib, 128, 1 << 20, 512)
+    assert big.split * 128 >= cus            # enough workgroups to cover the chip
+    one = _plan(lib, 1, 1 << 20, 512)
+    assert one.split > 1 and one.workspace_bytes > 0
+    small = _plan(lib, 4, 16384, 512)       # 16 blocks per row: no room to split
+    assert small.split == 1 and small.workspace_bytes == 0
+    forced = _plan(lib, 4, 16384, 512, split=3)
+    assert forced.split == 3
+    assert lib.topk_split_workspace_bytes(4, 16384, 512, 3) == forced.workspace_bytes
+    assert forced.workspace_bytes >= 4 * 3 * 512 * 8
+    assert lib.topk_split_workspace_bytes(4, 16384, 0, 3) == 0
+
+
+@pytest.mark.parametrize("nb", [1, 2, 3, 5, 16, 100, 128, 255, 256, 257, 1000, 1024, 4097])
+def test_visit_order_is_a_permutation(nb):
+    out = np.empty(nb, dtype=np.int32)
+    lib = _lib.load()
+    for seed, row in [(0, 0), (1, 0), (0, 7), (123456789, 3)]:
+        assert lib.topk_visit_order(seed, row, nb, out.ctypes.data) == 0
+        assert np.array_equal(np.sort(out), np.arange(nb))
+
+
+def test_visit_order_depends_on_seed_and_row_only():
+    lib = _lib.load()
+    a = np.empty(1024, dtype=np.int32)
+    b = np.empty(1024, dtype=np.int32)
+    lib.topk_visit_order(5, 9, 1024, a.ctypes.data)
+    lib.topk_visit_order(5, 9, 1024, b.ctypes.data)
+    assert np.array_equal(a, b)
+    lib.topk_visit_order(6, 9, 1024, b.ctypes.data)
+    assert not np.array_equal(a, b)
+    lib.topk_visit_order(5, 10, 1024, b.ctypes.data)
+    assert not np.array_equal(a, b)
+
+
+def test_visit_order_looks_shuffled():
+    # a sequential or strided walk would make ascending rows expensive; check
+    # that the first block visited is spread over the range and that the walk
+    # has few ascending runs' worth of records
+    lib = _lib.load()
+    nb = 1024
+    out = np.empty(nb, dtype=np.int32)
+    firsts = []
+    records = []
+    for row in range(400):
+        lib.topk_visit_order(0, row, nb, out.ctypes.data)
+        firsts.append(out[0])
+        records.append(int(np.sum(out == np.maximum.accumulate(out))))
+    hist = np.bincount(np.array(firsts) * 8 // nb, minlength=8)
+    assert hist.min() > 20                  # about 50 per eighth if uniform
+    # records of a uniform random order average H(1024) ~ 7.5
+    assert 5.0 < np.mean(records) < 10.5

@@ -1,0 +1,259 @@
+"""GPU parity: the HIP library against the CPU oracle, bit-exact.
+
+Values are compared as float32 bit patterns and indices exactly, slot by
+slot, including order and the (-inf, -1) filler.  Every case calls the
+library through its C ABI (via the thin binding).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as H
+from sparse_attention_indexer_row_amd import api, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    H.require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_select(scores_np, k, lengths_np=None, **opts):
+    s = H.to_dev(scores_np)
+    ln = H.to_dev(lengths_np) if lengths_np is not None else None
+    if opts:
+        split = opts.get("split", 0)
+        ws = None
+        plan = api.topk_plan(s.shape[0], s.shape[1], k, split=split, waves=opts.get("waves", 0),
+                             watermark=opts.get("watermark", 0))
+        if plan["split"] > 1:
+            ws = api.new_workspace(s.shape[0], s.shape[1], k, plan["split"])
+        v, i = api.topk_select_ex(s, k, ln, workspace=ws, **opts)
+    else:
+        v, i = api.topk_select(s, k, ln)
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), i.cpu().numpy()
+
+
+def check(scores_np, k, lengths_np=None, what="", **opts):
+    print(f"[case] {what} rows={scores_np.shape[0]} n={scores_np.shape[1]} k={k} opts={opts}",
+          flush=True)
+    gv, gi = run_select(scores_np, k, lengths_np, **opts)
+    rv, ri = H.oracle_topk(scores_np, k, lengths_np)
+    H.assert_same(gv, gi, rv, ri, what)
+
+
+# ---- the five named workloads at full size --------------------------------
+
+@pytest.mark.parametrize("name", ["small", "outlier", "one_row", "adverse", "ragged"])
+def test_workload_full_size(name):
+    w = workloads.make(name)
+    check(w.scores, w.k, w.lengths, what=name)
+
+
+def test_ragged_rows_shorter_than_k():
+    # the ragged workload draws few rows below k=2048; force several
+    w = workloads.ragged(rows=40, n=8192, k=2048, seed=11)
+    w.lengths[:8] = np.array([0, 1, 2, 63, 2047, 2048, 2049, 8192], dtype=np.int32)
+    check(w.scores, w.k, w.lengths, what="ragged-short")
+
+
+# ---- edge cases ------------------------------------------------------------
+
+@pytest.mark.parametrize("k", [1, 2, 63, 64, 65, 300, 511, 512, 513, 1000, 1024, 2048])
+def test_k_values(k):
+    x = workloads.normal_rows(6, 50_000, seed=k)
+    check(x, k, what=f"k={k}")
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1023, 1024, 1025, 16383, 129_000])
+def test_unaligned_lengths(n):
+    x = workloads.normal_rows(5, n, seed=n)
+    check(x, 512, what=f"n={n}")
+
+
+@pytest.mark.parametrize("L", [0, 1, 511, 512, 513, 4095, 4096, 4097])
+def test_lengths_around_k(L):
+    n = 4096
+    x = workloads.normal_rows(4, n, seed=L + 3)
+    lengths = np.array([L, max(L - 1, 0), n, n + 10], dtype=np.int32)
+    check(x, 512, lengths, what=f"L={L}")
+
+
+def test_negative_and_oversized_lengths():
+    x = workloads.normal_rows(4, 3000, seed=4)
+    check(x, 100, np.array([-7, 0, 99999, 2999], dtype=np.int32), what="odd lengths")
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_misaligned_base_pointer(offset):
+    rows, n = 7, 10_001
+    flat = workloads.normal_rows(1, rows * n + 8, seed=offset)[0]
+    d = H.to_dev(flat)
+    view = d[offset:offset + rows * n].view(rows, n)
+    assert view.data_ptr() % 16 == 4 * offset
+    v, i = api.topk_select(view, 300)
+    torch.cuda.synchronize()
+    ref = flat[offset:offset + rows * n].reshape(rows, n)
+    rv, ri = H.oracle_topk(ref, 300)
+    H.assert_same(v, i, rv, ri, f"offset={offset}")
+
+
+def test_heavy_ties():
+    g = np.random.default_rng(9)
+    x = np.empty((6, 70_000), dtype=np.float32)
+    x[0] = 1.5                                                    # all equal
+    x[1] = workloads.quantized_levels(g.standard_normal(70_000))  # 256 levels
+    x[2] = np.float32(g.integers(0, 3, 70_000))                   # 3 levels
+    x[3] = np.where(g.random(70_000) < 0.5, np.float32(0.0), np.float32(-0.0))
+    x[4] = np.float32(-np.inf)
+    x[4, ::1000] = np.float32(np.inf)
+    x[5] = g.choice(np.array([-np.inf, -1, -0.0, 0.0, 1, np.inf], dtype=np.float32), 70_000)
+    for k in (1, 512, 2048):
+        check(x, k, what=f"ties k={k}")
+
+
+def test_denormals_and_extremes():
+    g = np.random.default_rng(10)
+    b = g.integers(0, 1 << 23, size=(3, 20_000), dtype=np.uint32)
+    b[1] |= np.uint32(0x80000000)
+    x = b.view(np.float32).copy()
+    x[2] = np.where(g.random(20_000) < 0.5, np.float32(3.4028235e38), np.float32(-3.4028235e38))
+    check(x, 700, what="denormals")
+
+
+def test_strictly_descending_and_ascending_rows():
+    n = 300_000
+    base = workloads.strictly_ascending(workloads.normal_rows(1, n, 12)[0])
+    x = np.stack([base, base[::-1].copy(), base, base[::-1].copy()])
+    check(x, 512, what="monotone")
+
+
+# ---- schedule invariance ---------------------------------------------------
+
+SCHEDULES = [
+    dict(seed=0, split=1), dict(seed=1, split=1), dict(seed=2, split=2),
+    dict(seed=3, split=4, waves=2), dict(seed=4, split=16, waves=3), dict(seed=5, split=64),
+    dict(seed=6, split=1, watermark=64), dict(seed=7, split=3, watermark=2048),
+    dict(seed=8, split=256, waves=2), dict(seed=9, split=1, waves=2, watermark=100),
+]
+
+
+@pytest.mark.parametrize("opts", SCHEDULES, ids=lambda o: "-".join(f"{k}{v}" for k, v in o.items()))
+def test_schedule_invariance(opts):
+    w = workloads.adverse(rows=4, n=1 << 18, seed=21)
+    check(w.scores, 512, what="schedule", **opts)
+
+
+def test_schedule_invariance_ragged():
+    w = workloads.ragged(rows=16, n=60_000, k=1000, seed=22)
+    ref = None
+    for opts in (dict(split=1), dict(split=5, seed=3), dict(split=2, waves=2, watermark=256)):
+        v, i = run_select(w.scores, w.k, w.lengths, **opts)
+        if ref is None:
+            ref = (v, i)
+            rv, ri = H.oracle_topk(w.scores, w.k, w.lengths)
+            H.assert_same(v, i, rv, ri, "ragged schedule")
+        else:
+            assert np.array_equal(i, ref[1]) and np.array_equal(H.bits(v), H.bits(ref[0]))
+
+
+# ---- memory hazards --------------------------------------------------------
+
+def test_outputs_have_no_overrun():
+    rows, n, k = 9, 33_333, 777
+    x = workloads.normal_rows(rows, n, 31)
+    s = H.to_dev(x)
+    guard = 4096
+    vbuf = torch.full((rows * k + 2 * guard,), 12345.0, dtype=torch.float32, device="cuda")
+    ibuf = torch.full((rows * k + 2 * guard,), 777777, dtype=torch.int32, device="cuda")
+    v = vbuf[guard:guard + rows * k].view(rows, k)
+    i = ibuf[guard:guard + rows * k].view(rows, k)
+    for split in (1, 4):
+        ws = api.new_workspace(rows, n, k, split) if split > 1 else None
+        api.topk_select_ex(s, k, split=split, workspace=ws, out=(v, i))
+        torch.cuda.synchronize()
+        vb = vbuf.cpu().numpy()
+        ib = ibuf.cpu().numpy()
+        assert np.all(vb[:guard] == 12345.0) and np.all(vb[-guard:] == 12345.0)
+        assert np.all(ib[:guard] == 777777) and np.all(ib[-guard:] == 777777)
+        rv, ri = H.oracle_topk(x, k)
+        H.assert_same(v, i, rv, ri, f"canary split={split}")
+
+
+def test_workspace_reuse_across_shapes():
+    # one workspace, calls with different shapes back to back: the ticket and
+    # threshold words must come back to zero after every call
+    ws = api.new_workspace(64, 1 << 17, 1000, 8)
+    cases = [(8, 1 << 17, 1000, 8), (64, 50_000, 512, 4), (3, 1 << 17, 64, 8), (64, 9999, 1000, 2)]
+    for it in range(2):
+        for rows, n, k, split in cases:
+            x = workloads.normal_rows(rows, n, seed=rows + n + k + it)
+            s = H.to_dev(x)
+            v, i = api.topk_select_split(s, k, split, ws)
+            torch.cuda.synchronize()
+            rv, ri = H.oracle_topk(x, k)
+            H.assert_same(v, i, rv, ri, f"reuse {rows}x{n} k={k} split={split}")
+    # the whole workspace is zero again
+    assert int(ws.count_nonzero()) == 0
+
+
+def test_argument_error_leaves_outputs_untouched():
+    s = H.to_dev(workloads.normal_rows(2, 1000, 5))
+    v = torch.full((2, 8), 3.0, device="cuda")
+    i = torch.full((2, 8), 5, dtype=torch.int32, device="cuda")
+    from sparse_attention_indexer_row_amd import _lib
+    lib = _lib.load()
+    st = lib.topk_select(s.data_ptr(), None, 2, 1000, 0, v.data_ptr(), i.data_ptr(), None)
+    assert st == _lib.TOPK_EK_RANGE
+    st = lib.topk_select_split(s.data_ptr(), None, 2, 1000, 8, v.data_ptr(), i.data_ptr(), 4,
+                               None, 0, None)
+    assert st == _lib.TOPK_EWORKSPACE
+    torch.cuda.synchronize()
+    assert bool(torch.all(v == 3.0)) and bool(torch.all(i == 5))
+
+
+def test_large_offsets_beyond_2gib():
+    # rows * n * 4 > 2^31 bytes: row offsets must be computed in 64 bits
+    rows, n, k = 600, 1 << 20, 512
+    s = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    s.normal_(generator=g)
+    v, i = api.topk_select(s, k)
+    torch.cuda.synchronize()
+    for r in (0, 511, 512, 599):
+        row = s[r:r + 1].cpu().numpy()
+        rv, ri = H.oracle_topk(row, k)
+        H.assert_same(v[r:r + 1], i[r:r + 1], rv, ri, f"large row {r}")
+    del s
+
+
+# ---- instrumentation -------------------------------------------------------
+
+def test_entrant_counts_single_stream_bound():
+    # One streamer wave per row and no split: the visit is a single stream,
+    # the setting of the pages' bound 1.5 * buffer * H(number of blocks).
+    rows, n, k = 16, 1 << 20, 512
+    x = workloads.normal_rows(rows, n, 41)
+    s = H.to_dev(x)
+    stats = torch.zeros((rows, 2), dtype=torch.int64, device="cuda")
+    v, i = api.topk_select_ex(s, k, split=1, waves=2, stats=stats, seed=5)
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy()
+    plan = api.topk_plan(rows, n, k, split=1, waves=2)
+    nb = n // 1024
+    H_nb = float(np.sum(1.0 / np.arange(1, nb + 1)))
+    bound = 1.5 * plan["tray_words"] * H_nb
+    print(f"[stats] entrants mean={st[:, 0].mean():.0f} max={st[:, 0].max()} "
+          f"sorts mean={st[:, 1].mean():.1f} bound={bound:.0f}", flush=True)
+    assert st[:, 0].mean() <= bound
+    assert np.all(st[:, 0] >= k)
+    rv, ri = H.oracle_topk(x, k)
+    H.assert_same(v, i, rv, ri, "stats run")
