@@ -106,16 +106,24 @@ int topk_select_split(const float *scores, const int32_t *lengths, int32_t rows,
                       int32_t k, float *out_vals, int32_t *out_idx, int32_t split,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Flags for topk_options.flags. */
+/* Skip the sampled threshold estimate: filter with exact bounds only. */
+#define TOPK_FLAG_NO_ESTIMATE 1
+/* Testing aid: make the estimate admit nothing, so every row that uses an
+ * estimate takes the verified re-stream path.  The result is unchanged. */
+#define TOPK_FLAG_FORCE_RERUN 2
+
 /* Tuning and instrumentation knobs.  Zero fields take the defaults. */
 typedef struct {
-    uint64_t seed;           /* visit-order seed; the result never depends on it */
+    uint64_t seed;           /* visit-order and sample seed; the result never depends on it */
     int32_t split;           /* workgroups per row; 0 = automatic                */
     int32_t waves;           /* waves per workgroup, 2..4: one sorts, the rest stream */
-    int32_t watermark;       /* tray words that trigger a sort; 0 = default      */
-    int32_t reserved;
+    int32_t watermark;       /* tray words that trigger a hand-off; 0 = default  */
+    int32_t flags;           /* TOPK_FLAG_* bits; 0 = default behaviour          */
     /* Optional device array [rows][2] of uint64, accumulated into (zero it
-     * first): [0] scores that entered a tray (the only ones ever sorted),
-     * [1] sort passes run.  NULL turns the counters off. */
+     * first): [0] scores that entered a tray (the only ones that ever meet
+     * more than one comparison), [1] threshold-raising selections run over
+     * trays.  NULL turns the counters off. */
     unsigned long long *stats;
 } topk_options;
 

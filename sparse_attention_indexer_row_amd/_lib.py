@@ -22,6 +22,8 @@ TOPK_ELAUNCH = -5
 TOPK_EDEVICE = -6
 TOPK_EALLOC = -7
 TOPK_MAX_K = 2048
+TOPK_FLAG_NO_ESTIMATE = 1
+TOPK_FLAG_FORCE_RERUN = 2
 TOPK_MAX_SPLIT = 1024
 
 # Every function the header declares, in header order.
@@ -46,7 +48,7 @@ class TopkOptions(ctypes.Structure):
         ("split", ctypes.c_int32),
         ("waves", ctypes.c_int32),
         ("watermark", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("stats", ctypes.c_void_p),
     ]
 

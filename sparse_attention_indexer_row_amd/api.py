@@ -109,13 +109,13 @@ def topk_select_split(scores: torch.Tensor, k: int, split: int, workspace: torch
     return vals, idx
 
 
-def _options(seed=0, split=0, waves=0, watermark=0, stats=None) -> TopkOptions:
+def _options(seed=0, split=0, waves=0, watermark=0, stats=None, flags=0) -> TopkOptions:
     o = TopkOptions()
     o.seed = seed
     o.split = split
     o.waves = waves
     o.watermark = watermark
-    o.reserved = 0
+    o.flags = flags
     o.stats = stats.data_ptr() if stats is not None else None
     return o
 
@@ -123,7 +123,7 @@ def _options(seed=0, split=0, waves=0, watermark=0, stats=None) -> TopkOptions:
 def topk_select_ex(scores: torch.Tensor, k: int, lengths: torch.Tensor | None = None, *,
                    seed: int = 0, split: int = 0, waves: int = 0, watermark: int = 0,
                    stats: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                   out=None, stream=None):
+                   flags: int = 0, out=None, stream=None):
     """Selection with explicit options.  ``stats``: int64 [rows][2] to accumulate into."""
     _check_scores(scores)
     lp = _check_lengths(lengths, scores)
@@ -132,7 +132,7 @@ def topk_select_ex(scores: torch.Tensor, k: int, lengths: torch.Tensor | None = 
     if stats is not None and (stats.dtype != torch.int64 or stats.shape != (rows, 2)
                               or stats.device != scores.device or not stats.is_contiguous()):
         raise ValueError("stats must be a contiguous int64 [rows][2] tensor on the device")
-    o = _options(seed, split, waves, watermark, stats)
+    o = _options(seed, split, waves, watermark, stats, flags)
     wp = workspace.data_ptr() if workspace is not None else None
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.load().topk_select_ex(scores.data_ptr(), lp, rows, n, k, vals.data_ptr(),

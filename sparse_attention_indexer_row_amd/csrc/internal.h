@@ -22,6 +22,7 @@ struct SelectArgs {
     uint64_t *ws_lists;        // [rows][split][list_words] (split > 1)
     unsigned long long *stats; // [rows][2] or null
     uint64_t seed;
+    uint32_t flags;            // bit 0: no sampled estimate; bit 1: force the rerun path
 };
 
 // Launches the selection kernel for list capacity 64*E (E in 1..32).

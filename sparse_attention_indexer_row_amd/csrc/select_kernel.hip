@@ -16,9 +16,12 @@
 //     depend on the data, so future addresses are known), and appends
 //     survivors to a double-buffered tray in LDS.  When a tray passes the
 //     watermark the streamer publishes it and keeps streaming into the other
-//     buffer.  One sorter wave owns the kept list (the best 64*E words so
-//     far) in registers, sorts each published tray with a register bitonic
-//     network, merges it into the kept list and raises the shared threshold.
+//     buffer.  One sorter wave owns the kept set (the best k words seen so
+//     far, unsorted, in LDS).  For each published tray it finds the k-th
+//     best word of kept set + tray with a radix selection (LDS histogram
+//     passes over 8-bit digits, finished by a 64-word register sort), drops
+//     everything below it and raises the shared threshold to it.  The kept
+//     set is sorted once, at the end, with a register bitonic network.
 //     Streamers never stop for a sort, and the threshold is the k-th best of
 //     everything the workgroup has seen.
 //   * The per-score test is one compare against the threshold's value, done
@@ -126,28 +129,85 @@ __device__ __forceinline__ void lds_store_u32(uint32_t *p, uint32_t v, uint32_t 
 // ---------------------------------------------------------------------------
 // Streamer waves: read blocks, test, compact survivors into a tray.
 
-// Exact test and tray compaction of one block already in registers.
+// Test and tray compaction of one block already in registers.  Cheap tests
+// first: per quarter (the lane's 4 scores of one dwordx4), then per score,
+// each on the integer bits against `tb`; only score slots where some lane
+// passes build the packed word and take the exact 64-bit test.  The maximum
+// of every quarter that reaches the per-score tests is inserted into the
+// lane's running list of its E best keys, lk[0] >= ... >= lk[E-1]
+// (branch-free max/min insertion); each entry is a distinct element.
+template <int E>
 __device__ __forceinline__ uint32_t admit_block(uint64_t *tray, uint32_t cnt, uint64_t T,
-                                                const float4 (&x)[kLoadsPerBlock], uint32_t vbase,
-                                                uint32_t off0, uint32_t vend, bool ragged,
-                                                uint32_t lane) {
+                                                int32_t tb, const float4 (&x)[kLoadsPerBlock],
+                                                uint32_t vbase, uint32_t off0, uint32_t vend,
+                                                bool ragged, uint32_t (&lk)[E], uint32_t lane) {
 #pragma unroll
     for (int u = 0; u < kLoadsPerBlock; ++u) {
-        const float v4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+        const int32_t v4[4] = {__float_as_int(x[u].x), __float_as_int(x[u].y),
+                               __float_as_int(x[u].z), __float_as_int(x[u].w)};
+        const int32_t m4 = max(max(v4[0], v4[1]), max(v4[2], v4[3]));
+        if (__ballot(ragged || m4 >= tb) == 0ull) continue;
+        const uint32_t g0 = vbase + (uint32_t)u * 256u + lane * 4u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint32_t g = vbase + (uint32_t)u * 256u + lane * 4u + (uint32_t)c;
+            const uint32_t g = g0 + (uint32_t)c;
             const bool valid = !ragged || (g >= off0 && g < vend);
-            const uint64_t w = pack_word(order_key(__float_as_uint(v4[c])), g - off0);
-            const bool pass = valid && (w > T);
+            const bool pre = valid && v4[c] >= tb;
+            if (__ballot(pre) == 0ull) continue;
+            const uint32_t key = order_key((uint32_t)v4[c]);
+            const uint64_t w = pack_word(key, g - off0);
+            const bool pass = pre && (w > T);
             const uint64_t m = __ballot(pass);
             if (m) {
                 if (pass) tray[cnt + mbcnt64(m)] = w;
                 cnt += (uint32_t)__popcll(m);
             }
         }
+        if (!ragged) {
+            // The quarter's largest score is a real element of this lane:
+            // fold it into the lane's running list of its E best keys.
+            uint32_t v = order_key((uint32_t)m4);
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                const uint32_t hi = max(lk[i], v);
+                v = min(lk[i], v);
+                lk[i] = hi;
+            }
+        }
     }
     return cnt;
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t min_step32(uint32_t v, uint32_t lane) {
+    return min(v, xor_lane<D>(v, lane));
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t max_step32(uint32_t v, uint32_t lane) {
+    return max(v, xor_lane<D>(v, lane));
+}
+
+// Largest value over the wave (uniform).
+__device__ __forceinline__ uint32_t wave_max32(uint32_t v, uint32_t lane) {
+    v = max_step32<32>(v, lane);
+    v = max_step32<16>(v, lane);
+    v = max_step32<8>(v, lane);
+    v = max_step32<4>(v, lane);
+    v = max_step32<2>(v, lane);
+    v = max_step32<1>(v, lane);
+    return __builtin_amdgcn_readfirstlane((int)v);
+}
+
+// Smallest value over the wave (returned in every lane, as a uniform value).
+__device__ __forceinline__ uint32_t wave_min32(uint32_t v, uint32_t lane) {
+    v = min_step32<32>(v, lane);
+    v = min_step32<16>(v, lane);
+    v = min_step32<8>(v, lane);
+    v = min_step32<4>(v, lane);
+    v = min_step32<2>(v, lane);
+    v = min_step32<1>(v, lane);
+    return __builtin_amdgcn_readfirstlane((int)v);
 }
 
 // Publishes the tray (its word count) to the sorter.
@@ -163,79 +223,590 @@ __device__ __forceinline__ void wait_tray_free(uint32_t *fill) {
 }
 
 // ---------------------------------------------------------------------------
-// Sorter wave: fold published trays into the kept list (in registers).
+// Sorter wave: keeps the best k words seen by the workgroup, unsorted, in
+// LDS.  Each published tray is folded in by a selection -- the k-th best
+// word of (kept set + tray) becomes the new threshold and everything below
+// it is dropped -- so the per-score cost of the stream stays a few LDS
+// passes.  The kept words are sorted once, at the end.
 
-// Compacts buf[0, c) in place to the words above T; returns the new count.
-__device__ __forceinline__ uint32_t compact_above(uint64_t *buf, uint32_t c, uint64_t T,
-                                                  uint32_t lane) {
-    uint32_t out = 0;
-    for (uint32_t base = 0; base < c; base += kWave) {
-        const uint32_t i = base + lane;
-        const uint64_t v = i < c ? buf[i] : 0ull;
-        const bool keep = v > T;
-        const uint64_t m = __ballot(keep);
-        if (keep) buf[out + mbcnt64(m)] = v;
-        out += (uint32_t)__popcll(m);
-    }
-    return out;
+template <int D>
+__device__ __forceinline__ uint64_t max_step(uint64_t v, uint32_t lane) {
+    return umax64(v, xor_lane64<D>(v, lane));
+}
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v, uint32_t lane) {
+    v = max_step<32>(v, lane);
+    v = max_step<16>(v, lane);
+    v = max_step<8>(v, lane);
+    v = max_step<4>(v, lane);
+    v = max_step<2>(v, lane);
+    v = max_step<1>(v, lane);
+    return uniform64(v);
 }
 
-struct SorterState {
-    uint64_t T;       // k-th best word of the kept list, or any larger bound
-    uint32_t sorts;   // sort passes run
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ uint32_t dpp_add_src(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+
+// Inclusive prefix sum over the wave's lanes with DPP: shifts by 1, 2, 4, 8
+// inside each 16-lane row, then row_bcast:15 and row_bcast:31 carry the row
+// totals upward.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += dpp_add_src<0x111, 0xF, true>(v);
+    v += dpp_add_src<0x112, 0xF, true>(v);
+    v += dpp_add_src<0x114, 0xF, true>(v);
+    v += dpp_add_src<0x118, 0xF, true>(v);
+    v += dpp_add_src<0x142, 0xA, false>(v);
+    v += dpp_add_src<0x143, 0xC, false>(v);
+    return v;
+}
+
+// Tray words folded into the candidate pool per step, per lane.
+constexpr int kPiece = 16;
+// LDS passes read kBatch words per lane before using any of them, so a pass
+// costs a few LDS round trips instead of one per 64 words.
+constexpr int kBatch = 8;
+constexpr uint32_t kBatchWords = kBatch * kWave;
+
+// Appends the nonzero words >= T of a[] to dst[n, ...) (ballot compaction);
+// returns the new n.
+template <int N>
+__device__ __forceinline__ uint32_t write_ge(uint64_t *dst, uint32_t n, const uint64_t (&a)[N],
+                                             uint64_t T, uint32_t lane) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const bool keep = a[j] != 0ull && a[j] >= T;
+        const uint64_t m = __ballot(keep);
+        if (keep) dst[n + mbcnt64(m)] = a[j];
+        n += (uint32_t)__popcll(m);
+    }
+    return n;
+}
+
+template <int N>
+__device__ __forceinline__ void count_digits(const uint64_t (&a)[N], uint64_t fmask,
+                                             uint64_t prefix, int low, uint32_t dmask,
+                                             uint32_t *hist) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        if (a[j] != 0ull && (a[j] & fmask) == prefix) {
+            atomicAdd(&hist[(uint32_t)(a[j] >> low) & dmask], 1u);
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ uint32_t gather_prefix(const uint64_t (&a)[N], uint64_t fmask,
+                                                  uint64_t prefix, uint64_t *out, uint32_t n,
+                                                  uint32_t lane) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const bool take = a[j] != 0ull && (a[j] & fmask) == prefix;
+        const uint64_t m = __ballot(take);
+        if (take) out[n + mbcnt64(m)] = a[j];
+        n += (uint32_t)__popcll(m);
+    }
+    return n;
+}
+
+// The r-th largest (r >= 1) of the distinct nonzero words held in a[] and b[]
+// (zero marks an empty slot), all within [lo, hi], lo < hi.  Most-significant-
+// digit radix selection: starting at the highest bit where lo and hi differ,
+// each pass histograms (in LDS) the next 8 bits of the words sharing the bits
+// fixed so far and fixes the digit holding the r-th largest.  Once that
+// digit's bin holds at most 64 words they are gathered and ranked by one
+// 64-word register sort.
+template <int NA, int NB>
+__device__ __forceinline__ uint64_t select_rth(const uint64_t (&a)[NA], const uint64_t (&b)[NB],
+                                               uint32_t r, uint64_t lo, uint64_t hi,
+                                               uint32_t *hist, uint64_t *gath, uint32_t lane) {
+    int top = 63 - __clzll(lo ^ hi);
+    uint64_t fmask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
+    uint64_t prefix = hi & fmask;
+    for (;;) {
+        const int low = top >= 7 ? top - 7 : 0;
+        const uint32_t dmask = (2u << (top - low)) - 1u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        count_digits(a, fmask, prefix, low, dmask, hist);
+        count_digits(b, fmask, prefix, low, dmask, hist);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+        // bins 4*lane .. 4*lane+3; count of words in higher lanes' bins
+        uint32_t h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = hist[lane * 4 + j];
+        const uint32_t mine = h[0] + h[1] + h[2] + h[3];
+        const uint32_t incl = wave_incl_scan(mine);
+        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+        uint32_t above = total - incl;
+        int hit = -1;
+        uint32_t hit_above = 0, hit_cnt = 0;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+            if (hit < 0 && above < r && r <= above + h[j]) {
+                hit = j;
+                hit_above = above;
+                hit_cnt = h[j];
+            }
+            above += h[j];
+        }
+        const uint64_t who = __ballot(hit >= 0);
+        const int src = (int)__ffsll((unsigned long long)who) - 1;
+        const uint32_t bin = (uint32_t)__builtin_amdgcn_readlane(
+            (int)(lane * 4 + (uint32_t)(hit < 0 ? 0 : hit)), src);
+        const uint32_t bin_above = (uint32_t)__builtin_amdgcn_readlane((int)hit_above, src);
+        const uint32_t bin_cnt = (uint32_t)__builtin_amdgcn_readlane((int)hit_cnt, src);
+        r -= bin_above;
+        prefix |= (uint64_t)bin << low;
+        fmask |= (uint64_t)dmask << low;
+        if (bin_cnt <= (uint32_t)kWave) {
+            uint32_t n = gather_prefix(a, fmask, prefix, gath, 0, lane);
+            n = gather_prefix(b, fmask, prefix, gath, n, lane);
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+            uint64_t v[1] = {lane < n ? gath[lane] : 0ull};
+            wave_sort<1, false>(v, lane);
+            return list_word_at<1>(v, r - 1);
+        }
+        top = low - 1;
+    }
+}
+
+// Candidate pool of the sorter: kept words (at most 64*E) plus up to one
+// tray piece (kPiece*64 words), all >= some earlier threshold.
+template <int E>
+struct PoolCfg {
+    static constexpr uint32_t cap = (uint32_t)(64 * E + kPiece * kWave);
 };
 
-// Sorts one published tray into `kept` chunk by chunk (tray sort on
-// registers, then keep-the-best merge), refiltering the rest of the tray
-// against the raised threshold before each chunk.
+struct SorterState {
+    uint64_t T;       // valid lower bound of the k-th best word
+    uint32_t pc;      // words in the pool
+    uint32_t base;    // histogram: bucket b counts keys in [base + b<<shift, ...)
+    uint32_t shift;
+    uint32_t kmax;    // largest key ever added to the pool
+    uint32_t sorts;   // exact selections run
+};
+
+// Bucket of key x (x >= base); the top bucket is open-ended.
+__device__ __forceinline__ uint32_t bucket_of(uint32_t x, uint32_t base, uint32_t shift) {
+    const uint32_t b = (x - base) >> shift;
+    return b > 255u ? 255u : b;
+}
+
+// Lower bound from the histogram: the lower key edge of the highest bucket
+// b* such that buckets b*..255 hold at least k words; 0 when fewer than k
+// words are counted.  Those k words are real candidates with keys at or
+// above the edge, so (edge << 32) is a valid threshold word.
+__device__ __forceinline__ uint64_t hist_bound(const uint32_t *hist, uint32_t k, uint32_t base,
+                                               uint32_t shift, uint32_t &bstar, uint32_t lane) {
+    uint32_t h[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = hist[lane * 4 + j];
+    const uint32_t mine = h[0] + h[1] + h[2] + h[3];
+    const uint32_t incl = wave_incl_scan(mine);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    bstar = 0;
+    if (total < k) return 0ull;
+    uint32_t above = total - incl;  // words in higher lanes' buckets
+    int hit = -1;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+        if (hit < 0 && above < k && k <= above + h[j]) hit = j;
+        above += h[j];
+    }
+    const uint64_t who = __ballot(hit >= 0);
+    const int src = (int)__ffsll((unsigned long long)who) - 1;
+    bstar = (uint32_t)__builtin_amdgcn_readlane((int)(lane * 4 + (uint32_t)(hit < 0 ? 0 : hit)), src);
+    return (uint64_t)(base + (bstar << shift)) << 32;
+}
+
+// Counts the pool words >= T into a fresh histogram over [base, ...).
+__device__ __forceinline__ void rebuild_hist(const uint64_t *pool, uint32_t pc, uint64_t T,
+                                             uint32_t base, uint32_t shift, uint32_t *hist,
+                                             uint32_t lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    for (uint32_t i = lane; i < pc; i += kWave) {
+        const uint64_t w = pool[i];
+        const uint32_t key = (uint32_t)(w >> 32);
+        if (w >= T && key >= base) atomicAdd(&hist[bucket_of(key, base, shift)], 1u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+}
+
+// Smallest shift that maps keys [base, kmax] onto 256 buckets.
+__device__ __forceinline__ uint32_t fit_shift(uint32_t base, uint32_t kmax) {
+    const uint32_t span = kmax - base;
+    const uint32_t bits = span == 0u ? 0u : 32u - (uint32_t)__clz(span);
+    return bits > 8u ? bits - 8u : 0u;
+}
+
+template <bool SPLIT>
+__device__ __forceinline__ void raise_threshold(SorterState &ss, uint64_t nt, uint64_t *sT,
+                                                uint64_t *gT, uint32_t lane) {
+    if (nt <= ss.T) return;
+    ss.T = nt;
+    if (lane == 0) {
+        __hip_atomic_fetch_max(sT, nt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if constexpr (SPLIT) {
+            __hip_atomic_fetch_max(gT, nt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Exact pruning: keeps exactly the k best pool words (if there are more) and
+// sets the threshold to the k-th best.  Pool words are loaded into registers
+// (64*E + kPiece*64 at most) and ranked by select_rth.
 template <int E, bool SPLIT>
-__device__ __forceinline__ void sort_tray(uint64_t (&kept)[E], SorterState &ss, uint64_t *buf,
-                                          uint32_t c, uint64_t *sT, uint64_t *gT, uint32_t k,
-                                          uint32_t lane) {
-    constexpr uint32_t KP = (uint32_t)Cfg<E>::KP;
-    for (;;) {
+__device__ __noinline__ void prune_pool(SorterState &ss, uint64_t *pool, uint64_t *sT,
+                                        uint64_t *gT, uint32_t k, uint32_t *hist, uint64_t *gath,
+                                        uint32_t lane) {
+    uint64_t a[E], b[kPiece];
+    uint32_t n = 0;
+    uint64_t lmx = 0ull;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t i = (uint32_t)e * kWave + lane;
+        const uint64_t w = i < ss.pc ? pool[i] : 0ull;
+        a[e] = w >= ss.T ? w : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < kPiece; ++j) {
+        const uint32_t i = (uint32_t)(E + j) * kWave + lane;
+        const uint64_t w = i < ss.pc ? pool[i] : 0ull;
+        b[j] = w >= ss.T ? w : 0ull;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        n += (uint32_t)__popcll(__ballot(a[e] != 0ull));
+        lmx = umax64(lmx, a[e]);
+    }
+#pragma unroll
+    for (int j = 0; j < kPiece; ++j) {
+        n += (uint32_t)__popcll(__ballot(b[j] != 0ull));
+        lmx = umax64(lmx, b[j]);
+    }
+    uint64_t nt = 0ull;
+    if (n > k) {
+        nt = select_rth(a, b, k, ss.T, wave_max64(lmx, lane), hist, gath, lane);
+        ++ss.sorts;
+    }
+    const uint32_t w = write_ge(pool, 0, a, nt, lane);
+    ss.pc = write_ge(pool, w, b, nt, lane);
+    if (nt != 0ull) raise_threshold<SPLIT>(ss, nt, sT, gT, lane);
+}
+
+// Folds one published tray into the pool, kPiece*64 words at a time: words
+// below the threshold are dropped, the rest are appended and counted in the
+// key histogram, and the histogram's bound raises the threshold.  When the
+// bound sits in the top quarter of the histogram's range, the range is
+// re-fitted to [threshold key, largest key] and recounted, so the bound
+// keeps tracking the k-th best closely.
+template <int E, bool SPLIT>
+__device__ __forceinline__ void merge_tray(SorterState &ss, uint64_t *pool, const uint64_t *buf,
+                                           uint32_t c, uint64_t *sT, uint64_t *gT, uint32_t k,
+                                           uint32_t *hist, uint64_t *gath, uint32_t lane) {
+    constexpr uint32_t kPieceWords = (uint32_t)(kPiece * kWave);
+    for (uint32_t off = 0; off < c; off += kPieceWords) {
         ss.T = umax64(ss.T, lds_load_word(sT));
         if constexpr (SPLIT) {
             ss.T = umax64(ss.T, uniform64(__hip_atomic_load(gT, __ATOMIC_RELAXED,
                                                             __HIP_MEMORY_SCOPE_AGENT)));
         }
-        c = compact_above(buf, c, ss.T, lane);
-        if (c == 0) break;
-        const uint32_t take = c < KP ? c : KP;
-        const uint32_t start = c - take;
-        uint64_t a[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const uint32_t i = (uint32_t)e * kWave + lane;
-            a[e] = i < take ? buf[start + i] : 0ull;
+        const uint32_t piece = c - off < kPieceWords ? c - off : kPieceWords;
+        if (ss.pc + piece > PoolCfg<E>::cap) {
+            prune_pool<E, SPLIT>(ss, pool, sT, gT, k, hist, gath, lane);
+            uint32_t base = (uint32_t)(ss.T >> 32);
+            ss.base = base;
+            ss.shift = fit_shift(base, ss.kmax);
+            rebuild_hist(pool, ss.pc, ss.T, ss.base, ss.shift, hist, lane);
         }
-        c = start;
-        wave_sort<E, true>(a, lane);
-        keep_best<E>(kept, a, lane);
-        ++ss.sorts;
-        const uint64_t nt = list_word_at<E>(kept, k - 1);
-        if (nt > ss.T) {
-            ss.T = nt;
-            if (lane == 0) {
-                __hip_atomic_fetch_max(sT, nt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                if constexpr (SPLIT) {
-                    __hip_atomic_fetch_max(gT, nt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+        const uint64_t T = ss.T;
+        uint32_t lkmax = 0u;
+        for (uint32_t i0 = 0; i0 < piece; i0 += kBatchWords) {
+            uint64_t v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const uint32_t i = i0 + (uint32_t)j * kWave + lane;
+                v[j] = i < piece ? buf[off + i] : 0ull;
             }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const bool keep = v[j] != 0ull && v[j] >= T;
+                const uint64_t m = __ballot(keep);
+                if (keep) {
+                    pool[ss.pc + mbcnt64(m)] = v[j];
+                    const uint32_t key = (uint32_t)(v[j] >> 32);
+                    lkmax = max(lkmax, key);
+                    if (key >= ss.base) atomicAdd(&hist[bucket_of(key, ss.base, ss.shift)], 1u);
+                }
+                ss.pc += (uint32_t)__popcll(m);
+            }
+        }
+        ss.kmax = max(ss.kmax, wave_max32(lkmax, lane));
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+        uint32_t bstar = 0;
+        const uint64_t hb = hist_bound(hist, k, ss.base, ss.shift, bstar, lane);
+        raise_threshold<SPLIT>(ss, hb, sT, gT, lane);
+        if (hb != 0ull && bstar >= 192u && ss.shift > 0u) {
+            ss.base = (uint32_t)(ss.T >> 32);
+            ss.shift = fit_shift(ss.base, ss.kmax);
+            rebuild_hist(pool, ss.pc, ss.T, ss.base, ss.shift, hist, lane);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 
+// Geometry of one row.  Blocks are aligned to 16 bytes of the row's
+// storage: virtual position g = position + off0, off0 being the row start's
+// misalignment in floats, so interior blocks are whole dwordx4 groups.
+struct RowGeom {
+    const float *abase;    // 16-byte aligned; position p is abase[p + off0]
+    uint32_t off0;
+    uint32_t L;            // valid positions
+    uint32_t vend;         // L + off0
+    uint32_t nb;           // blocks
+    uint32_t last_group;   // last aligned 4-group holding a valid position
+};
+
+__device__ __forceinline__ RowGeom row_geometry(const SelectArgs &p, uint32_t r) {
+    RowGeom g;
+    int64_t L = p.n;
+    if (p.lengths) {
+        L = p.lengths[r];
+        L = L < 0 ? 0 : (L > p.n ? p.n : L);
+    }
+    const float *rowp = p.scores + (int64_t)r * p.n;
+    g.off0 = (uint32_t)(((uintptr_t)rowp >> 2) & 3u);
+    g.abase = rowp - g.off0;
+    g.L = (uint32_t)L;
+    g.vend = g.L + g.off0;
+    g.nb = L > 0 ? (g.vend + kBlock - 1) / kBlock : 0u;
+    g.last_group = L > 0 ? ((g.vend - 1u) & ~3u) : 0u;
+    return g;
+}
+
+// Sampled threshold estimate ("The Secret GPU Kernel Behind DeepSeek V4.1
+// Flash", transcript 10:57-11:09, on LightTopK: sample a small subset to
+// estimate a threshold, filter online, still return the exact answer; and
+// 11:47-12:10: the shipped kernel starts its scan already holding a working
+// threshold).  512 aligned 4-score groups are drawn one per stratum of the
+// row's aligned groups, at a seeded position inside the stratum; the
+// estimate is the j-th best sampled word with j = ceil(10 k 2048 / L), so
+// about 10k scores of the row lie above it.  It is not a bound: whether it
+// was low enough is checked at the end (at least k scores admitted), and the
+// row is streamed again without it otherwise.  Returns 0 (no estimate) for
+// rows too short for it to pay.
+constexpr uint32_t kSampleGroups = 512;
+constexpr uint32_t kSampleWords = 4 * kSampleGroups;
+constexpr uint32_t kEstimateMargin = 10;
+constexpr uint32_t kFlagNoEstimate = 1u;
+constexpr uint32_t kFlagForceRerun = 2u;
+
+template <int D>
+__device__ __forceinline__ uint64_t min_step(uint64_t v, uint32_t lane) {
+    return umin64(v, xor_lane64<D>(v, lane));
+}
+
+__device__ __forceinline__ uint64_t wave_min64(uint64_t v, uint32_t lane) {
+    v = min_step<32>(v, lane);
+    v = min_step<16>(v, lane);
+    v = min_step<8>(v, lane);
+    v = min_step<4>(v, lane);
+    v = min_step<2>(v, lane);
+    v = min_step<1>(v, lane);
+    return uniform64(v);
+}
+
+__device__ __noinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t seed, uint32_t r,
+                                                    uint32_t k, uint32_t flags, uint32_t *hist,
+                                                    uint64_t *gath, uint32_t lane) {
+    if ((flags & kFlagNoEstimate) || g.L == 0u) return 0ull;
+    const uint64_t jn = ((uint64_t)kEstimateMargin * k * kSampleWords + g.L - 1) / g.L;
+    if (jn > kSampleWords / 8) return 0ull;
+    if (flags & kFlagForceRerun) return ~0ull;  // admits nothing: forces the rerun path
+    const uint32_t ngroups = g.last_group / 4u + 1u;
+    const uint64_t key = splitmix64(seed ^ 0x5851F42D4C957F2Dull ^ ((uint64_t)r << 20));
+    uint64_t a[16], b[16];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t si = (uint32_t)t * kWave + lane;               // stratum
+        const uint32_t g0 = (uint32_t)((uint64_t)si * ngroups / kSampleGroups);
+        const uint32_t g1 = (uint32_t)((uint64_t)(si + 1) * ngroups / kSampleGroups);
+        const uint32_t span = g1 > g0 ? g1 - g0 : 1u;
+        const uint32_t grp = g0 + mix32((uint32_t)key ^ (si * 0x9E3779B1u) ^ (uint32_t)(key >> 32)) % span;
+        const uint32_t gs = grp * 4u;
+        const float4 x = *reinterpret_cast<const float4 *>(g.abase + gs);
+        const float v4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t gc = gs + (uint32_t)c;
+            const bool valid = g1 > g0 && gc >= g.off0 && gc < g.vend;
+            const uint64_t w = valid ? pack_word(order_key(__float_as_uint(v4[c])), gc - g.off0)
+                                     : 0ull;
+            if (t < 4) a[t * 4 + c] = w; else b[(t - 4) * 4 + c] = w;
+        }
+    }
+    uint32_t n = 0;
+    uint64_t lmx = 0ull, lmn = ~0ull;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        n += (uint32_t)__popcll(__ballot(a[j] != 0ull)) + (uint32_t)__popcll(__ballot(b[j] != 0ull));
+        lmx = umax64(lmx, umax64(a[j], b[j]));
+        lmn = umin64(lmn, umin64(a[j] ? a[j] : ~0ull, b[j] ? b[j] : ~0ull));
+    }
+    if (n < 2u * (uint32_t)jn) return 0ull;
+    const uint64_t hi = wave_max64(lmx, lane);
+    const uint64_t lo = wave_min64(lmn, lane);
+    if (lo >= hi) return 0ull;
+    return select_rth(a, b, (uint32_t)jn, lo, hi, hist, gath, lane);
+}
+
+// Streams this wave's share of a row's blocks once: positions q, q+Q, ... of
+// the visit order.  Scores whose word beats max(threshold, estimate) go to
+// the tray; full trays are published to the sorter.  Returns the number of
+// scores that entered a tray.
+template <int E, bool SPLIT>
+__device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOrder &ord,
+                                                 uint32_t q, uint32_t Q, uint64_t tau,
+                                                 uint64_t &T, uint64_t *trays, uint32_t w,
+                                                 uint32_t CW, uint32_t Wm, uint64_t *sT,
+                                                 uint32_t (*fill)[2], uint64_t *gT,
+                                                 uint32_t lane) {
+    constexpr int D = Cfg<E>::D;
+    const uint32_t mine = q < g.nb ? (g.nb - 1u - q) / Q + 1u : 0u;
+    uint32_t cur = 0, cnt = 0, entered = 0;
+    uint32_t lk[E];   // this lane's E best keys seen, descending (0 = none)
+#pragma unroll
+    for (int i = 0; i < E; ++i) lk[i] = 0u;
+    uint64_t *tray = trays + (size_t)(2 * w) * CW;
+    if (mine == 0) return 0u;
+
+    float4 buf[D][kLoadsPerBlock];
+    uint32_t bid[D];
+    uint64_t gbuf[D];
+    // Every slot issues exactly one set of loads per visit (past the stream's
+    // end it re-reads its last block), so the wait before each slot is the
+    // same static count every time.
+    auto issue = [&](float4 (&dst)[kLoadsPerBlock], uint32_t &b_out, uint64_t &g_out,
+                     uint32_t t) __attribute__((always_inline)) {
+        const uint32_t tt = t < mine ? t : mine - 1u;
+        const uint32_t b = visit_block(ord, q + tt * Q);
+        b_out = b;
+        if constexpr (SPLIT) {
+            g_out = __hip_atomic_load(gT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const uint32_t vbase = b * (uint32_t)kBlock;
+        const bool ragged = vbase < g.off0 || vbase + (uint32_t)kBlock > g.vend;
+#pragma unroll
+        for (int u = 0; u < kLoadsPerBlock; ++u) {
+            uint32_t gp = vbase + (uint32_t)u * 256u + lane * 4u;
+            if (ragged) gp = gp > g.last_group ? g.last_group : gp;  // stay on a valid group
+            dst[u] = *reinterpret_cast<const float4 *>(g.abase + gp);
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(buf[d], bid[d], gbuf[d], (uint32_t)d);
+
+    for (uint32_t t0 = 0; t0 < mine; t0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const uint32_t t = t0 + (uint32_t)d;
+            if (t < mine) {
+                if constexpr (SPLIT) T = umax64(T, uniform64(gbuf[d]));
+                const uint64_t F = umax64(T, tau);
+                const int32_t tb = prefilter_bound(F);
+                const uint32_t vbase = bid[d] * (uint32_t)kBlock;
+                const bool ragged = vbase < g.off0 || vbase + (uint32_t)kBlock > g.vend;
+                const uint32_t before = cnt;
+                cnt = admit_block<E>(tray, cnt, F, tb, buf[d], vbase, g.off0, g.vend, ragged, lk,
+                                     lane);
+                entered += cnt - before;
+                if (cnt != before) {
+                    // 64*E >= k distinct elements have keys >= the smallest
+                    // lane's E-th best key: a lower bound of the k-th best.
+                    const uint32_t kb = wave_min32(lk[E - 1], lane);
+                    const uint64_t lb = (uint64_t)kb << 32;
+                    if (lb > T) {
+                        T = lb;
+                        if (lane == 0) {
+                            __hip_atomic_fetch_max(sT, lb, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+                        }
+                    }
+                }
+            }
+            issue(buf[d], bid[d], gbuf[d], t + (uint32_t)D);
+            T = umax64(T, lds_load_word(sT));
+            if (cnt >= Wm) {
+                publish_tray(&fill[w][cur], cnt, lane);
+                cur ^= 1u;
+                cnt = 0;
+                tray = trays + (size_t)(2 * w + cur) * CW;
+                wait_tray_free(&fill[w][cur]);
+            }
+        }
+    }
+    if (cnt > 0) publish_tray(&fill[w][cur], cnt, lane);
+    return entered;
+}
+
+// Sorter side of one pass: folds published trays into the pool until every
+// streamer is done, then keeps exactly the best min(k, candidates) words.
+template <int E, bool SPLIT>
+__device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_t *trays,
+                                        uint32_t CW, uint32_t NS, uint32_t (*fill)[2],
+                                        uint32_t *done_ctr, uint64_t *sT, uint64_t *gT,
+                                        uint32_t k, uint32_t *hist, uint64_t *gath,
+                                        uint32_t lane) {
+    for (;;) {
+        const uint32_t done = lds_load_u32(done_ctr);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        bool worked = false;
+        for (uint32_t v = 0; v < NS; ++v) {
+            for (uint32_t b = 0; b < 2; ++b) {
+                const uint32_t c = lds_load_u32(&fill[v][b]);
+                if (c == 0u) continue;
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+                merge_tray<E, SPLIT>(ss, pool, trays + (size_t)(2 * v + b) * CW, c, sT, gT, k,
+                                     hist, gath, lane);
+                publish_tray(&fill[v][b], 0u, lane);
+                worked = true;
+            }
+        }
+        if (!worked) {
+            if (done == NS) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    prune_pool<E, SPLIT>(ss, pool, sT, gT, k, hist, gath, lane);
+}
+
+__device__ __forceinline__ void reset_sorter(SorterState &ss, uint32_t *hist, uint32_t lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
+    ss.pc = 0u;
+    ss.base = 0u;
+    ss.shift = 24u;   // 256 buckets over the whole key range to start
+    ss.kmax = 0u;
+}
+
+constexpr uint32_t kVerdictExit = 1u;
+constexpr uint32_t kVerdictRerun = 2u;
+
 template <int E, bool SPLIT>
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs p) {
     constexpr int KP = Cfg<E>::KP;
-    constexpr int D = Cfg<E>::D;
-    extern __shared__ uint64_t trays[];          // [streamers][2][tray_words]
-    __shared__ uint64_t s_T;                      // workgroup threshold word
+    extern __shared__ uint64_t trays[];  // [streamers][2][tray_words], pool, gather[64], hist[256]
+    __shared__ uint64_t s_T;                      // workgroup threshold word (a lower bound)
+    __shared__ uint64_t s_tau;                    // sampled estimate (0 = none)
     __shared__ uint32_t s_fill[kMaxWaves][2];     // published tray word counts
-    __shared__ uint32_t s_done;                   // streamers finished
+    __shared__ uint32_t s_done;                   // streamers finished with the current pass
+    __shared__ uint32_t s_ready;                  // estimate published
+    __shared__ uint32_t s_verdict;                // after the first pass: exit or rerun
 
     const uint32_t lane = lane_id();
     const uint32_t w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
@@ -251,165 +822,135 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p) {
 
     if (threadIdx.x == 0) {
         s_T = 0ull;
+        s_tau = 0ull;
         s_done = 0u;
+        s_ready = 0u;
+        s_verdict = 0u;
     }
     if (threadIdx.x < 2 * kMaxWaves) s_fill[threadIdx.x / 2][threadIdx.x % 2] = 0u;
     __syncthreads();
 
+    const RowGeom g = row_geometry(p, r);
+    const VisitOrder ord = make_visit_order(p.seed, r, g.nb);
+
     if (w < NS) {
         // ---- streamer ----
-        // Row geometry.  Blocks are aligned to 16 bytes of the row's storage:
-        // virtual position g = position + off0, off0 being the row start's
-        // misalignment in floats, so interior blocks are whole dwordx4 groups.
-        int64_t L = p.n;
-        if (p.lengths) {
-            L = p.lengths[r];
-            L = L < 0 ? 0 : (L > p.n ? p.n : L);
-        }
-        const float *rowp = p.scores + (int64_t)r * p.n;
-        const uint32_t off0 = (uint32_t)(((uintptr_t)rowp >> 2) & 3u);
-        const float *abase = rowp - off0;
-        const uint32_t vend = (uint32_t)L + off0;
-        const uint32_t nb = L > 0 ? (vend + kBlock - 1) / kBlock : 0u;
-        const uint32_t last_group = L > 0 ? ((vend - 1u) & ~3u) : 0u;
-        const VisitOrder ord = make_visit_order(p.seed, r, nb);
-        const uint32_t Q = S * NS;                // streams over this row
-        const uint32_t q = s * NS + w;            // this wave's stream
-        const uint32_t mine = q < nb ? (nb - 1u - q) / Q + 1u : 0u;
-        const uint32_t Wm = (uint32_t)p.watermark;
-
-        uint32_t cur = 0, cnt = 0, entered = 0;
+        while (lds_load_u32(&s_ready) == 0u) __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        uint64_t tau = lds_load_word(&s_tau);
         uint64_t T = 0ull;
-        uint64_t *tray = trays + (size_t)(2 * w) * CW;
-
-        if (mine > 0) {
-            float4 buf[D][kLoadsPerBlock];
-            uint32_t bid[D];
-            uint64_t gbuf[D];
-            // Every slot issues exactly one set of loads per visit (past the
-            // stream's end it re-reads its last block), so the wait before
-            // each slot is the same static count every time.
-            auto issue = [&](float4 (&dst)[kLoadsPerBlock], uint32_t &b_out, uint64_t &g_out,
-                             uint32_t t) __attribute__((always_inline)) {
-                const uint32_t tt = t < mine ? t : mine - 1u;
-                const uint32_t b = visit_block(ord, q + tt * Q);
-                b_out = b;
-                if constexpr (SPLIT) {
-                    g_out = __hip_atomic_load(gT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-                const uint32_t vbase = b * (uint32_t)kBlock;
-                const bool ragged = vbase < off0 || vbase + (uint32_t)kBlock > vend;
-#pragma unroll
-                for (int u = 0; u < kLoadsPerBlock; ++u) {
-                    uint32_t g = vbase + (uint32_t)u * 256u + lane * 4u;
-                    if (ragged) g = g > last_group ? last_group : g;  // stay on a valid group
-                    dst[u] = *reinterpret_cast<const float4 *>(abase + g);
-                }
-            };
-#pragma unroll
-            for (int d = 0; d < D; ++d) issue(buf[d], bid[d], gbuf[d], (uint32_t)d);
-
-            for (uint32_t t0 = 0; t0 < mine; t0 += D) {
-#pragma unroll
-                for (int d = 0; d < D; ++d) {
-                    const uint32_t t = t0 + (uint32_t)d;
-                    if (t < mine) {
-                        if constexpr (SPLIT) T = umax64(T, uniform64(gbuf[d]));
-                        const int32_t tb = prefilter_bound(T);
-                        const uint32_t vbase = bid[d] * (uint32_t)kBlock;
-                        const bool ragged = vbase < off0 || vbase + (uint32_t)kBlock > vend;
-                        int32_t mx = INT32_MIN;
-#pragma unroll
-                        for (int u = 0; u < kLoadsPerBlock; ++u) {
-                            const int32_t a0 = __float_as_int(buf[d][u].x);
-                            const int32_t a1 = __float_as_int(buf[d][u].y);
-                            const int32_t a2 = __float_as_int(buf[d][u].z);
-                            const int32_t a3 = __float_as_int(buf[d][u].w);
-                            mx = max(max(mx, a0), a1);
-                            mx = max(max(mx, a2), a3);
-                        }
-                        if (__ballot(ragged || mx >= tb) != 0ull) {
-                            const uint32_t before = cnt;
-                            cnt = admit_block(tray, cnt, T, buf[d], vbase, off0, vend, ragged, lane);
-                            entered += cnt - before;
-                        }
-                    }
-                    issue(buf[d], bid[d], gbuf[d], t + (uint32_t)D);
-                    T = umax64(T, lds_load_word(&s_T));
-                    if (cnt >= Wm) {
-                        publish_tray(&s_fill[w][cur], cnt, lane);
-                        cur ^= 1u;
-                        cnt = 0;
-                        tray = trays + (size_t)(2 * w + cur) * CW;
-                        wait_tray_free(&s_fill[w][cur]);
-                    }
-                }
+        uint32_t q = s * NS + w, Q = S * NS;
+        uint32_t entered = 0;
+        for (int pass = 0; pass < 2; ++pass) {
+            entered += stream_share<E, SPLIT>(g, ord, q, Q, tau, T, trays, w, CW,
+                                              (uint32_t)p.watermark, &s_T, s_fill, gT, lane);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            if (lane == 0) {
+                __hip_atomic_fetch_add(&s_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-            if (cnt > 0) publish_tray(&s_fill[w][cur], cnt, lane);
+            if (pass == 1) break;
+            uint32_t verdict;
+            while ((verdict = lds_load_u32(&s_verdict)) == 0u) __builtin_amdgcn_s_sleep(2);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            if (verdict != kVerdictRerun) break;
+            // Stream the whole row again, without the estimate.
+            q = w;
+            Q = NS;
+            tau = 0ull;
         }
         if (p.stats && lane == 0 && entered > 0) {
             atomicAdd(p.stats + 2 * (size_t)r, (unsigned long long)entered);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-        if (lane == 0) __hip_atomic_fetch_add(&s_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         return;
     }
 
     // ---- sorter (wave NS) ----
-    uint64_t kept[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) kept[e] = 0ull;
+    uint64_t *pool = trays + (size_t)(2 * NS) * CW;            // [PoolCfg<E>::cap]
+    uint64_t *gath = pool + PoolCfg<E>::cap;                    // [64]
+    uint32_t *hist = reinterpret_cast<uint32_t *>(gath + kWave);  // [256]
+    const uint64_t tau = estimate_threshold(g, p.seed, r, k, p.flags, hist, gath, lane);
+    if (lane == 0) {
+        s_tau = tau;
+        __hip_atomic_store(&s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     SorterState ss;
     ss.T = 0ull;
     ss.sorts = 0u;
-    for (;;) {
-        const uint32_t done = lds_load_u32(&s_done);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        bool worked = false;
-        for (uint32_t v = 0; v < NS; ++v) {
-            for (uint32_t b = 0; b < 2; ++b) {
-                const uint32_t c = lds_load_u32(&s_fill[v][b]);
-                if (c == 0u) continue;
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-                sort_tray<E, SPLIT>(kept, ss, trays + (size_t)(2 * v + b) * CW, c, &s_T, gT, k,
-                                    lane);
-                publish_tray(&s_fill[v][b], 0u, lane);
-                worked = true;
-            }
-        }
-        if (!worked) {
-            if (done == NS) break;
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    if (p.stats && lane == 0 && ss.sorts > 0) {
-        atomicAdd(p.stats + 2 * (size_t)r + 1, (unsigned long long)ss.sorts);
-    }
+    reset_sorter(ss, hist, lane);
+    auto set_verdict = [&](uint32_t v) __attribute__((always_inline)) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        if (lane == 0) __hip_atomic_store(&s_verdict, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    // Starts the rerun: empty pool (every score is streamed again), the
+    // threshold stays (it is a valid bound of the row's k-th best).
+    auto start_rerun = [&]() __attribute__((always_inline)) {
+        reset_sorter(ss, hist, lane);
+        if (lane == 0) __hip_atomic_store(&s_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        set_verdict(kVerdictRerun);
+    };
 
-    if constexpr (!SPLIT) {
-        write_row<E>(p.out_vals + (size_t)r * k, p.out_idx + (size_t)r * k, k, kept, lane);
-    } else {
-        // Publish this segment's list, take a ticket; the last of the row's
-        // segments to arrive merges every list and writes the row.
+    uint64_t kept_sorted[E];
+    bool rerun = false;
+    for (int pass = 0; pass < 2; ++pass) {
+        collect<E, SPLIT>(ss, pool, trays, CW, NS, s_fill, &s_done, &s_T, gT, k, hist, gath, lane);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t i = (uint32_t)e * kWave + lane;
+            kept_sorted[e] = i < ss.pc ? pool[i] : 0ull;
+        }
+        wave_sort<E, false>(kept_sorted, lane);   // the one full sort of this pass
+        if (!SPLIT || rerun) {
+            // With an estimate in use, fewer than k admitted scores means
+            // some of the row's best k may lie below it: stream again.
+            if (!rerun && tau != 0ull && ss.pc < k) {
+                rerun = true;
+                start_rerun();
+                continue;
+            }
+            if (!rerun) set_verdict(kVerdictExit);
+            break;
+        }
+        // Split row: publish this segment's list and take a ticket; the last
+        // of the row's segments to arrive merges every list.
         uint64_t *lists = p.ws_lists + (size_t)r * S * KP;
-        store_list<E>(lists + (size_t)s * KP, kept, lane);
+        store_list<E>(lists + (size_t)s * KP, kept_sorted, lane);
         __threadfence();
         uint32_t old = 0;
         if (lane == 0) {
             old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         }
         old = __builtin_amdgcn_readfirstlane((int)old);
-        if (old != S - 1u) return;
+        if (old != S - 1u) {
+            set_verdict(kVerdictExit);
+            if (p.stats && lane == 0 && ss.sorts > 0) {
+                atomicAdd(p.stats + 2 * (size_t)r + 1, (unsigned long long)ss.sorts);
+            }
+            return;
+        }
         __threadfence();
         for (uint32_t j = 0; j < S; ++j) {
             if (j == s) continue;
             uint64_t b[E];
             load_list_reversed<E>(b, lists + (size_t)j * KP, lane);
-            keep_best<E>(kept, b, lane);
+            keep_best<E>(kept_sorted, b, lane);
         }
-        write_row<E>(p.out_vals + (size_t)r * k, p.out_idx + (size_t)r * k, k, kept, lane);
+        const uint64_t kth = list_word_at<E>(kept_sorted, k - 1);
+        if (tau != 0ull && kth == 0ull) {
+            rerun = true;
+            start_rerun();
+            continue;
+        }
+        set_verdict(kVerdictExit);
+        break;
+    }
+    if (p.stats && lane == 0 && ss.sorts > 0) {
+        atomicAdd(p.stats + 2 * (size_t)r + 1, (unsigned long long)ss.sorts);
+    }
+    write_row<E>(p.out_vals + (size_t)r * k, p.out_idx + (size_t)r * k, k, kept_sorted, lane);
+    if constexpr (SPLIT) {
         // Leave this row's part of the workspace all zero, so the next call
         // may use the same memory with any shape.
+        uint64_t *lists = p.ws_lists + (size_t)r * S * KP;
         uint64_t zero[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) zero[e] = 0ull;

@@ -17,7 +17,7 @@ using topk::kWave;
 
 constexpr size_t kAlign = 256;
 constexpr int kDefaultWaves = 4;      // three streamer waves and one sorter wave
-constexpr int kDefaultWatermark = 512;
+constexpr int kDefaultWatermark = 256;
 constexpr int kMaxDevices = 64;
 constexpr int kAssumedCUs = 256;  // MI355X, used only when no device can be queried
 constexpr int64_t kMaxGroupsPerLaunch = (int64_t)1 << 22;
@@ -81,6 +81,7 @@ int check_options(const topk_options *o) {
     if (o->split < 0 || o->split > TOPK_MAX_SPLIT) return TOPK_ESPLIT;
     if (o->waves != 0 && (o->waves < 2 || o->waves > topk::kMaxWaves)) return TOPK_EINVAL;
     if (o->watermark < 0 || o->watermark > 4096) return TOPK_EINVAL;
+    if (o->flags & ~(TOPK_FLAG_NO_ESTIMATE | TOPK_FLAG_FORCE_RERUN)) return TOPK_EINVAL;
     return TOPK_OK;
 }
 
@@ -95,7 +96,9 @@ Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cu
     if (p.watermark < 64) p.watermark = 64;
     p.tray = p.watermark + kBlock;  // a tray below the mark never overflows in one block
     const int streamers = p.waves - 1;
-    p.lds = (size_t)8 * (size_t)(2 * streamers * p.tray);
+    // trays, then the sorter's candidate pool (list + one 1,024-word tray
+    // piece), gather buffer and key histogram
+    p.lds = (size_t)8 * (size_t)(2 * streamers * p.tray + list_words + 1024 + kWave) + 4 * 256;
 
     if (o && o->split) {
         p.split = o->split;
@@ -118,7 +121,7 @@ Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cu
 
 int run(const float *scores, const int32_t *lengths, int32_t rows, int32_t n, int32_t k,
         float *out_vals, int32_t *out_idx, const Plan &pl, void *ws, uint64_t seed,
-        unsigned long long *stats, hipStream_t stream) {
+        uint32_t flags, unsigned long long *stats, hipStream_t stream) {
     topk::SelectArgs a{};
     a.scores = scores;
     a.lengths = lengths;
@@ -131,6 +134,7 @@ int run(const float *scores, const int32_t *lengths, int32_t rows, int32_t n, in
     a.out_idx = out_idx;
     a.stats = stats;
     a.seed = seed;
+    a.flags = flags;
     if (pl.split > 1) {
         char *base = static_cast<char *>(ws);
         a.ws_ctrl = reinterpret_cast<uint64_t *>(base);
@@ -240,7 +244,8 @@ int topk_select_ex(const float *scores, const int32_t *lengths, int32_t rows, in
     Plan pl = make_plan(rows, n, k, opts, cus);
     if (pl.split > 1 && (!workspace || workspace_bytes < pl.ws_bytes)) return TOPK_EWORKSPACE;
     return run(scores, lengths, rows, n, k, out_vals, out_idx, pl, workspace,
-               opts ? opts->seed : 0, opts ? opts->stats : nullptr, (hipStream_t)stream);
+               opts ? opts->seed : 0, opts ? (uint32_t)opts->flags : 0u,
+               opts ? opts->stats : nullptr, (hipStream_t)stream);
 }
 
 int topk_select_split(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
@@ -267,7 +272,7 @@ int topk_select(const float *scores, const int32_t *lengths, int32_t rows, int32
         st = internal_workspace(pl.ws_bytes, (hipStream_t)stream, &ws);
         if (st != TOPK_OK) return st;
     }
-    return run(scores, lengths, rows, n, k, out_vals, out_idx, pl, ws, 0, nullptr,
+    return run(scores, lengths, rows, n, k, out_vals, out_idx, pl, ws, 0, 0u, nullptr,
                (hipStream_t)stream);
 }
 

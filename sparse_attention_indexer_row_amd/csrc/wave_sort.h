@@ -2,8 +2,9 @@
 //
 // Element i of a list lives in lane i / E, register i % E ("blocked" layout):
 // compare-exchange distances below E stay inside a lane's registers, larger
-// ones pair lane l with lane l ^ (distance / E) through a cross-lane permute.
-// No LDS traffic and no barrier: one wavefront sorts its own list.
+// ones pair lane l with lane l ^ (distance / E) through DPP or permlane-swap
+// lane exchanges.  No LDS traffic and no barrier: one wavefront sorts its
+// own list with VALU instructions only.
 //
 // Keep-the-best merge (kernelbench.com "DeepSeek V4.1 Flash",
 // bitonic-selection paragraph: the second list is compared in reverse
@@ -24,16 +25,42 @@ __device__ __forceinline__ uint32_t lane_id() {
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
-// Value of `v` in lane (lane ^ D).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Value of `v` in lane (lane ^ D), with VALU lane exchanges only:
+//   D = 1, 2     DPP quad_perm [1,0,3,2] / [2,3,0,1]
+//   D = 4        DPP row_half_mirror (l -> 7-l in 8) then quad_perm [3,2,1,0]
+//   D = 8        DPP row_ror:8 (rotating a 16-lane row by 8 is l ^ 8)
+//   D = 16, 32   v_permlane16_swap / v_permlane32_swap of the value with
+//                itself: the first result holds the lower half-group's data
+//                in both halves, the second the upper half-group's.
 template <int D>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v, uint32_t lane) {
-    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((lane ^ D) << 2), (int)v);
+    if constexpr (D == 1) {
+        return dpp_mov<0xB1>(v);
+    } else if constexpr (D == 2) {
+        return dpp_mov<0x4E>(v);
+    } else if constexpr (D == 4) {
+        return dpp_mov<0x1B>(dpp_mov<0x141>(v));
+    } else if constexpr (D == 8) {
+        return dpp_mov<0x128>(v);
+    } else if constexpr (D == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16u) ? p[0] : p[1];
+    } else {
+        static_assert(D == 32, "lane distance must be a power of two below 64");
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32u) ? p[0] : p[1];
+    }
 }
 
 template <int D>
 __device__ __forceinline__ uint64_t xor_lane64(uint64_t v, uint32_t lane) {
-    uint32_t lo = xor_lane<D>((uint32_t)v, lane);
-    uint32_t hi = xor_lane<D>((uint32_t)(v >> 32), lane);
+    const uint32_t lo = xor_lane<D>((uint32_t)v, lane);
+    const uint32_t hi = xor_lane<D>((uint32_t)(v >> 32), lane);
     return ((uint64_t)hi << 32) | lo;
 }
 
@@ -58,9 +85,9 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&a)[E], uint32_t lane) {
                 up = ((((lane * E) & SIZE) == 0) == ASC);
             }
             const uint64_t x = a[e], y = a[e2];
-            const uint64_t lo = umin64(x, y), hi = umax64(x, y);
-            a[e] = up ? lo : hi;
-            a[e2] = up ? hi : lo;
+            const bool swap = (x > y) == up;
+            a[e] = swap ? y : x;
+            a[e2] = swap ? x : y;
         }
     } else {
         constexpr int D = J / E;
@@ -76,7 +103,7 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&a)[E], uint32_t lane) {
         for (int e = 0; e < E; ++e) {
             const uint64_t x = a[e];
             const uint64_t y = xor_lane64<D>(x, lane);
-            a[e] = take_min ? umin64(x, y) : umax64(x, y);
+            a[e] = ((x < y) == take_min) ? x : y;
         }
     }
 }

@@ -81,6 +81,8 @@ def test_split_and_ex_argument_errors(lib):
     assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_EINVAL
     o.watermark, o.split = 0, 2000
     assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_ESPLIT
+    o.split, o.flags = 0, 4
+    assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_EINVAL
 
 
 def test_workspace_init_and_probe_argument_errors(lib):
@@ -112,7 +114,7 @@ def test_plan_list_sizes_and_lds(lib):
                      (2048, 2048)]:
         p = _plan(lib, 4, 1 << 16, k)
         assert p.list_words == words
-        assert p.lds_bytes == 8 * 2 * (p.waves - 1) * p.tray_words
+        assert p.lds_bytes == 8 * (2 * (p.waves - 1) * p.tray_words + words + 1024 + 64) + 4 * 256
         assert p.lds_bytes <= 160 * 1024
         assert p.tray_words == p.watermark + 1024
 

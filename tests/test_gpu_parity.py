@@ -57,6 +57,15 @@ def test_workload_full_size(name):
     check(w.scores, w.k, w.lengths, what=name)
 
 
+@pytest.mark.parametrize("flags", [1, 2], ids=["no-estimate", "forced-rerun"])
+@pytest.mark.parametrize("name", ["adverse", "ragged"])
+def test_workload_full_size_fallback_paths(name, flags):
+    # flags=1 filters with exact bounds only; flags=2 makes the sampled
+    # estimate admit nothing, so every estimated row is streamed again.
+    w = workloads.make(name)
+    check(w.scores, w.k, w.lengths, what=f"{name} flags={flags}", flags=flags)
+
+
 def test_ragged_rows_shorter_than_k():
     # the ragged workload draws few rows below k=2048; force several
     w = workloads.ragged(rows=40, n=8192, k=2048, seed=11)
@@ -142,6 +151,9 @@ SCHEDULES = [
     dict(seed=3, split=4, waves=2), dict(seed=4, split=16, waves=3), dict(seed=5, split=64),
     dict(seed=6, split=1, watermark=64), dict(seed=7, split=3, watermark=2048),
     dict(seed=8, split=256, waves=2), dict(seed=9, split=1, waves=2, watermark=100),
+    dict(seed=10, split=1, flags=1), dict(seed=11, split=4, flags=1),
+    dict(seed=12, split=1, flags=2), dict(seed=13, split=4, flags=2),
+    dict(seed=14, split=7, waves=3, flags=2),
 ]
 
 
