@@ -136,7 +136,7 @@ __device__ __forceinline__ void lds_store_u32(uint32_t *p, uint32_t v, uint32_t 
 // of every quarter that reaches the per-score tests is inserted into the
 // lane's running list of its E best keys, lk[0] >= ... >= lk[E-1]
 // (branch-free max/min insertion); each entry is a distinct element.
-template <int E>
+template <int E, bool LANE_BOUNDS>
 __device__ __forceinline__ uint32_t admit_block(uint64_t *tray, uint32_t cnt, uint64_t T,
                                                 int32_t tb, const float4 (&x)[kLoadsPerBlock],
                                                 uint32_t vbase, uint32_t off0, uint32_t vend,
@@ -146,7 +146,18 @@ __device__ __forceinline__ uint32_t admit_block(uint64_t *tray, uint32_t cnt, ui
         const int32_t v4[4] = {__float_as_int(x[u].x), __float_as_int(x[u].y),
                                __float_as_int(x[u].z), __float_as_int(x[u].w)};
         const int32_t m4 = max(max(v4[0], v4[1]), max(v4[2], v4[3]));
-        if (__ballot(ragged || m4 >= tb) == 0ull) continue;
+        if (__ballot(ragged || m4 >= tb) == 0ull) {
+            if (LANE_BOUNDS && !ragged) {
+                uint32_t v = order_key((uint32_t)m4);
+#pragma unroll
+                for (int i = 0; i < E; ++i) {
+                    const uint32_t hi = max(lk[i], v);
+                    v = min(lk[i], v);
+                    lk[i] = hi;
+                }
+            }
+            continue;
+        }
         const uint32_t g0 = vbase + (uint32_t)u * 256u + lane * 4u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -163,7 +174,7 @@ __device__ __forceinline__ uint32_t admit_block(uint64_t *tray, uint32_t cnt, ui
                 cnt += (uint32_t)__popcll(m);
             }
         }
-        if (!ragged) {
+        if (LANE_BOUNDS && !ragged) {
             // The quarter's largest score is a real element of this lane:
             // fold it into the lane's running list of its E best keys.
             uint32_t v = order_key((uint32_t)m4);
@@ -595,8 +606,8 @@ __device__ __forceinline__ RowGeom row_geometry(const SelectArgs &p, uint32_t r)
 // 11:47-12:10: the shipped kernel starts its scan already holding a working
 // threshold).  512 aligned 4-score groups are drawn one per stratum of the
 // row's aligned groups, at a seeded position inside the stratum; the
-// estimate is the j-th best sampled word with j = ceil(10 k 2048 / L), so
-// about 10k scores of the row lie above it.  It is not a bound: whether it
+// estimate is about the j-th best of those 2,048 scores with
+// j = ceil(10 k 2048 / L), so roughly 10k scores of the row lie above it.  It is not a bound: whether it
 // was low enough is checked at the end (at least k scores admitted), and the
 // row is streamed again without it otherwise.  Returns 0 (no estimate) for
 // rows too short for it to pay.
@@ -606,24 +617,8 @@ constexpr uint32_t kEstimateMargin = 10;
 constexpr uint32_t kFlagNoEstimate = 1u;
 constexpr uint32_t kFlagForceRerun = 2u;
 
-template <int D>
-__device__ __forceinline__ uint64_t min_step(uint64_t v, uint32_t lane) {
-    return umin64(v, xor_lane64<D>(v, lane));
-}
-
-__device__ __forceinline__ uint64_t wave_min64(uint64_t v, uint32_t lane) {
-    v = min_step<32>(v, lane);
-    v = min_step<16>(v, lane);
-    v = min_step<8>(v, lane);
-    v = min_step<4>(v, lane);
-    v = min_step<2>(v, lane);
-    v = min_step<1>(v, lane);
-    return uniform64(v);
-}
-
 __device__ __noinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t seed, uint32_t r,
-                                                    uint32_t k, uint32_t flags, uint32_t *hist,
-                                                    uint64_t *gath, uint32_t lane) {
+                                                    uint32_t k, uint32_t flags, uint32_t lane) {
     if ((flags & kFlagNoEstimate) || g.L == 0u) return 0ull;
     const uint64_t jn = ((uint64_t)kEstimateMargin * k * kSampleWords + g.L - 1) / g.L;
     if (jn > kSampleWords / 8) return 0ull;
@@ -650,25 +645,29 @@ __device__ __noinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t se
             if (t < 4) a[t * 4 + c] = w; else b[(t - 4) * 4 + c] = w;
         }
     }
-    uint32_t n = 0;
-    uint64_t lmx = 0ull, lmn = ~0ull;
+    // The j-th best of the 64 lane maxima: at most the j-th best sampled
+    // word (the maxima are a subset of the sample), so it admits at least as
+    // much, and it costs one 64-word register sort.
+    uint64_t lmx = 0ull;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        n += (uint32_t)__popcll(__ballot(a[j] != 0ull)) + (uint32_t)__popcll(__ballot(b[j] != 0ull));
-        lmx = umax64(lmx, umax64(a[j], b[j]));
-        lmn = umin64(lmn, umin64(a[j] ? a[j] : ~0ull, b[j] ? b[j] : ~0ull));
-    }
-    if (n < 2u * (uint32_t)jn) return 0ull;
-    const uint64_t hi = wave_max64(lmx, lane);
-    const uint64_t lo = wave_min64(lmn, lane);
-    if (lo >= hi) return 0ull;
-    return select_rth(a, b, (uint32_t)jn, lo, hi, hist, gath, lane);
+    for (int j = 0; j < 16; ++j) lmx = umax64(lmx, umax64(a[j], b[j]));
+    const uint32_t have = (uint32_t)__popcll(__ballot(lmx != 0ull));
+    if (have < 2u * (uint32_t)jn) return 0ull;
+    uint64_t v[1] = {lmx};
+    wave_sort<1, false>(v, lane);
+    return list_word_at<1>(v, (uint32_t)jn - 1u);
 }
 
 // Streams this wave's share of a row's blocks once: positions q, q+Q, ... of
 // the visit order.  Scores whose word beats max(threshold, estimate) go to
 // the tray; full trays are published to the sorter.  Returns the number of
 // scores that entered a tray.
+//
+// Per block the wave does little besides the loads: the visit order is
+// computed 64 blocks ahead by the vector unit (one permutation step per
+// lane) and read back with one v_readlane; interior blocks are loaded from a
+// wave-uniform base plus a fixed per-lane offset; the shared threshold is
+// read from LDS early and folded in after the block's tests.
 template <int E, bool SPLIT>
 __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOrder &ord,
                                                  uint32_t q, uint32_t Q, uint64_t tau,
@@ -684,6 +683,15 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
     for (int i = 0; i < E; ++i) lk[i] = 0u;
     uint64_t *tray = trays + (size_t)(2 * w) * CW;
     if (mine == 0) return 0u;
+    const bool lane_bounds = tau == 0ull;   // the estimate, when present, is far tighter
+
+    // Visit list: lane j holds the block of this stream's step c0 + j.
+    uint32_t c0 = 0;
+    auto visit_chunk = [&](uint32_t first) __attribute__((always_inline)) {
+        const uint32_t t = first + lane;
+        return t < mine ? visit_block(ord, q + t * Q) : 0u;
+    };
+    uint32_t vis = visit_chunk(0);
 
     float4 buf[D][kLoadsPerBlock];
     uint32_t bid[D];
@@ -694,18 +702,29 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
     auto issue = [&](float4 (&dst)[kLoadsPerBlock], uint32_t &b_out, uint64_t &g_out,
                      uint32_t t) __attribute__((always_inline)) {
         const uint32_t tt = t < mine ? t : mine - 1u;
-        const uint32_t b = visit_block(ord, q + tt * Q);
+        if (tt - c0 >= (uint32_t)kWave) {   // next chunk of the visit list
+            c0 = tt & ~(uint32_t)(kWave - 1);
+            vis = visit_chunk(c0);
+        }
+        const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)vis, (int)(tt - c0));
         b_out = b;
         if constexpr (SPLIT) {
             g_out = __hip_atomic_load(gT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         const uint32_t vbase = b * (uint32_t)kBlock;
-        const bool ragged = vbase < g.off0 || vbase + (uint32_t)kBlock > g.vend;
+        if (vbase >= g.off0 && vbase + (uint32_t)kBlock <= g.vend) {
+            const float *bp = g.abase + vbase;
 #pragma unroll
-        for (int u = 0; u < kLoadsPerBlock; ++u) {
-            uint32_t gp = vbase + (uint32_t)u * 256u + lane * 4u;
-            if (ragged) gp = gp > g.last_group ? g.last_group : gp;  // stay on a valid group
-            dst[u] = *reinterpret_cast<const float4 *>(g.abase + gp);
+            for (int u = 0; u < kLoadsPerBlock; ++u) {
+                dst[u] = *reinterpret_cast<const float4 *>(bp + u * 256 + lane * 4u);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kLoadsPerBlock; ++u) {
+                uint32_t gp = vbase + (uint32_t)u * 256u + lane * 4u;
+                gp = gp > g.last_group ? g.last_group : gp;   // stay on a valid group
+                dst[u] = *reinterpret_cast<const float4 *>(g.abase + gp);
+            }
         }
     };
 #pragma unroll
@@ -715,6 +734,8 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const uint32_t t = t0 + (uint32_t)d;
+            const uint64_t shared_T = __hip_atomic_load(sT, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_WORKGROUP);
             if (t < mine) {
                 if constexpr (SPLIT) T = umax64(T, uniform64(gbuf[d]));
                 const uint64_t F = umax64(T, tau);
@@ -722,10 +743,15 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                 const uint32_t vbase = bid[d] * (uint32_t)kBlock;
                 const bool ragged = vbase < g.off0 || vbase + (uint32_t)kBlock > g.vend;
                 const uint32_t before = cnt;
-                cnt = admit_block<E>(tray, cnt, F, tb, buf[d], vbase, g.off0, g.vend, ragged, lk,
-                                     lane);
+                if (lane_bounds) {
+                    cnt = admit_block<E, true>(tray, cnt, F, tb, buf[d], vbase, g.off0, g.vend,
+                                               ragged, lk, lane);
+                } else {
+                    cnt = admit_block<E, false>(tray, cnt, F, tb, buf[d], vbase, g.off0, g.vend,
+                                                ragged, lk, lane);
+                }
                 entered += cnt - before;
-                if (cnt != before) {
+                if (lane_bounds && cnt != before) {
                     // 64*E >= k distinct elements have keys >= the smallest
                     // lane's E-th best key: a lower bound of the k-th best.
                     const uint32_t kb = wave_min32(lk[E - 1], lane);
@@ -740,7 +766,7 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                 }
             }
             issue(buf[d], bid[d], gbuf[d], t + (uint32_t)D);
-            T = umax64(T, lds_load_word(sT));
+            T = umax64(T, uniform64(shared_T));
             if (cnt >= Wm) {
                 publish_tray(&fill[w][cur], cnt, lane);
                 cur ^= 1u;
@@ -868,7 +894,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p) {
     uint64_t *pool = trays + (size_t)(2 * NS) * CW;            // [PoolCfg<E>::cap]
     uint64_t *gath = pool + PoolCfg<E>::cap;                    // [64]
     uint32_t *hist = reinterpret_cast<uint32_t *>(gath + kWave);  // [256]
-    const uint64_t tau = estimate_threshold(g, p.seed, r, k, p.flags, hist, gath, lane);
+    const uint64_t tau = estimate_threshold(g, p.seed, r, k, p.flags, lane);
     if (lane == 0) {
         s_tau = tau;
         __hip_atomic_store(&s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
