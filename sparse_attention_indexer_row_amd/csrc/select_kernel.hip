@@ -129,60 +129,69 @@ __device__ __forceinline__ void lds_store_u32(uint32_t *p, uint32_t v, uint32_t 
 // ---------------------------------------------------------------------------
 // Streamer waves: read blocks, test, compact survivors into a tray.
 
+// Inserts key v into a lane's running list of its E best keys,
+// lk[0] >= ... >= lk[E-1] (branch-free max/min insertion).
+template <int E>
+__device__ __forceinline__ void insert_lane_key(uint32_t (&lk)[E], uint32_t v) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const uint32_t hi = max(lk[i], v);
+        v = min(lk[i], v);
+        lk[i] = hi;
+    }
+}
+
 // Test and tray compaction of one block already in registers.  Cheap tests
-// first: per quarter (the lane's 4 scores of one dwordx4), then per score,
-// each on the integer bits against `tb`; only score slots where some lane
-// passes build the packed word and take the exact 64-bit test.  The maximum
-// of every quarter that reaches the per-score tests is inserted into the
-// lane's running list of its E best keys, lk[0] >= ... >= lk[E-1]
-// (branch-free max/min insertion); each entry is a distinct element.
-template <int E, bool LANE_BOUNDS>
+// first, all on the integer bits against `tb`: the lane's whole block (when
+// an estimate filters the stream, so most blocks stop there), then each
+// quarter (the lane's 4 scores of one dwordx4), then each score slot; only
+// slots where some lane passes build the packed word and take the exact
+// 64-bit test.  Lane predicates are combined with bitwise operators, so each
+// test is one compare and one scalar branch on its ballot.
+//
+// RAGGED blocks straddle the row's start or end: there a slot outside the
+// row gets word 0, which fails the exact test (T >= 0).  With LANE_BOUNDS the
+// maximum of every quarter of an interior block is inserted into the lane's
+// running list of its E best keys; each entry is a distinct element.
+template <int E, bool LANE_BOUNDS, bool RAGGED>
 __device__ __forceinline__ uint32_t admit_block(uint64_t *tray, uint32_t cnt, uint64_t T,
                                                 int32_t tb, const float4 (&x)[kLoadsPerBlock],
                                                 uint32_t vbase, uint32_t off0, uint32_t vend,
-                                                bool ragged, uint32_t (&lk)[E], uint32_t lane) {
+                                                uint32_t (&lk)[E], uint32_t lane) {
+    int32_t v[kLoadsPerBlock][4];
+    int32_t m4[kLoadsPerBlock];
 #pragma unroll
     for (int u = 0; u < kLoadsPerBlock; ++u) {
-        const int32_t v4[4] = {__float_as_int(x[u].x), __float_as_int(x[u].y),
-                               __float_as_int(x[u].z), __float_as_int(x[u].w)};
-        const int32_t m4 = max(max(v4[0], v4[1]), max(v4[2], v4[3]));
-        if (__ballot(ragged || m4 >= tb) == 0ull) {
-            if (LANE_BOUNDS && !ragged) {
-                uint32_t v = order_key((uint32_t)m4);
+        v[u][0] = __float_as_int(x[u].x);
+        v[u][1] = __float_as_int(x[u].y);
+        v[u][2] = __float_as_int(x[u].z);
+        v[u][3] = __float_as_int(x[u].w);
+        m4[u] = max(max(v[u][0], v[u][1]), max(v[u][2], v[u][3]));
+    }
+    if constexpr (LANE_BOUNDS && !RAGGED) {
 #pragma unroll
-                for (int i = 0; i < E; ++i) {
-                    const uint32_t hi = max(lk[i], v);
-                    v = min(lk[i], v);
-                    lk[i] = hi;
-                }
-            }
-            continue;
-        }
+        for (int u = 0; u < kLoadsPerBlock; ++u) insert_lane_key<E>(lk, order_key((uint32_t)m4[u]));
+    }
+    if constexpr (!LANE_BOUNDS && !RAGGED) {
+        const int32_t m = max(max(m4[0], m4[1]), max(m4[2], m4[3]));
+        if (__ballot(m >= tb) == 0ull) return cnt;
+    }
+#pragma unroll
+    for (int u = 0; u < kLoadsPerBlock; ++u) {
+        if (!RAGGED && __ballot(m4[u] >= tb) == 0ull) continue;
         const uint32_t g0 = vbase + (uint32_t)u * 256u + lane * 4u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint32_t g = g0 + (uint32_t)c;
-            const bool valid = !ragged || (g >= off0 && g < vend);
-            const bool pre = valid && v4[c] >= tb;
+            const bool pre = v[u][c] >= tb;
             if (__ballot(pre) == 0ull) continue;
-            const uint32_t key = order_key((uint32_t)v4[c]);
-            const uint64_t w = pack_word(key, g - off0);
-            const bool pass = pre && (w > T);
-            const uint64_t m = __ballot(pass);
-            if (m) {
-                if (pass) tray[cnt + mbcnt64(m)] = w;
-                cnt += (uint32_t)__popcll(m);
-            }
-        }
-        if (LANE_BOUNDS && !ragged) {
-            // The quarter's largest score is a real element of this lane:
-            // fold it into the lane's running list of its E best keys.
-            uint32_t v = order_key((uint32_t)m4);
-#pragma unroll
-            for (int i = 0; i < E; ++i) {
-                const uint32_t hi = max(lk[i], v);
-                v = min(lk[i], v);
-                lk[i] = hi;
+            const uint32_t g = g0 + (uint32_t)c;
+            uint64_t w = pack_word(order_key((uint32_t)v[u][c]), g - off0);
+            if constexpr (RAGGED) w = ((g >= off0) & (g < vend)) ? w : 0ull;
+            const bool pass = pre & (w > T);
+            const uint64_t mk = __ballot(pass);
+            if (mk != 0ull) {
+                if (pass) tray[cnt + mbcnt64(mk)] = w;
+                cnt += (uint32_t)__popcll(mk);
             }
         }
     }
@@ -741,14 +750,17 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                 const uint64_t F = umax64(T, tau);
                 const int32_t tb = prefilter_bound(F);
                 const uint32_t vbase = bid[d] * (uint32_t)kBlock;
-                const bool ragged = vbase < g.off0 || vbase + (uint32_t)kBlock > g.vend;
+                const bool ragged = (vbase < g.off0) | (vbase + (uint32_t)kBlock > g.vend);
                 const uint32_t before = cnt;
-                if (lane_bounds) {
-                    cnt = admit_block<E, true>(tray, cnt, F, tb, buf[d], vbase, g.off0, g.vend,
-                                               ragged, lk, lane);
+                if (ragged) {
+                    cnt = admit_block<E, false, true>(tray, cnt, F, tb, buf[d], vbase, g.off0,
+                                                      g.vend, lk, lane);
+                } else if (lane_bounds) {
+                    cnt = admit_block<E, true, false>(tray, cnt, F, tb, buf[d], vbase, g.off0,
+                                                      g.vend, lk, lane);
                 } else {
-                    cnt = admit_block<E, false>(tray, cnt, F, tb, buf[d], vbase, g.off0, g.vend,
-                                                ragged, lk, lane);
+                    cnt = admit_block<E, false, false>(tray, cnt, F, tb, buf[d], vbase, g.off0,
+                                                       g.vend, lk, lane);
                 }
                 entered += cnt - before;
                 if (lane_bounds && cnt != before) {
