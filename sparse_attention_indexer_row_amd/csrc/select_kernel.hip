@@ -480,7 +480,7 @@ __device__ __forceinline__ void raise_threshold(SorterState &ss, uint64_t nt, ui
 // sets the threshold to the k-th best.  Pool words are loaded into registers
 // (64*E + kPiece*64 at most) and ranked by select_rth.
 template <int E, bool SPLIT>
-__device__ __noinline__ void prune_pool(SorterState &ss, uint64_t *pool, uint64_t *sT,
+__device__ __forceinline__ void prune_pool(SorterState &ss, uint64_t *pool, uint64_t *sT,
                                         uint64_t *gT, uint32_t k, uint32_t *hist, uint64_t *gath,
                                         uint32_t lane) {
     uint64_t a[E], b[kPiece];
@@ -626,7 +626,7 @@ constexpr uint32_t kEstimateMargin = 10;
 constexpr uint32_t kFlagNoEstimate = 1u;
 constexpr uint32_t kFlagForceRerun = 2u;
 
-__device__ __noinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t seed, uint32_t r,
+__device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t seed, uint32_t r,
                                                     uint32_t k, uint32_t flags, uint32_t lane) {
     if ((flags & kFlagNoEstimate) || g.L == 0u) return 0ull;
     const uint64_t jn = ((uint64_t)kEstimateMargin * k * kSampleWords + g.L - 1) / g.L;
@@ -833,6 +833,7 @@ __device__ __forceinline__ void reset_sorter(SorterState &ss, uint32_t *hist, ui
 }
 
 constexpr uint32_t kVerdictExit = 1u;
+constexpr uint32_t kMergeBatch = 3;   // segment lists in flight during the leader's merge
 constexpr uint32_t kVerdictRerun = 2u;
 
 template <int E, bool SPLIT>
@@ -949,13 +950,15 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p) {
             break;
         }
         // Split row: publish this segment's list and take a ticket; the last
-        // of the row's segments to arrive merges every list.
+        // of the row's segments to arrive merges every list.  One release
+        // fence orders the list stores before the ticket; only the leader
+        // needs the matching acquire.
         uint64_t *lists = p.ws_lists + (size_t)r * S * KP;
         store_list<E>(lists + (size_t)s * KP, kept_sorted, lane);
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         uint32_t old = 0;
         if (lane == 0) {
-            old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         old = __builtin_amdgcn_readfirstlane((int)old);
         if (old != S - 1u) {
@@ -965,12 +968,31 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p) {
             }
             return;
         }
-        __threadfence();
-        for (uint32_t j = 0; j < S; ++j) {
-            if (j == s) continue;
-            uint64_t b[E];
-            load_list_reversed<E>(b, lists + (size_t)j * KP, lane);
-            keep_best<E>(kept_sorted, b, lane);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // The leader's own list is not read again: clear it now.  The other
+        // lists are fetched kMergeBatch at a time (all loads of a batch in
+        // flight together), merged, and cleared behind the merge, so the
+        // workspace is all zero again when the call ends.
+        uint64_t zero[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) zero[e] = 0ull;
+        store_list<E>(lists + (size_t)s * KP, zero, lane);
+        const uint32_t others = S - 1u;
+        for (uint32_t t = 0; t < others; t += kMergeBatch) {
+            uint64_t nb[kMergeBatch][E];
+#pragma unroll
+            for (uint32_t a = 0; a < kMergeBatch; ++a) {
+                const uint32_t j = t + a < s ? t + a : t + a + 1u;   // skip the leader's own
+                if (t + a < others) load_list_reversed<E>(nb[a], lists + (size_t)j * KP, lane);
+            }
+#pragma unroll
+            for (uint32_t a = 0; a < kMergeBatch; ++a) {
+                const uint32_t j = t + a < s ? t + a : t + a + 1u;
+                if (t + a < others) {
+                    keep_best<E>(kept_sorted, nb[a], lane);
+                    store_list<E>(lists + (size_t)j * KP, zero, lane);
+                }
+            }
         }
         const uint64_t kth = list_word_at<E>(kept_sorted, k - 1);
         if (tau != 0ull && kth == 0ull) {
@@ -986,13 +1008,9 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p) {
     }
     write_row<E>(p.out_vals + (size_t)r * k, p.out_idx + (size_t)r * k, k, kept_sorted, lane);
     if constexpr (SPLIT) {
-        // Leave this row's part of the workspace all zero, so the next call
-        // may use the same memory with any shape.
-        uint64_t *lists = p.ws_lists + (size_t)r * S * KP;
-        uint64_t zero[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) zero[e] = 0ull;
-        for (uint32_t j = 0; j < S; ++j) store_list<E>(lists + (size_t)j * KP, zero, lane);
+        // Leave this row's part of the workspace all zero (the lists were
+        // cleared behind the merge), so the next call may use the same
+        // memory with any shape.
         if (lane == 0) {
             __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(gT, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
