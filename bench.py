@@ -52,6 +52,106 @@ def load_traffic(workload: str):
     return t
 
 
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -T -f csv -d {d} -o trace -- "
+             "python3 bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline --no-probe",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -T -f csv -d {d} -o fetch -- "
+             "python3 bench.py --workload {w} --profile-run --steps 5 --warmup 2",
+    "write": "rocprofv3 --pmc WRITE_SIZE -T -f csv -d {d} -o write -- "
+             "python3 bench.py --workload {w} --profile-run --steps 5 --warmup 2",
+}
+COPY_BYTES = 1 << 30   # one probe copy in --profile-run: 1 GiB read, 1 GiB written
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(workload: str, trace_dir: str, fetch_dir: str, write_dir: str) -> int:
+    """Turns the three rocprofv3 runs of PROFILE_COMMANDS into the committed
+    summaries: profiles/topk_select_<workload>_rocprof.md (kernel statistics)
+    and profiles/topk_select_<workload>_traffic.json (HBM bytes per launch,
+    scaled by the counters' reading for the 1 GiB probe copy)."""
+    import numpy as np
+
+    from sparse_attention_indexer_row_amd import workloads
+
+    stats = _csv_rows(os.path.join(trace_dir, "trace_kernel_stats.csv"))
+    trace = _csv_rows(os.path.join(trace_dir, "trace_kernel_trace.csv"))
+    sel = [r for r in stats if r["Name"].startswith("select_kernel")]
+    if not sel:
+        print("no select_kernel in the kernel statistics", file=sys.stderr)
+        return 1
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            for r in trace if r["Kernel_Name"].startswith("select_kernel")]
+
+    def counter(dirname, prefix, name):
+        rows = _csv_rows(os.path.join(dirname, f"{prefix}_counter_collection.csv"))
+        pick = lambda kn: [float(r["Counter_Value"]) for r in rows
+                           if r["Kernel_Name"].startswith(kn) and r["Counter_Name"] == name]
+        return pick("select_kernel"), pick("probe_copy_kernel")
+
+    f_sel, f_copy = counter(fetch_dir, "fetch", "FETCH_SIZE")
+    w_sel, w_copy = counter(write_dir, "write", "WRITE_SIZE")
+    if not (f_sel and f_copy and w_sel and w_copy):
+        print("counter files lack select_kernel or probe_copy_kernel rows", file=sys.stderr)
+        return 1
+    fetch_scale = (COPY_BYTES / 1024) / float(np.mean(f_copy))
+    write_scale = (COPY_BYTES / 1024) / float(np.mean(w_copy))
+    fetch_b = float(np.mean(f_sel)) * 1024 * fetch_scale
+    write_b = float(np.mean(w_sel)) * 1024 * write_scale
+    w = workloads.make(workload)
+    algo_read = 4 * w.valid_elements()
+    algo_write = 8 * w.rows * w.k
+    traffic = {
+        "kernel": "select_kernel", "workload": workload,
+        "kernel_source_sha256": kernel_source_hash(),
+        "fetch_kib_per_dispatch": round(float(np.mean(f_sel)), 3),
+        "write_kib_per_dispatch": round(float(np.mean(w_sel)), 3),
+        "copy_bytes": COPY_BYTES,
+        "copy_fetch_kib": round(float(np.mean(f_copy)), 3),
+        "copy_write_kib": round(float(np.mean(w_copy)), 3),
+        "fetch_scale": round(fetch_scale, 5), "write_scale": round(write_scale, 5),
+        "bytes_per_launch": int(round(fetch_b + write_b)),
+        "fetch_bytes_per_launch": int(round(fetch_b)),
+        "write_bytes_per_launch": int(round(write_b)),
+        "algorithmic_read_bytes": algo_read, "algorithmic_write_bytes": algo_write,
+        "commands": {k: v.format(d="<dir>", w=workload) for k, v in PROFILE_COMMANDS.items()},
+    }
+    os.makedirs(TRAFFIC_DIR, exist_ok=True)
+    with open(os.path.join(TRAFFIC_DIR, f"topk_select_{workload}_traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    lines = [f"# select_kernel, workload `{workload}`: rocprofv3 summary", "",
+             f"Workload: {w.description}.", "",
+             "Commands (run from the repository root; `<dir>` is any output directory):", ""]
+    lines += [f"    {v.format(d='<dir>', w=workload)}" for v in PROFILE_COMMANDS.values()]
+    lines += ["", "Kernel statistics (`--kernel-trace --stats`):", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    lines += ["", f"select_kernel dispatch durations: mean {np.mean(durs):.1f} us, median "
+              f"{np.median(durs):.1f} us over {len(durs)} dispatches (includes the warm-up and "
+              f"parity launches).", "",
+              "HBM traffic per select_kernel dispatch (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`):", "",
+              f"- FETCH_SIZE {traffic['fetch_kib_per_dispatch']} KiB; the 1 GiB probe copy reads as "
+              f"{traffic['copy_fetch_kib']} KiB, scale {traffic['fetch_scale']} -> "
+              f"{fetch_b / 1e6:.1f} MB read (algorithmic {algo_read / 1e6:.1f} MB).",
+              f"- WRITE_SIZE {traffic['write_kib_per_dispatch']} KiB; the 1 GiB probe copy writes as "
+              f"{traffic['copy_write_kib']} KiB, scale {traffic['write_scale']} -> "
+              f"{write_b / 1e6:.2f} MB written (algorithmic {algo_write / 1e6:.2f} MB of outputs).",
+              f"- Total {traffic['bytes_per_launch'] / 1e6:.1f} MB per launch, "
+              f"{traffic['bytes_per_launch'] / (algo_read + algo_write):.3f} x the algorithmic bytes.",
+              "", f"Kernel sources: sha256 {traffic['kernel_source_sha256']}.", ""]
+    with open(os.path.join(TRAFFIC_DIR, f"topk_select_{workload}_rocprof.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+    return 0
+
+
 def host_cores() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -73,7 +173,11 @@ def main() -> int:
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the timed selection launches (for rocprofv3 counter runs)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summaries from the rocprofv3 runs of PROFILE_COMMANDS")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        return summarize_profiles(args.workload, *args.summarize_profiles)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -154,6 +258,17 @@ def main() -> int:
           file=sys.stderr, flush=True)
 
     if args.profile_run:
+        # Counter calibration: a plain copy of a known size (1 GiB read, 1 GiB
+        # written) profiled in the same run, so HBM byte counters can be
+        # scaled by what they read for known traffic.
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            api.topk_probe_copy(src, dst, stream=stream)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 x {src.numel() * 4} bytes", file=sys.stderr, flush=True)
         return 0
 
     value = read_bytes / (ms_per_step * 1e-3) / 1e9
