@@ -613,64 +613,68 @@ __device__ __forceinline__ RowGeom row_geometry(const SelectArgs &p, uint32_t r)
 // Flash", transcript 10:57-11:09, on LightTopK: sample a small subset to
 // estimate a threshold, filter online, still return the exact answer; and
 // 11:47-12:10: the shipped kernel starts its scan already holding a working
-// threshold).  512 aligned 4-score groups are drawn one per stratum of the
-// row's aligned groups, at a seeded position inside the stratum; the
-// estimate is about the j-th best of those 2,048 scores with
-// j = ceil(10 k 2048 / L), so roughly 10k scores of the row lie above it.  It is not a bound: whether it
-// was low enough is checked at the end (at least k scores admitted), and the
-// row is streamed again without it otherwise.  Returns 0 (no estimate) for
-// rows too short for it to pay.
-constexpr uint32_t kSampleGroups = 512;
-constexpr uint32_t kSampleWords = 4 * kSampleGroups;
+// threshold).  Lane j reads one aligned 128-byte line (32 consecutive
+// scores) at a seeded place inside stratum j of the row's 64 equal strata:
+// 2,048 scores for 64 line fetches.  The estimate is the j-th best of the 64
+// lane maxima with j = ceil(10 k 2048 / L), so roughly 10k scores of the row
+// lie above it.  A lane contributes one maximum however many of the row's
+// best scores its line holds, so crowding the best scores into one place
+// cannot lift the estimate above the k-th best.  It is not a bound: whether
+// it was low enough is checked at the end (at least k scores admitted), and
+// the row is streamed again without it otherwise.  Returns 0 (no estimate)
+// for rows too short for it to pay.
+constexpr uint32_t kSampleSpan = 32;                      // scores per lane, one 128-byte line
+constexpr uint32_t kSampleWords = kWave * kSampleSpan;    // 2,048
 constexpr uint32_t kEstimateMargin = 10;
 constexpr uint32_t kFlagNoEstimate = 1u;
 constexpr uint32_t kFlagForceRerun = 2u;
 
 __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t seed, uint32_t r,
-                                                    uint32_t k, uint32_t flags, uint32_t lane) {
+                                                       uint32_t k, uint32_t flags, uint32_t lane) {
     if ((flags & kFlagNoEstimate) || g.L == 0u) return 0ull;
     const uint64_t jn = ((uint64_t)kEstimateMargin * k * kSampleWords + g.L - 1) / g.L;
-    if (jn > kSampleWords / 8) return 0ull;
+    if (jn > kWave / 2) return 0ull;
     if (flags & kFlagForceRerun) return ~0ull;  // admits nothing: forces the rerun path
-    const uint32_t ngroups = g.last_group / 4u + 1u;
+    // Line m starts at virtual position 32m - mis, 128-byte aligned in memory;
+    // lines first .. last_end-1 lie wholly inside the valid positions.
+    const uint32_t mis = (uint32_t)(((uintptr_t)g.abase >> 2) & (kSampleSpan - 1u));
+    const uint32_t first = (g.off0 + mis + kSampleSpan - 1u) / kSampleSpan;
+    const uint32_t last_end = (g.vend + mis) / kSampleSpan;
+    if (last_end < first + (uint32_t)kWave) return 0ull;
+    const uint32_t nlines = last_end - first;
+    const uint32_t l0 = first + (uint32_t)((uint64_t)lane * nlines / kWave);
+    const uint32_t l1 = first + (uint32_t)((uint64_t)(lane + 1u) * nlines / kWave);
     const uint64_t key = splitmix64(seed ^ 0x5851F42D4C957F2Dull ^ ((uint64_t)r << 20));
-    uint64_t a[16], b[16];
+    const uint32_t m = l0 + mix32((uint32_t)key ^ (lane * 0x9E3779B1u) ^ (uint32_t)(key >> 32)) %
+                                (l1 - l0);
+    const uint32_t gv = m * kSampleSpan - mis;
+    const float4 *src = reinterpret_cast<const float4 *>(g.abase + gv);
+    float4 x[kSampleSpan / 4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const uint32_t si = (uint32_t)t * kWave + lane;               // stratum
-        const uint32_t g0 = (uint32_t)((uint64_t)si * ngroups / kSampleGroups);
-        const uint32_t g1 = (uint32_t)((uint64_t)(si + 1) * ngroups / kSampleGroups);
-        const uint32_t span = g1 > g0 ? g1 - g0 : 1u;
-        const uint32_t grp = g0 + mix32((uint32_t)key ^ (si * 0x9E3779B1u) ^ (uint32_t)(key >> 32)) % span;
-        const uint32_t gs = grp * 4u;
-        const float4 x = *reinterpret_cast<const float4 *>(g.abase + gs);
-        const float v4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t gc = gs + (uint32_t)c;
-            const bool valid = g1 > g0 && gc >= g.off0 && gc < g.vend;
-            const uint64_t w = valid ? pack_word(order_key(__float_as_uint(v4[c])), gc - g.off0)
-                                     : 0ull;
-            if (t < 4) a[t * 4 + c] = w; else b[(t - 4) * 4 + c] = w;
-        }
-    }
-    // The j-th best of the 64 lane maxima: at most the j-th best sampled
-    // word (the maxima are a subset of the sample), so it admits at least as
-    // much, and it costs one 64-word register sort.
+    for (int u = 0; u < (int)(kSampleSpan / 4); ++u) x[u] = src[u];
     uint64_t lmx = 0ull;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) lmx = umax64(lmx, umax64(a[j], b[j]));
-    const uint32_t have = (uint32_t)__popcll(__ballot(lmx != 0ull));
-    if (have < 2u * (uint32_t)jn) return 0ull;
+    for (int u = 0; u < (int)(kSampleSpan / 4); ++u) {
+        const float v4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t pos = gv + (uint32_t)(4 * u + c) - g.off0;
+            lmx = umax64(lmx, pack_word(order_key(__float_as_uint(v4[c])), pos));
+        }
+    }
+    // The j-th best lane maximum is at most the j-th best sampled word (the
+    // maxima are a subset of the sample), so it admits at least as much.
     uint64_t v[1] = {lmx};
     wave_sort<1, false>(v, lane);
     return list_word_at<1>(v, (uint32_t)jn - 1u);
 }
 
-// Streams this wave's share of a row's blocks once: positions q, q+Q, ... of
-// the visit order.  Scores whose word beats max(threshold, estimate) go to
-// the tray; full trays are published to the sorter.  Returns the number of
-// scores that entered a tray.
+// Streams this wave's share of a row's blocks once: visit positions q, q+Q,
+// ... of the row's visit order.  Scores whose word beats max(threshold,
+// estimate) go to the tray; full trays are published to the sorter.  Returns
+// the number of scores that entered a tray.  With tau_ready set, the
+// estimate is read from tau_src once the sorter flags it, after the first
+// loads are issued.
 //
 // Per block the wave does little besides the loads: the visit order is
 // computed 64 blocks ahead by the vector unit (one permutation step per
@@ -680,9 +684,10 @@ __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t
 template <int E, bool SPLIT>
 __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOrder &ord,
                                                  uint32_t q, uint32_t Q, uint64_t tau,
-                                                 uint64_t &T, uint64_t *trays, uint32_t w,
-                                                 uint32_t CW, uint32_t Wm, uint64_t *sT,
-                                                 uint32_t (*fill)[2], uint64_t *gT,
+                                                 uint32_t *tau_ready,
+                                                 uint64_t *tau_src, uint64_t &T, uint64_t *trays,
+                                                 uint32_t w, uint32_t CW, uint32_t Wm,
+                                                 uint64_t *sT, uint32_t (*fill)[2], uint64_t *gT,
                                                  uint32_t lane) {
     constexpr int D = Cfg<E>::D;
     const uint32_t mine = q < g.nb ? (g.nb - 1u - q) / Q + 1u : 0u;
@@ -691,8 +696,7 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
 #pragma unroll
     for (int i = 0; i < E; ++i) lk[i] = 0u;
     uint64_t *tray = trays + (size_t)(2 * w) * CW;
-    if (mine == 0) return 0u;
-    const bool lane_bounds = tau == 0ull;   // the estimate, when present, is far tighter
+    if (mine == 0u) return 0u;
 
     // Visit list: lane j holds the block of this stream's step c0 + j.
     uint32_t c0 = 0;
@@ -705,18 +709,19 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
     float4 buf[D][kLoadsPerBlock];
     uint32_t bid[D];
     uint64_t gbuf[D];
-    // Every slot issues exactly one set of loads per visit (past the stream's
-    // end it re-reads its last block), so the wait before each slot is the
-    // same static count every time.
-    auto issue = [&](float4 (&dst)[kLoadsPerBlock], uint32_t &b_out, uint64_t &g_out,
-                     uint32_t t) __attribute__((always_inline)) {
-        const uint32_t tt = t < mine ? t : mine - 1u;
+    // Block of step u; past the stream's end the last block is read again:
+    // every slot issues exactly one set of loads per visit, so the wait
+    // before each slot is the same static count every time.
+    auto block_of = [&](uint32_t u) __attribute__((always_inline)) {
+        const uint32_t tt = u < mine ? u : mine - 1u;
         if (tt - c0 >= (uint32_t)kWave) {   // next chunk of the visit list
             c0 = tt & ~(uint32_t)(kWave - 1);
             vis = visit_chunk(c0);
         }
-        const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)vis, (int)(tt - c0));
-        b_out = b;
+        return (uint32_t)__builtin_amdgcn_readlane((int)vis, (int)(tt - c0));
+    };
+    auto issue = [&](float4 (&dst)[kLoadsPerBlock], uint32_t b, uint64_t &g_out)
+        __attribute__((always_inline)) {
         if constexpr (SPLIT) {
             g_out = __hip_atomic_load(gT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -737,7 +742,17 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
         }
     };
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(buf[d], bid[d], gbuf[d], (uint32_t)d);
+    for (int d = 0; d < D; ++d) {
+        bid[d] = block_of((uint32_t)d);
+        issue(buf[d], bid[d], gbuf[d]);
+    }
+    // The first blocks are in flight while the sorter computes the estimate.
+    if (tau_ready) {
+        while (lds_load_u32(tau_ready) == 0u) __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        tau = lds_load_word(tau_src);
+    }
+    const bool lane_bounds = tau == 0ull;   // the estimate, when present, is far tighter
 
     for (uint32_t t0 = 0; t0 < mine; t0 += D) {
 #pragma unroll
@@ -777,7 +792,8 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                     }
                 }
             }
-            issue(buf[d], bid[d], gbuf[d], t + (uint32_t)D);
+            bid[d] = block_of(t + (uint32_t)D);
+            issue(buf[d], bid[d], gbuf[d]);
             T = umax64(T, uniform64(shared_T));
             if (cnt >= Wm) {
                 publish_tray(&fill[w][cur], cnt, lane);
@@ -833,7 +849,7 @@ __device__ __forceinline__ void reset_sorter(SorterState &ss, uint32_t *hist, ui
 }
 
 constexpr uint32_t kVerdictExit = 1u;
-constexpr uint32_t kMergeBatch = 3;   // segment lists in flight during the leader's merge
+constexpr uint32_t kMergeBatch = 3;    // segment lists in flight during the leader's merge
 constexpr uint32_t kVerdictRerun = 2u;
 
 template <int E, bool SPLIT>
@@ -852,8 +868,11 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p) {
     const uint32_t NW = blockDim.x / kWave;
     const uint32_t NS = NW - 1;                   // streamer waves; wave NS sorts
     const uint32_t S = (uint32_t)p.split;
-    const uint32_t s = blockIdx.x % S;
-    const uint32_t r = (uint32_t)p.row0 + blockIdx.x / S;
+    // Segment-major grid: the segments of a row are dispatched far apart, so
+    // every row mixes early and late workgroups (the later of two workgroups
+    // on a compute unit tends to run slower).
+    const uint32_t s = blockIdx.x / (uint32_t)p.rows;
+    const uint32_t r = (uint32_t)p.row0 + blockIdx.x % (uint32_t)p.rows;
     const uint32_t k = (uint32_t)p.k;
     const uint32_t CW = (uint32_t)p.tray_words;
     uint64_t *gT = SPLIT ? p.ws_ctrl + 2 * (size_t)r : nullptr;
@@ -874,14 +893,14 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p) {
 
     if (w < NS) {
         // ---- streamer ----
-        while (lds_load_u32(&s_ready) == 0u) __builtin_amdgcn_s_sleep(1);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        uint64_t tau = lds_load_word(&s_tau);
         uint64_t T = 0ull;
         uint32_t q = s * NS + w, Q = S * NS;
         uint32_t entered = 0;
         for (int pass = 0; pass < 2; ++pass) {
-            entered += stream_share<E, SPLIT>(g, ord, q, Q, tau, T, trays, w, CW,
+            // Pass 0 reads the estimate once its first loads are issued; a
+            // rerun streams the whole row without it.
+            entered += stream_share<E, SPLIT>(g, ord, q, Q, 0ull, pass == 0 ? &s_ready : nullptr,
+                                              &s_tau, T, trays, w, CW,
                                               (uint32_t)p.watermark, &s_T, s_fill, gT, lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             if (lane == 0) {
@@ -895,7 +914,6 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p) {
             // Stream the whole row again, without the estimate.
             q = w;
             Q = NS;
-            tau = 0ull;
         }
         if (p.stats && lane == 0 && entered > 0) {
             atomicAdd(p.stats + 2 * (size_t)r, (unsigned long long)entered);
