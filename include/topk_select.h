@@ -117,7 +117,9 @@ int topk_select_split(const float *scores, const int32_t *lengths, int32_t rows,
 typedef struct {
     uint64_t seed;           /* visit-order and sample seed; the result never depends on it */
     int32_t split;           /* workgroups per row; 0 = automatic                */
-    int32_t waves;           /* waves per workgroup, 2..4: one sorts, the rest stream */
+    int32_t waves;           /* waves per workgroup, 2..8 (2..4 when k > 1024), as long
+                              * as the trays fit in LDS: one sorts, the rest stream;
+                              * TOPK_EINVAL otherwise                                */
     int32_t watermark;       /* tray words that trigger a hand-off; 0 = default  */
     int32_t flags;           /* TOPK_FLAG_* bits; 0 = default behaviour          */
     /* Optional device array [rows][2] of uint64, accumulated into (zero it

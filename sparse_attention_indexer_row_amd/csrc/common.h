@@ -21,7 +21,7 @@ namespace topk {
 // Kernel Behind DeepSeek V4.1 Flash", transcript 3:30).
 constexpr int kBlock = 1024;
 constexpr int kWave = 64;
-constexpr int kMaxWaves = 4;
+constexpr int kMaxWaves = 8;
 
 TOPK_HD uint32_t order_key(uint32_t bits) {
     // negative floats: flip all bits; non-negative: set the sign bit

@@ -50,6 +50,9 @@ template <int E>
 struct Cfg {
     static constexpr int KP = kWave * E;       // kept-list words
     static constexpr int D = E <= 8 ? 4 : 2;   // blocks in flight per wave
+    // Largest workgroup: the widest lists need more than half a SIMD's
+    // registers per wave, so they run at most one wave per SIMD.
+    static constexpr int kMaxThreads = kWave * (E >= 32 ? 4 : kMaxWaves);
 };
 
 __device__ __forceinline__ uint32_t mbcnt64(uint64_t mask) {
@@ -853,7 +856,7 @@ constexpr uint32_t kMergeBatch = 3;    // segment lists in flight during the lea
 constexpr uint32_t kVerdictRerun = 2u;
 
 template <int E, bool SPLIT>
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs p) {
+__global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs p) {
     constexpr int KP = Cfg<E>::KP;
     extern __shared__ uint64_t trays[];  // [streamers][2][tray_words], pool, gather[64], hist[256]
     __shared__ uint64_t s_T;                      // workgroup threshold word (a lower bound)

@@ -85,6 +85,18 @@ int check_options(const topk_options *o) {
     return TOPK_OK;
 }
 
+// A plan the kernel can launch: the widest lists run at most four waves
+// (one per SIMD), and the dynamic LDS plus the kernel's own shared words must
+// fit one workgroup's LDS.
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;
+constexpr size_t kStaticLdsBound = 256;
+int check_plan(const Plan &p) {
+    const int max_waves = p.E >= 32 ? 4 : topk::kMaxWaves;
+    if (p.waves > max_waves) return TOPK_EINVAL;
+    if (p.lds + kStaticLdsBound > kLdsPerWorkgroup) return TOPK_EINVAL;
+    return TOPK_OK;
+}
+
 // Plans a call.  `cus` is the compute-unit count to plan for.
 Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cus) {
     Plan p{};
@@ -198,6 +210,8 @@ int topk_plan(int32_t rows, int32_t n, int32_t k, const topk_options *opts, topk
     if (hipGetDeviceCount(&count) == hipSuccess && count > 0 && device_cus(&dev_cus) == TOPK_OK)
         cus = dev_cus;
     Plan p = make_plan(rows, n, k, opts, cus);
+    st = check_plan(p);
+    if (st != TOPK_OK) return st;
     out->split = p.split;
     out->waves = p.waves;
     out->list_words = 64 * p.E;
@@ -237,6 +251,10 @@ int topk_select_ex(const float *scores, const int32_t *lengths, int32_t rows, in
     st = check_options(opts);
     if (st != TOPK_OK) return st;
     if (workspace && misaligned(workspace, kAlign)) return TOPK_EWORKSPACE;
+    // Whether the launch fits does not depend on the device's CU count, so
+    // it is checked with the other arguments, before any HIP call.
+    st = check_plan(make_plan(rows, n, k, opts, kAssumedCUs));
+    if (st != TOPK_OK) return st;
     if (rows == 0) return TOPK_OK;
     int cus = 0;
     st = device_cus(&cus);

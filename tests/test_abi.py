@@ -75,8 +75,11 @@ def test_split_and_ex_argument_errors(lib):
     o = _lib.TopkOptions()
     o.waves = 1
     assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_EINVAL
-    o.waves = 5
+    o.waves = 9
     assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_EINVAL
+    o.waves = 5   # k = 2048 lists run at most four waves
+    big = (FAKE, None, 4, 4096, 2048, FAKE, FAKE)
+    assert lib.topk_select_ex(*big, ctypes.byref(o), None, 0, None) == _lib.TOPK_EINVAL
     o.waves, o.watermark = 4, -3
     assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_EINVAL
     o.watermark, o.split = 0, 2000
@@ -117,6 +120,17 @@ def test_plan_list_sizes_and_lds(lib):
         assert p.lds_bytes == 8 * (2 * (p.waves - 1) * p.tray_words + words + 1024 + 64) + 4 * 256
         assert p.lds_bytes <= 160 * 1024
         assert p.tray_words == p.watermark + 1024
+
+
+def test_plan_rejects_what_does_not_fit(lib):
+    # eight waves fit for k <= 1024; k = 2048 lists run at most four waves
+    assert _plan(lib, 4, 1 << 16, 512, waves=8).waves == 8
+    o = _lib.TopkOptions()
+    o.waves = 8
+    p = _lib.TopkPlan()
+    assert lib.topk_plan(4, 1 << 16, 2048, ctypes.byref(o), ctypes.byref(p)) == _lib.TOPK_EINVAL
+    o.waves, o.watermark = 8, 4096   # trays of 4096 + 1024 words per streamer exceed LDS
+    assert lib.topk_plan(4, 1 << 16, 512, ctypes.byref(o), ctypes.byref(p)) == _lib.TOPK_EINVAL
 
 
 def test_plan_split_policy(lib):

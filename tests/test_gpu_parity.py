@@ -154,6 +154,8 @@ SCHEDULES = [
     dict(seed=10, split=1, flags=1), dict(seed=11, split=4, flags=1),
     dict(seed=12, split=1, flags=2), dict(seed=13, split=4, flags=2),
     dict(seed=14, split=7, waves=3, flags=2),
+    dict(seed=15, split=2, waves=8), dict(seed=16, split=1, waves=6, flags=2),
+    dict(seed=17, split=5, waves=5, watermark=64),
 ]
 
 
@@ -166,7 +168,8 @@ def test_schedule_invariance(opts):
 def test_schedule_invariance_ragged():
     w = workloads.ragged(rows=16, n=60_000, k=1000, seed=22)
     ref = None
-    for opts in (dict(split=1), dict(split=5, seed=3), dict(split=2, waves=2, watermark=256)):
+    for opts in (dict(split=1), dict(split=5, seed=3), dict(split=2, waves=2, watermark=256),
+                 dict(split=3, waves=8)):
         v, i = run_select(w.scores, w.k, w.lengths, **opts)
         if ref is None:
             ref = (v, i)
