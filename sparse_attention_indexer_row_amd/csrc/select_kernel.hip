@@ -842,6 +842,96 @@ __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_
     prune_pool<E, SPLIT>(ss, pool, sT, gT, k, hist, gath, lane);
 }
 
+// Bitonic sort, descending, of the pool's pc words (zero padded to 64*E) by
+// P waves of the workgroup.  Wave `chunk` loads words [chunk*C, chunk*C + C)
+// (C = 64*E/P) and sorts them in registers, even chunks descending and odd
+// ones ascending, so neighbours form bitonic runs; each merge level above C
+// then runs its stages across chunks through LDS (every element keeps the
+// max or the min of itself and its partner, as its position and the level
+// dictate) and the stages inside a chunk in registers.  LDS `x` holds
+// position i of chunk c at c*C + (i mod E/P)*64 + lane, so each exchange is
+// one coalesced access per register.  The sorter wave ends holding the
+// result in its usual blocked register layout.  Every wave of the workgroup
+// calls this and meets the same barriers; waves with no chunk only wait.
+template <int E, int P>
+__device__ __forceinline__ void wg_sort_impl(uint64_t *x, const uint64_t *pool,
+                                             const uint32_t *pc_p, int chunk, bool sorter,
+                                             uint64_t (&kept)[E], uint32_t lane) {
+    constexpr int EP = E / P;
+    constexpr uint32_t C = 64u * EP, N = 64u * E;
+    __syncthreads();   // the pool and its word count are final
+    const bool active = chunk >= 0 && chunk < P;
+    const uint32_t base = active ? (uint32_t)chunk * C : 0u;
+    uint64_t a[EP];
+    if (active) {
+        const uint32_t pc = *pc_p;
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+            const uint32_t i = base + lane * EP + (uint32_t)e;
+            a[e] = i < pc ? pool[i] : 0ull;
+        }
+        if (chunk & 1) {
+            wave_sort<EP, true>(a, lane);
+        } else {
+            wave_sort<EP, false>(a, lane);
+        }
+    }
+    for (uint32_t S = 2u * C; S <= N; S *= 2u) {
+        for (uint32_t J = S / 2u; J >= C; J /= 2u) {
+            if (active) {
+#pragma unroll
+                for (int e = 0; e < EP; ++e) x[base + (uint32_t)e * kWave + lane] = a[e];
+            }
+            __syncthreads();
+            if (active) {
+                const bool keep_max = ((base & J) == 0u) == ((base & S) == 0u);
+#pragma unroll
+                for (int e = 0; e < EP; ++e) {
+                    const uint64_t y = x[(base ^ J) + (uint32_t)e * kWave + lane];
+                    a[e] = keep_max ? umax64(a[e], y) : umin64(a[e], y);
+                }
+            }
+            __syncthreads();
+        }
+        if (active) {
+            if ((base & S) == 0u) {
+                wave_merge<EP, false>(a, lane);
+            } else {
+                wave_merge<EP, true>(a, lane);
+            }
+        }
+    }
+    if (active) {
+#pragma unroll
+        for (int e = 0; e < EP; ++e) x[base + (uint32_t)e * kWave + lane] = a[e];
+    }
+    __syncthreads();
+    if (sorter) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t i = lane * E + (uint32_t)e;
+            const uint32_t l = i % C;
+            kept[e] = x[(i / C) * C + (l % EP) * kWave + l / EP];
+        }
+    }
+}
+
+// The sorter takes chunk 0 and streamer w chunk w+1; four waves share the
+// sort when the workgroup has them, else two.
+template <int E>
+__device__ __forceinline__ void wg_sort(uint64_t *x, const uint64_t *pool, const uint32_t *pc_p,
+                                        uint32_t w, uint32_t NW, bool sorter, uint64_t (&kept)[E],
+                                        uint32_t lane) {
+    constexpr int P4 = E < 4 ? E : 4;
+    constexpr int P2 = E < 2 ? E : 2;
+    const int chunk = sorter ? 0 : (int)w + 1;
+    if (NW >= 4u) {
+        wg_sort_impl<E, P4>(x, pool, pc_p, chunk, sorter, kept, lane);
+    } else {
+        wg_sort_impl<E, P2>(x, pool, pc_p, chunk, sorter, kept, lane);
+    }
+}
+
 __device__ __forceinline__ void reset_sorter(SorterState &ss, uint32_t *hist, uint32_t lane) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
@@ -865,6 +955,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     __shared__ uint32_t s_done;                   // streamers finished with the current pass
     __shared__ uint32_t s_ready;                  // estimate published
     __shared__ uint32_t s_verdict;                // after the first pass: exit or rerun
+    __shared__ uint32_t s_pc;                     // pool words at the end of a pass
 
     const uint32_t lane = lane_id();
     const uint32_t w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
@@ -908,6 +999,10 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             if (lane == 0) {
                 __hip_atomic_fetch_add(&s_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            {
+                uint64_t unused[E];
+                wg_sort<E>(trays, trays + (size_t)(2 * NS) * CW, &s_pc, w, NW, false, unused, lane);
             }
             if (pass == 1) break;
             uint32_t verdict;
@@ -953,12 +1048,10 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     bool rerun = false;
     for (int pass = 0; pass < 2; ++pass) {
         collect<E, SPLIT>(ss, pool, trays, CW, NS, s_fill, &s_done, &s_T, gT, k, hist, gath, lane);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const uint32_t i = (uint32_t)e * kWave + lane;
-            kept_sorted[e] = i < ss.pc ? pool[i] : 0ull;
-        }
-        wave_sort<E, false>(kept_sorted, lane);   // the one full sort of this pass
+        if (lane == 0) s_pc = ss.pc;
+        // The one full sort of this pass, shared with the streamer waves
+        // (they are done streaming); the trays hold the exchange buffer.
+        wg_sort<E>(trays, pool, &s_pc, NS, NW, true, kept_sorted, lane);
         if (!SPLIT || rerun) {
             // With an estimate in use, fewer than k admitted scores means
             // some of the row's best k may lie below it: stream again.
