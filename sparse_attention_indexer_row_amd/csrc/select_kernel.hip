@@ -409,6 +409,7 @@ struct SorterState {
     uint32_t shift;
     uint32_t kmax;    // largest key ever added to the pool
     uint32_t sorts;   // exact selections run
+    uint64_t gnext;   // split rows: the row's threshold word, read one tray piece ahead
 };
 
 // Bucket of key x (x >= base); the top bucket is open-ended.
@@ -535,13 +536,16 @@ __device__ __forceinline__ void merge_tray(SorterState &ss, uint64_t *pool, cons
     for (uint32_t off = 0; off < c; off += kPieceWords) {
         ss.T = umax64(ss.T, lds_load_word(sT));
         if constexpr (SPLIT) {
-            ss.T = umax64(ss.T, uniform64(__hip_atomic_load(gT, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT)));
+            // The row's word read at the previous piece (any stale value is
+            // still a bound); the next read is in flight while this piece is
+            // folded in.
+            ss.T = umax64(ss.T, uniform64(ss.gnext));
+            ss.gnext = __hip_atomic_load(gT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         const uint32_t piece = c - off < kPieceWords ? c - off : kPieceWords;
         if (ss.pc + piece > PoolCfg<E>::cap) {
             prune_pool<E, SPLIT>(ss, pool, sT, gT, k, hist, gath, lane);
-            uint32_t base = (uint32_t)(ss.T >> 32);
+            const uint32_t base = (uint32_t)(ss.T >> 32);
             ss.base = base;
             ss.shift = fit_shift(base, ss.kmax);
             rebuild_hist(pool, ss.pc, ss.T, ss.base, ss.shift, hist, lane);
@@ -1031,6 +1035,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     SorterState ss;
     ss.T = 0ull;
     ss.sorts = 0u;
+    ss.gnext = 0ull;
     reset_sorter(ss, hist, lane);
     auto set_verdict = [&](uint32_t v) __attribute__((always_inline)) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");

@@ -149,7 +149,7 @@ def test_strictly_descending_and_ascending_rows():
 SCHEDULES = [
     dict(seed=0, split=1), dict(seed=1, split=1), dict(seed=2, split=2),
     dict(seed=3, split=4, waves=2), dict(seed=4, split=16, waves=3), dict(seed=5, split=64),
-    dict(seed=6, split=1, watermark=64), dict(seed=7, split=3, watermark=2048),
+    dict(seed=6, split=1, watermark=64), dict(seed=7, split=3, waves=3, watermark=2048),
     dict(seed=8, split=256, waves=2), dict(seed=9, split=1, waves=2, watermark=100),
     dict(seed=10, split=1, flags=1), dict(seed=11, split=4, flags=1),
     dict(seed=12, split=1, flags=2), dict(seed=13, split=4, flags=2),
@@ -169,7 +169,7 @@ def test_schedule_invariance_ragged():
     w = workloads.ragged(rows=16, n=60_000, k=1000, seed=22)
     ref = None
     for opts in (dict(split=1), dict(split=5, seed=3), dict(split=2, waves=2, watermark=256),
-                 dict(split=3, waves=8)):
+                 dict(split=3, waves=6)):
         v, i = run_select(w.scores, w.k, w.lengths, **opts)
         if ref is None:
             ref = (v, i)
