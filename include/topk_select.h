@@ -79,8 +79,9 @@ int topk_select(const float *scores, const int32_t *lengths, int32_t rows, int32
 /*
  * topk_split_workspace_bytes -- device bytes topk_select_split needs.
  * `split` == 0 means the automatic choice.  Returns 0 for invalid arguments.
- * The workspace holds per-row threshold and ticket words and one k-list per
- * (row, split) pair.
+ * The workspace holds per-row threshold and ticket words, one arrival ticket
+ * per group of eight of a row's workgroups, and one k-list per (row, split)
+ * pair.
  */
 size_t topk_split_workspace_bytes(int32_t rows, int32_t n, int32_t k, int32_t split);
 
@@ -96,8 +97,10 @@ int topk_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
  * topk_select_split -- top-k with each row split across `split` workgroups
  * (0 = automatic, 1 = no split).  Each workgroup keeps a local top-k of its
  * share of the row's blocks; workgroups of a row share a rising threshold
- * through the workspace; the last to finish (elected by an atomic ticket)
- * merges the local lists and writes the row's output.  `workspace` is
+ * through the workspace.  The last of each group of eight workgroups to
+ * finish (elected by an atomic ticket) merges the group's lists, and the last
+ * group to finish merges the groups' lists and writes the row's output.
+ * `workspace` is
  * caller-owned device memory of at least topk_split_workspace_bytes(...),
  * 256-byte aligned, zeroed once by topk_workspace_init.  Allocates nothing.
  * Two calls that use one workspace must not run concurrently.

@@ -6,6 +6,10 @@
 
 namespace topk {
 
+// Split rows merge in two levels: segments in groups of kMergeGroup, then
+// the groups' lists.
+constexpr int kMergeGroup = 8;
+
 struct SelectArgs {
     const float *scores;       // [rows][n]
     const int32_t *lengths;    // [rows] or null
@@ -19,6 +23,7 @@ struct SelectArgs {
     float *out_vals;           // [rows][k]
     int32_t *out_idx;          // [rows][k]
     uint64_t *ws_ctrl;         // [rows][2]: threshold word, arrival ticket (split > 1)
+    uint32_t *ws_groups;       // [rows][groups] arrival tickets of segment groups (split > 1)
     uint64_t *ws_lists;        // [rows][split][list_words] (split > 1)
     unsigned long long *stats; // [rows][2] or null
     uint64_t seed;

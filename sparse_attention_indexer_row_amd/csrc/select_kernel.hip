@@ -945,9 +945,46 @@ __device__ __forceinline__ void reset_sorter(SorterState &ss, uint32_t *hist, ui
     ss.kmax = 0u;
 }
 
+// Folds kept lists from the workspace into acc (descending): the lists at
+// slots first + t*stride for t < count, except slot `skip`, fetched
+// kMergeBatch at a time (all loads of a batch in flight together), each
+// cleared right after it is merged.
+template <int E>
+__device__ __forceinline__ void merge_lists(uint64_t (&acc)[E], uint64_t *lists, uint32_t first,
+                                            uint32_t count, uint32_t stride, uint32_t skip,
+                                            uint32_t lane);
+
 constexpr uint32_t kVerdictExit = 1u;
 constexpr uint32_t kMergeBatch = 3;    // segment lists in flight during the leader's merge
 constexpr uint32_t kVerdictRerun = 2u;
+
+template <int E>
+__device__ __forceinline__ void merge_lists(uint64_t (&acc)[E], uint64_t *lists, uint32_t first,
+                                            uint32_t count, uint32_t stride, uint32_t skip,
+                                            uint32_t lane) {
+    constexpr int KP = Cfg<E>::KP;
+    uint64_t zero[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) zero[e] = 0ull;
+    for (uint32_t t = 0; t < count; t += kMergeBatch) {
+        uint64_t nb[kMergeBatch][E];
+        bool use[kMergeBatch];
+        uint32_t slot[kMergeBatch];
+#pragma unroll
+        for (uint32_t a = 0; a < kMergeBatch; ++a) {
+            slot[a] = first + (t + a) * stride;
+            use[a] = t + a < count && slot[a] != skip;
+            if (use[a]) load_list_reversed<E>(nb[a], lists + (size_t)slot[a] * KP, lane);
+        }
+#pragma unroll
+        for (uint32_t a = 0; a < kMergeBatch; ++a) {
+            if (use[a]) {
+                keep_best<E>(acc, nb[a], lane);
+                store_list<E>(lists + (size_t)slot[a] * KP, zero, lane);
+            }
+        }
+    }
+}
 
 template <int E, bool SPLIT>
 __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs p) {
@@ -1068,50 +1105,57 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
             if (!rerun) set_verdict(kVerdictExit);
             break;
         }
-        // Split row: publish this segment's list and take a ticket; the last
-        // of the row's segments to arrive merges every list.  One release
-        // fence orders the list stores before the ticket; only the leader
-        // needs the matching acquire.
+        // Split row: publish this segment's list and take its group's
+        // ticket; the last of a group to arrive merges the group's lists,
+        // and with several groups publishes the result in the group's first
+        // slot and takes the row ticket; the last group to arrive merges the
+        // groups' lists.  One release fence orders each publication before
+        // its ticket; only the leaders need the matching acquire.
         uint64_t *lists = p.ws_lists + (size_t)r * S * KP;
+        const uint32_t G = (uint32_t)kMergeGroup;
+        const uint32_t ng = (S + G - 1u) / G;
+        const uint32_t grp = s / G, g0 = grp * G;
+        const uint32_t gsz = S - g0 < G ? S - g0 : G;
+        uint32_t *gticket = p.ws_groups + (size_t)r * ng + grp;
         store_list<E>(lists + (size_t)s * KP, kept_sorted, lane);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         uint32_t old = 0;
         if (lane == 0) {
-            old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __hip_atomic_fetch_add(gticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         old = __builtin_amdgcn_readfirstlane((int)old);
-        if (old != S - 1u) {
+        bool lead = old == gsz - 1u;
+        if (lead) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            // The group leader's own list is not read again: clear it.
+            uint64_t zero[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) zero[e] = 0ull;
+            store_list<E>(lists + (size_t)s * KP, zero, lane);
+            merge_lists<E>(kept_sorted, lists, g0, gsz, 1u, s, lane);
+            if (lane == 0) __hip_atomic_store(gticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (ng > 1u) {
+                store_list<E>(lists + (size_t)g0 * KP, kept_sorted, lane);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                if (lane == 0) {
+                    old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                }
+                old = __builtin_amdgcn_readfirstlane((int)old);
+                lead = old == ng - 1u;
+                if (lead) {
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    store_list<E>(lists + (size_t)g0 * KP, zero, lane);
+                    merge_lists<E>(kept_sorted, lists, 0u, ng, G, g0, lane);
+                }
+            }
+        }
+        if (!lead) {
             set_verdict(kVerdictExit);
             if (p.stats && lane == 0 && ss.sorts > 0) {
                 atomicAdd(p.stats + 2 * (size_t)r + 1, (unsigned long long)ss.sorts);
             }
             return;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        // The leader's own list is not read again: clear it now.  The other
-        // lists are fetched kMergeBatch at a time (all loads of a batch in
-        // flight together), merged, and cleared behind the merge, so the
-        // workspace is all zero again when the call ends.
-        uint64_t zero[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) zero[e] = 0ull;
-        store_list<E>(lists + (size_t)s * KP, zero, lane);
-        const uint32_t others = S - 1u;
-        for (uint32_t t = 0; t < others; t += kMergeBatch) {
-            uint64_t nb[kMergeBatch][E];
-#pragma unroll
-            for (uint32_t a = 0; a < kMergeBatch; ++a) {
-                const uint32_t j = t + a < s ? t + a : t + a + 1u;   // skip the leader's own
-                if (t + a < others) load_list_reversed<E>(nb[a], lists + (size_t)j * KP, lane);
-            }
-#pragma unroll
-            for (uint32_t a = 0; a < kMergeBatch; ++a) {
-                const uint32_t j = t + a < s ? t + a : t + a + 1u;
-                if (t + a < others) {
-                    keep_best<E>(kept_sorted, nb[a], lane);
-                    store_list<E>(lists + (size_t)j * KP, zero, lane);
-                }
-            }
         }
         const uint64_t kth = list_word_at<E>(kept_sorted, k - 1);
         if (tau != 0ull && kth == 0ull) {

@@ -33,17 +33,23 @@ int list_multiplier(int32_t k) {  // E: list capacity 64*E >= k
 struct Plan {
     int E, waves, split, watermark, tray, cus;
     size_t lds, ws_bytes;
-    size_t off_lists;
+    size_t off_groups, off_lists;
 };
 
 // Workspace: per-row 16-byte control records (threshold word, ticket) at
 // the front, then the per-(row, split) kept lists.  Every call leaves all of
 // it zero again, so one zeroed buffer serves calls of any shape.
-size_t workspace_layout(int64_t rows, int split, int list_words, size_t *off_lists) {
+// Split-row workspace: per-row control records (threshold word, ticket),
+// per-row group tickets, then the kept lists.
+size_t workspace_layout(int64_t rows, int split, int list_words, size_t *off_groups,
+                        size_t *off_lists) {
     const size_t ctrl = align_up((size_t)rows * 16, kAlign);
+    const size_t groups_per_row = (size_t)((split + topk::kMergeGroup - 1) / topk::kMergeGroup);
+    const size_t groups = align_up((size_t)rows * groups_per_row * 4, kAlign);
     const size_t lists = (size_t)rows * (size_t)split * (size_t)list_words * 8;
-    if (off_lists) *off_lists = ctrl;
-    return ctrl + lists;
+    if (off_groups) *off_groups = ctrl;
+    if (off_lists) *off_lists = ctrl + groups;
+    return ctrl + groups + lists;
 }
 
 int device_cus(int *cus) {
@@ -127,7 +133,7 @@ Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cu
         if (s < 1) s = 1;
         p.split = (int)s;
     }
-    p.ws_bytes = p.split > 1 ? workspace_layout(rows, p.split, list_words, &p.off_lists) : 0;
+    p.ws_bytes = p.split > 1 ? workspace_layout(rows, p.split, list_words, &p.off_groups, &p.off_lists) : 0;
     return p;
 }
 
@@ -150,6 +156,7 @@ int run(const float *scores, const int32_t *lengths, int32_t rows, int32_t n, in
     if (pl.split > 1) {
         char *base = static_cast<char *>(ws);
         a.ws_ctrl = reinterpret_cast<uint64_t *>(base);
+        a.ws_groups = reinterpret_cast<uint32_t *>(base + pl.off_groups);
         a.ws_lists = reinterpret_cast<uint64_t *>(base + pl.off_lists);
     }
     // Keep each launch's work-item count well inside 32 bits.
