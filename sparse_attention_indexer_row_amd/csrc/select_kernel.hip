@@ -622,25 +622,30 @@ __device__ __forceinline__ RowGeom row_geometry(const SelectArgs &p, uint32_t r)
 // 11:47-12:10: the shipped kernel starts its scan already holding a working
 // threshold).  Lane j reads one aligned 128-byte line (32 consecutive
 // scores) at a seeded place inside stratum j of the row's 64 equal strata:
-// 2,048 scores for 64 line fetches.  The estimate is the j-th best of the 64
-// lane maxima with j = ceil(10 k 2048 / L), so roughly 10k scores of the row
-// lie above it.  A lane contributes one maximum however many of the row's
-// best scores its line holds, so crowding the best scores into one place
-// cannot lift the estimate above the k-th best.  It is not a bound: whether
-// it was low enough is checked at the end (at least k scores admitted), and
-// the row is streamed again without it otherwise.  Returns 0 (no estimate)
-// for rows too short for it to pay.
+// 2,048 scores for 64 line fetches.  Each line is cut into 4 groups of 8
+// scores, and the estimate is the j-th best of the 256 group maxima.  For a
+// row of independent scores, the sample holds about lam = 2048 k / L of the
+// row's best k, and j = ceil(lam + 6 sqrt(lam) + 6) lies far enough above
+// that for the estimate to fall below the k-th best in all but a vanishing
+// fraction of rows.  A group contributes one maximum however many of the
+// row's best scores it holds, so crowding the best scores together cannot
+// lift the estimate either.  It is not a bound: whether it was low enough is
+// checked at the end (at least k scores admitted), and the row is streamed
+// again without it otherwise.  Returns 0 (no estimate) for rows too short
+// for it to pay.
 constexpr uint32_t kSampleSpan = 32;                      // scores per lane, one 128-byte line
 constexpr uint32_t kSampleWords = kWave * kSampleSpan;    // 2,048
-constexpr uint32_t kEstimateMargin = 10;
+constexpr int kSampleGroups = 4;                          // groups of 8 scores per lane
 constexpr uint32_t kFlagNoEstimate = 1u;
 constexpr uint32_t kFlagForceRerun = 2u;
 
 __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t seed, uint32_t r,
                                                        uint32_t k, uint32_t flags, uint32_t lane) {
     if ((flags & kFlagNoEstimate) || g.L == 0u) return 0ull;
-    const uint64_t jn = ((uint64_t)kEstimateMargin * k * kSampleWords + g.L - 1) / g.L;
-    if (jn > kWave / 2) return 0ull;
+    const float lam = (float)k * (float)kSampleWords / (float)g.L;
+    const float jf = ceilf(lam + 6.0f * sqrtf(lam) + 6.0f);
+    if (!(jf <= (float)(kSampleGroups * kWave / 2))) return 0ull;
+    const uint32_t jn = (uint32_t)jf;
     if (flags & kFlagForceRerun) return ~0ull;  // admits nothing: forces the rerun path
     // Line m starts at virtual position 32m - mis, 128-byte aligned in memory;
     // lines first .. last_end-1 lie wholly inside the valid positions.
@@ -659,21 +664,24 @@ __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t
     float4 x[kSampleSpan / 4];
 #pragma unroll
     for (int u = 0; u < (int)(kSampleSpan / 4); ++u) x[u] = src[u];
-    uint64_t lmx = 0ull;
+    uint64_t gm[kSampleGroups];
 #pragma unroll
-    for (int u = 0; u < (int)(kSampleSpan / 4); ++u) {
-        const float v4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+    for (int q = 0; q < kSampleGroups; ++q) {
+        gm[q] = 0ull;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t pos = gv + (uint32_t)(4 * u + c) - g.off0;
-            lmx = umax64(lmx, pack_word(order_key(__float_as_uint(v4[c])), pos));
+        for (int u = 2 * q; u < 2 * q + 2; ++u) {
+            const float v4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t pos = gv + (uint32_t)(4 * u + c) - g.off0;
+                gm[q] = umax64(gm[q], pack_word(order_key(__float_as_uint(v4[c])), pos));
+            }
         }
     }
-    // The j-th best lane maximum is at most the j-th best sampled word (the
+    // The j-th best group maximum is at most the j-th best sampled word (the
     // maxima are a subset of the sample), so it admits at least as much.
-    uint64_t v[1] = {lmx};
-    wave_sort<1, false>(v, lane);
-    return list_word_at<1>(v, (uint32_t)jn - 1u);
+    wave_sort<kSampleGroups, false>(gm, lane);
+    return list_word_at<kSampleGroups>(gm, jn - 1u);
 }
 
 // Streams this wave's share of a row's blocks once: visit positions q, q+Q,
