@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -16,7 +17,13 @@ using topk::kBlock;
 using topk::kWave;
 
 constexpr size_t kAlign = 256;
-constexpr int kDefaultWaves = 4;      // three streamer waves and one sorter wave
+// Default waves per workgroup: six streamers and one sorter, one workgroup
+// per compute unit (the trays fill most of its LDS), when the rows alone do
+// not outnumber the compute units; otherwise (and for lists of 2,048 words,
+// whose registers allow one wave per SIMD) four waves, so more rows run at
+// once.
+constexpr int kDefaultWaves = 7;
+constexpr int kDefaultWavesWide = 4;
 constexpr int kDefaultWatermark = 256;
 constexpr int kMaxDevices = 64;
 constexpr int kAssumedCUs = 256;  // MI355X, used only when no device can be queried
@@ -109,7 +116,8 @@ Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cu
     p.cus = cus;
     p.E = list_multiplier(k);
     const int list_words = 64 * p.E;
-    p.waves = (o && o->waves) ? o->waves : kDefaultWaves;
+    p.waves = (o && o->waves) ? o->waves
+                              : (p.E >= 32 || rows > cus ? kDefaultWavesWide : kDefaultWaves);
     p.watermark = (o && o->watermark) ? o->watermark : kDefaultWatermark;
     if (p.watermark < 64) p.watermark = 64;
     p.tray = p.watermark + kBlock;  // a tray below the mark never overflows in one block
@@ -121,10 +129,13 @@ Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cu
     if (o && o->split) {
         p.split = o->split;
     } else {
-        // Enough workgroups for about two per compute unit, but at least four
-        // blocks per wave so every stream does real work.
+        // Enough workgroups to fill every compute unit once (as many per
+        // unit as its LDS holds), but at least four blocks per wave so every
+        // stream does real work.
         const int64_t nb = ((int64_t)n + 3 + kBlock - 1) / kBlock;
-        const int64_t target = 2 * (int64_t)cus;
+        const int64_t per_cu = std::max<int64_t>(
+            1, (int64_t)((kLdsPerWorkgroup - kStaticLdsBound) / std::max<size_t>(p.lds, 1)));
+        const int64_t target = per_cu * (int64_t)cus;
         int64_t s = rows > 0 ? (target + rows - 1) / rows : 1;
         int64_t cap = nb / (4 * (int64_t)streamers);
         if (cap < 1) cap = 1;
