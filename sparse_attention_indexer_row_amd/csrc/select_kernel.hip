@@ -955,15 +955,18 @@ __device__ __forceinline__ void reset_sorter(SorterState &ss, uint32_t *hist, ui
 
 // Folds kept lists from the workspace into acc (descending): the lists at
 // slots first + t*stride for t < count, except slot `skip`, fetched
-// kMergeBatch at a time (all loads of a batch in flight together), each
-// cleared right after it is merged.
+// merge_batch<E>() at a time (all loads of a batch in flight together),
+// each cleared right after it is merged.
 template <int E>
 __device__ __forceinline__ void merge_lists(uint64_t (&acc)[E], uint64_t *lists, uint32_t first,
                                             uint32_t count, uint32_t stride, uint32_t skip,
                                             uint32_t lane);
 
 constexpr uint32_t kVerdictExit = 1u;
-constexpr uint32_t kMergeBatch = 3;    // segment lists in flight during the leader's merge
+// Segment lists in flight during a leader's merge (the widest lists have
+// registers for one at a time).
+template <int E>
+constexpr uint32_t merge_batch() { return E <= 8 ? 3u : 1u; }
 constexpr uint32_t kVerdictRerun = 2u;
 
 template <int E>
@@ -974,18 +977,19 @@ __device__ __forceinline__ void merge_lists(uint64_t (&acc)[E], uint64_t *lists,
     uint64_t zero[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) zero[e] = 0ull;
-    for (uint32_t t = 0; t < count; t += kMergeBatch) {
-        uint64_t nb[kMergeBatch][E];
-        bool use[kMergeBatch];
-        uint32_t slot[kMergeBatch];
+    constexpr uint32_t kB = merge_batch<E>();
+    for (uint32_t t = 0; t < count; t += kB) {
+        uint64_t nb[kB][E];
+        bool use[kB];
+        uint32_t slot[kB];
 #pragma unroll
-        for (uint32_t a = 0; a < kMergeBatch; ++a) {
+        for (uint32_t a = 0; a < kB; ++a) {
             slot[a] = first + (t + a) * stride;
             use[a] = t + a < count && slot[a] != skip;
             if (use[a]) load_list_reversed<E>(nb[a], lists + (size_t)slot[a] * KP, lane);
         }
 #pragma unroll
-        for (uint32_t a = 0; a < kMergeBatch; ++a) {
+        for (uint32_t a = 0; a < kB; ++a) {
             if (use[a]) {
                 keep_best<E>(acc, nb[a], lane);
                 store_list<E>(lists + (size_t)slot[a] * KP, zero, lane);
@@ -1133,30 +1137,33 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         }
         old = __builtin_amdgcn_readfirstlane((int)old);
         bool lead = old == gsz - 1u;
-        if (lead) {
+        // Level 0 merges the group's lists, level 1 the groups' lists; a
+        // leader's own list (its segment's, then its group's) is already
+        // in registers and is cleared instead of read.
+        uint32_t first = g0, count = gsz, stride = 1u, own = s;
+        for (int level = 0; lead; ++level) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            // The group leader's own list is not read again: clear it.
             uint64_t zero[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) zero[e] = 0ull;
-            store_list<E>(lists + (size_t)s * KP, zero, lane);
-            merge_lists<E>(kept_sorted, lists, g0, gsz, 1u, s, lane);
+            store_list<E>(lists + (size_t)own * KP, zero, lane);
+            merge_lists<E>(kept_sorted, lists, first, count, stride, own, lane);
+            if (level == 1 || ng == 1u) break;
             if (lane == 0) __hip_atomic_store(gticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (ng > 1u) {
-                store_list<E>(lists + (size_t)g0 * KP, kept_sorted, lane);
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-                if (lane == 0) {
-                    old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-                }
-                old = __builtin_amdgcn_readfirstlane((int)old);
-                lead = old == ng - 1u;
-                if (lead) {
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                    store_list<E>(lists + (size_t)g0 * KP, zero, lane);
-                    merge_lists<E>(kept_sorted, lists, 0u, ng, G, g0, lane);
-                }
+            store_list<E>(lists + (size_t)g0 * KP, kept_sorted, lane);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            if (lane == 0) {
+                old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+            old = __builtin_amdgcn_readfirstlane((int)old);
+            lead = old == ng - 1u;
+            first = 0u;
+            count = ng;
+            stride = G;
+            own = g0;
+        }
+        if (lead && ng == 1u && lane == 0) {
+            __hip_atomic_store(gticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (!lead) {
             set_verdict(kVerdictExit);
