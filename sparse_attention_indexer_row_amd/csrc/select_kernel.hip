@@ -160,7 +160,7 @@ template <int E, bool LANE_BOUNDS, bool RAGGED>
 __device__ __forceinline__ uint32_t admit_block(uint64_t *tray, uint32_t cnt, uint64_t T,
                                                 int32_t tb, const float4 (&x)[kLoadsPerBlock],
                                                 uint32_t vbase, uint32_t off0, uint32_t vend,
-                                                uint32_t (&lk)[E], uint32_t lane) {
+                                                uint32_t (&lk)[E], uint32_t &kmx, uint32_t lane) {
     int32_t v[kLoadsPerBlock][4];
     int32_t m4[kLoadsPerBlock];
 #pragma unroll
@@ -193,7 +193,10 @@ __device__ __forceinline__ uint32_t admit_block(uint64_t *tray, uint32_t cnt, ui
             const bool pass = pre & (w > T);
             const uint64_t mk = __ballot(pass);
             if (mk != 0ull) {
-                if (pass) tray[cnt + mbcnt64(mk)] = w;
+                if (pass) {
+                    tray[cnt + mbcnt64(mk)] = w;
+                    kmx = max(kmx, (uint32_t)(w >> 32));
+                }
                 cnt += (uint32_t)__popcll(mk);
             }
         }
@@ -527,11 +530,14 @@ __device__ __forceinline__ void prune_pool(SorterState &ss, uint64_t *pool, uint
 // key histogram, and the histogram's bound raises the threshold.  When the
 // bound sits in the top quarter of the histogram's range, the range is
 // re-fitted to [threshold key, largest key] and recounted, so the bound
-// keeps tracking the k-th best closely.
+// keeps tracking the k-th best closely.  A `last` tray (a stream's final
+// one) is appended without counting: the histogram then covers a subset of
+// the pool, so its bound stays valid.
 template <int E, bool SPLIT>
 __device__ __forceinline__ void merge_tray(SorterState &ss, uint64_t *pool, const uint64_t *buf,
-                                           uint32_t c, uint64_t *sT, uint64_t *gT, uint32_t k,
-                                           uint32_t *hist, uint64_t *gath, uint32_t lane) {
+                                           uint32_t c, bool last, uint64_t *sT, uint64_t *gT,
+                                           uint32_t k, uint32_t *hist, uint64_t *gath,
+                                           uint32_t lane) {
     constexpr uint32_t kPieceWords = (uint32_t)(kPiece * kWave);
     for (uint32_t off = 0; off < c; off += kPieceWords) {
         ss.T = umax64(ss.T, lds_load_word(sT));
@@ -567,13 +573,18 @@ __device__ __forceinline__ void merge_tray(SorterState &ss, uint64_t *pool, cons
                     pool[ss.pc + mbcnt64(m)] = v[j];
                     const uint32_t key = (uint32_t)(v[j] >> 32);
                     lkmax = max(lkmax, key);
-                    if (key >= ss.base) atomicAdd(&hist[bucket_of(key, ss.base, ss.shift)], 1u);
+                    if (!last && key >= ss.base) {
+                        atomicAdd(&hist[bucket_of(key, ss.base, ss.shift)], 1u);
+                    }
                 }
                 ss.pc += (uint32_t)__popcll(m);
             }
         }
         ss.kmax = max(ss.kmax, wave_max32(lkmax, lane));
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+        // A stream's last tray is only appended: no bound can help the
+        // streams any more, and the final pruning follows.
+        if (last) continue;
         uint32_t bstar = 0;
         const uint64_t hb = hist_bound(hist, k, ss.base, ss.shift, bstar, lane);
         raise_threshold<SPLIT>(ss, hb, sT, gT, lane);
@@ -684,57 +695,93 @@ __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t
     return list_word_at<kSampleGroups>(gm, jn - 1u);
 }
 
-// Streams this wave's share of a row's blocks once: visit positions q, q+Q,
-// ... of the row's visit order.  Scores whose word beats max(threshold,
-// estimate) go to the tray; full trays are published to the sorter.  Returns
-// the number of scores that entered a tray.  With tau_ready set, the
-// estimate is read from tau_src once the sorter flags it, after the first
-// loads are issued.
+// Streams a workgroup's steps of a row's visit order once.  Step j of the
+// workgroup is visit position base + j % NS + (j / NS) * Q, for the j whose
+// position is below the row's block count.  Each of the NS streamer waves
+// takes the steps j = w, w + NS, ... of the first ts * NS, computed ahead;
+// the rest are claimed one at a time from the workgroup's LDS counter
+// `claim` (zero at the start of the pass), so waves that ran faster take
+// more of the tail and all of them finish close together.  Scores whose word
+// beats max(threshold, estimate) go to the tray; full trays are published
+// to the sorter, the last one marked final.  Returns the number of scores
+// that entered a tray and raises *tray_kmax to the largest key put in a
+// tray.  With tau_ready set, the estimate is read from
+// tau_src once the sorter flags it, after the first loads are issued.
 //
-// Per block the wave does little besides the loads: the visit order is
-// computed 64 blocks ahead by the vector unit (one permutation step per
-// lane) and read back with one v_readlane; interior blocks are loaded from a
-// wave-uniform base plus a fixed per-lane offset; the shared threshold is
-// read from LDS early and folded in after the block's tests.
+// Per block the wave does little besides the loads: the static steps' visit
+// order is computed 64 blocks ahead by the vector unit (one permutation step
+// per lane) and read back with one v_readlane; interior blocks are loaded
+// from a wave-uniform base plus a fixed per-lane offset; the shared
+// threshold is read from LDS early and folded in after the block's tests.
+constexpr uint32_t kTrayFinal = 0x80000000u;   // fill flag: the stream's last tray
+
 template <int E, bool SPLIT>
 __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOrder &ord,
-                                                 uint32_t q, uint32_t Q, uint64_t tau,
+                                                 uint32_t base, uint32_t Q, uint32_t NS,
+                                                 uint32_t *claim, uint64_t tau,
                                                  uint32_t *tau_ready,
                                                  uint64_t *tau_src, uint64_t &T, uint64_t *trays,
                                                  uint32_t w, uint32_t CW, uint32_t Wm,
                                                  uint64_t *sT, uint32_t (*fill)[2], uint64_t *gT,
-                                                 uint32_t lane) {
+                                                 uint32_t *tray_kmax, uint32_t lane) {
     constexpr int D = Cfg<E>::D;
-    const uint32_t mine = q < g.nb ? (g.nb - 1u - q) / Q + 1u : 0u;
+    // Steps of the workgroup (positions grow with j).
+    uint32_t M = 0;
+    if (g.nb > base) {
+        const uint32_t rem = g.nb - base;
+        M = (rem / Q) * NS + min(rem % Q, NS);
+    }
+    // About an eighth of the steps, and at least two per wave, are claimed.
+    const uint32_t dyn = max(M / 8u, 2u * NS);
+    const uint32_t ts = M > dyn ? (M - dyn) / NS : 0u;
+    const uint32_t j0 = ts * NS;
+    const uint32_t q = base + w;
     uint32_t cur = 0, cnt = 0, entered = 0;
+    uint32_t kmx = 0;  // this lane's largest key put in a tray
     uint32_t lk[E];   // this lane's E best keys seen, descending (0 = none)
 #pragma unroll
     for (int i = 0; i < E; ++i) lk[i] = 0u;
     uint64_t *tray = trays + (size_t)(2 * w) * CW;
-    if (mine == 0u) return 0u;
+    if (M == 0u) return 0u;
 
-    // Visit list: lane j holds the block of this stream's step c0 + j.
+    // Visit list: lane j holds the block of this wave's static step c0 + j.
     uint32_t c0 = 0;
     auto visit_chunk = [&](uint32_t first) __attribute__((always_inline)) {
         const uint32_t t = first + lane;
-        return t < mine ? visit_block(ord, q + t * Q) : 0u;
+        return t < ts ? visit_block(ord, q + t * Q) : 0u;
     };
     uint32_t vis = visit_chunk(0);
+    uint32_t t_next = 0;      // next static step
+    bool claiming = true;     // the counter may still hold steps
+    // Next block of this wave; false once its steps are exhausted.
+    auto next_block = [&](uint32_t &b) __attribute__((always_inline)) {
+        if (t_next < ts) {
+            if (t_next - c0 >= (uint32_t)kWave) {   // next chunk of the visit list
+                c0 = t_next & ~(uint32_t)(kWave - 1);
+                vis = visit_chunk(c0);
+            }
+            b = (uint32_t)__builtin_amdgcn_readlane((int)vis, (int)(t_next - c0));
+            ++t_next;
+            return true;
+        }
+        if (!claiming) return false;
+        uint32_t j = 0;
+        if (lane == 0) {
+            j = __hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        j = j0 + (uint32_t)__builtin_amdgcn_readfirstlane((int)j);
+        if (j >= M) {
+            claiming = false;
+            return false;
+        }
+        b = visit_block(ord, base + j % NS + (j / NS) * Q);
+        return true;
+    };
 
     float4 buf[D][kLoadsPerBlock];
     uint32_t bid[D];
+    bool live[D];
     uint64_t gbuf[D];
-    // Block of step u; past the stream's end the last block is read again:
-    // every slot issues exactly one set of loads per visit, so the wait
-    // before each slot is the same static count every time.
-    auto block_of = [&](uint32_t u) __attribute__((always_inline)) {
-        const uint32_t tt = u < mine ? u : mine - 1u;
-        if (tt - c0 >= (uint32_t)kWave) {   // next chunk of the visit list
-            c0 = tt & ~(uint32_t)(kWave - 1);
-            vis = visit_chunk(c0);
-        }
-        return (uint32_t)__builtin_amdgcn_readlane((int)vis, (int)(tt - c0));
-    };
     auto issue = [&](float4 (&dst)[kLoadsPerBlock], uint32_t b, uint64_t &g_out)
         __attribute__((always_inline)) {
         if constexpr (SPLIT) {
@@ -757,8 +804,15 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
         }
     };
 #pragma unroll
+    for (int d = 0; d < D; ++d) live[d] = next_block(bid[d]);
+    if (!live[0]) return 0u;   // slots fill in order: no step left for this wave
+    // A slot without a step reads its previous block again (the first
+    // slot's at the start): every slot issues exactly one set of loads per
+    // visit, so the wait before each slot is the same static count every
+    // time.
+#pragma unroll
     for (int d = 0; d < D; ++d) {
-        bid[d] = block_of((uint32_t)d);
+        if (!live[d]) bid[d] = bid[0];
         issue(buf[d], bid[d], gbuf[d]);
     }
     // The first blocks are in flight while the sorter computes the estimate.
@@ -769,13 +823,13 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
     }
     const bool lane_bounds = tau == 0ull;   // the estimate, when present, is far tighter
 
-    for (uint32_t t0 = 0; t0 < mine; t0 += D) {
+    for (bool more = true; more;) {
+        more = false;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const uint32_t t = t0 + (uint32_t)d;
             const uint64_t shared_T = __hip_atomic_load(sT, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (t < mine) {
+            if (live[d]) {
                 if constexpr (SPLIT) T = umax64(T, uniform64(gbuf[d]));
                 const uint64_t F = umax64(T, tau);
                 const int32_t tb = prefilter_bound(F);
@@ -784,13 +838,13 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                 const uint32_t before = cnt;
                 if (ragged) {
                     cnt = admit_block<E, false, true>(tray, cnt, F, tb, buf[d], vbase, g.off0,
-                                                      g.vend, lk, lane);
+                                                      g.vend, lk, kmx, lane);
                 } else if (lane_bounds) {
                     cnt = admit_block<E, true, false>(tray, cnt, F, tb, buf[d], vbase, g.off0,
-                                                      g.vend, lk, lane);
+                                                      g.vend, lk, kmx, lane);
                 } else {
                     cnt = admit_block<E, false, false>(tray, cnt, F, tb, buf[d], vbase, g.off0,
-                                                       g.vend, lk, lane);
+                                                       g.vend, lk, kmx, lane);
                 }
                 entered += cnt - before;
                 if (lane_bounds && cnt != before) {
@@ -806,8 +860,11 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                         }
                     }
                 }
+                uint32_t nb = 0;
+                live[d] = next_block(nb);
+                if (live[d]) bid[d] = nb;
             }
-            bid[d] = block_of(t + (uint32_t)D);
+            more |= live[d];
             issue(buf[d], bid[d], gbuf[d]);
             T = umax64(T, uniform64(shared_T));
             if (cnt >= Wm) {
@@ -819,12 +876,17 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
             }
         }
     }
-    if (cnt > 0) publish_tray(&fill[w][cur], cnt, lane);
+    if (cnt > 0) publish_tray(&fill[w][cur], cnt | kTrayFinal, lane);
+    kmx = wave_max32(kmx, lane);
+    if (lane == 0 && kmx != 0u) {
+        __hip_atomic_fetch_max(tray_kmax, kmx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     return entered;
 }
 
 // Sorter side of one pass: folds published trays into the pool until every
-// streamer is done, then keeps exactly the best min(k, candidates) words.
+// streamer is done.  Trays still published then stay where they are: the
+// end-of-pass selection takes them with the pool.
 template <int E, bool SPLIT>
 __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_t *trays,
                                         uint32_t CW, uint32_t NS, uint32_t (*fill)[2],
@@ -832,26 +894,194 @@ __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_
                                         uint32_t k, uint32_t *hist, uint64_t *gath,
                                         uint32_t lane) {
     for (;;) {
-        const uint32_t done = lds_load_u32(done_ctr);
+        uint32_t done = lds_load_u32(done_ctr);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        if (done == NS) break;
         bool worked = false;
-        for (uint32_t v = 0; v < NS; ++v) {
+        for (uint32_t v = 0; v < NS && done < NS; ++v) {
             for (uint32_t b = 0; b < 2; ++b) {
                 const uint32_t c = lds_load_u32(&fill[v][b]);
                 if (c == 0u) continue;
+                // Once every stream is done, what is left is taken by the
+                // end-of-pass selection.
+                done = lds_load_u32(done_ctr);
+                if (done == NS) break;
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-                merge_tray<E, SPLIT>(ss, pool, trays + (size_t)(2 * v + b) * CW, c, sT, gT, k,
+                merge_tray<E, SPLIT>(ss, pool, trays + (size_t)(2 * v + b) * CW,
+                                     c & ~kTrayFinal, (c & kTrayFinal) != 0u, sT, gT, k,
                                      hist, gath, lane);
                 publish_tray(&fill[v][b], 0u, lane);
                 worked = true;
             }
         }
-        if (!worked) {
-            if (done == NS) break;
-            __builtin_amdgcn_s_sleep(2);
+        if (done == NS) break;
+        if (!worked) __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// End of a pass, run by every wave of the workgroup: the candidates are the
+// sorter's pool and every tray buffer still holding words; the best
+// min(k, n) of the n candidates >= lo go to `fin` (unordered).  Rows of 64
+// candidate words are dealt to the waves in turn.  The k-th best is found by
+// the same most-significant-digit radix selection as select_rth, with one
+// shared LDS histogram per digit pass (three in rotation, so a single
+// barrier per pass separates counting from reading), then a 64-word sort of
+// the words in the final digit's bin.  `hi` bounds every candidate from
+// above, so the first pass counts all n of them.  Returns n in every wave.
+struct EndShared {
+    uint32_t gcnt;    // words gathered for the last digit
+    uint32_t out;     // words written to fin
+};
+
+struct Candidates {
+    const uint64_t *pool;
+    uint32_t pc;
+    const uint64_t *trays;
+    uint32_t CW;
+    uint64_t busy;          // tray buffers holding words (bit i: buffer i)
+    uint32_t lane_cnt;      // lane i: word count of tray buffer i
+};
+
+__device__ __forceinline__ Candidates make_candidates(const uint64_t *pool, uint32_t pc,
+                                                      const uint64_t *trays, uint32_t CW,
+                                                      uint32_t ntrays, uint32_t *fill,
+                                                      uint32_t lane) {
+    Candidates c{pool, pc, trays, CW, 0ull, 0u};
+    if (lane < ntrays) {
+        c.lane_cnt = __hip_atomic_load(fill + lane, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP) & ~kTrayFinal;
+    }
+    c.busy = __ballot(c.lane_cnt != 0u);
+    return c;
+}
+
+// Calls f(word) for every lane of every candidate row dealt to wave w of NW
+// (word 0 where a row runs past its region's end).  The pool's rows go to
+// waves 0, 1, ... in turn, and each further region starts one wave later.
+template <typename F>
+__device__ __forceinline__ void for_my_rows(const Candidates &c, uint32_t w, uint32_t NW,
+                                            uint32_t lane, F &&f) {
+    auto region = [&](const uint64_t *base, uint32_t cnt, uint32_t j0)
+        __attribute__((always_inline)) {
+        const uint32_t rows = (cnt + (uint32_t)kWave - 1u) / (uint32_t)kWave;
+        uint32_t j = j0;
+        for (; j + NW < rows; j += 2u * NW) {   // two rows in flight
+            const uint32_t i0 = j * (uint32_t)kWave + lane;
+            const uint32_t i1 = i0 + NW * (uint32_t)kWave;
+            const uint64_t x0 = base[i0];
+            const uint64_t x1 = i1 < cnt ? base[i1] : 0ull;
+            f(x0);
+            f(x1);
+        }
+        if (j < rows) {
+            const uint32_t i = j * (uint32_t)kWave + lane;
+            f(i < cnt ? base[i] : 0ull);
+        }
+    };
+    region(c.pool, c.pc, w);
+    uint32_t j0 = w;
+    for (uint64_t m = c.busy; m != 0ull; m &= m - 1ull) {
+        const uint32_t t = (uint32_t)__ffsll((unsigned long long)m) - 1u;
+        j0 = j0 == 0u ? NW - 1u : j0 - 1u;
+        region(c.trays + (size_t)t * c.CW,
+               (uint32_t)__builtin_amdgcn_readlane((int)c.lane_cnt, (int)t), j0);
+    }
+}
+
+// Appends the words of one row for which `take` holds to dst at an offset
+// reserved from the shared counter *ctr.
+__device__ __forceinline__ void append_shared(uint64_t *dst, uint32_t *ctr, uint64_t x, bool take,
+                                              uint32_t lane) {
+    const uint64_t m = __ballot(take);
+    if (m == 0ull) return;
+    uint32_t off = 0;
+    if (lane == 0) {
+        off = __hip_atomic_fetch_add(ctr, (uint32_t)__popcll(m), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    off = (uint32_t)__builtin_amdgcn_readfirstlane((int)off);
+    if (take) dst[off + mbcnt64(m)] = x;
+}
+
+__device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo, uint64_t hi,
+                                               uint32_t k, EndShared *sh, uint32_t *hist3,
+                                               uint64_t *gath, uint64_t *fin, uint32_t w,
+                                               uint32_t NW, bool zeroer, uint32_t lane) {
+    // The counters in *sh and hist3[0] are zero and the candidates final
+    // (the caller's barrier).
+    uint32_t n = 0;
+    uint64_t kth = lo;
+    if (hi >= lo) {
+        int top = hi == lo ? 0 : 63 - __clzll(lo ^ hi);
+        uint64_t fmask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
+        uint64_t prefix = hi & fmask;
+        uint32_t r = k;
+        uint32_t bin_cnt = 0;
+        for (uint32_t pass = 0;; ++pass) {
+            uint32_t *h = hist3 + 256u * (pass % 3u);
+            uint32_t *hz = hist3 + 256u * ((pass + 1u) % 3u);
+            const int low = top >= 7 ? top - 7 : 0;
+            const uint32_t dmask = (2u << (top - low)) - 1u;
+            if (zeroer) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) hz[lane * 4 + j] = 0u;
+            }
+            for_my_rows(c, w, NW, lane, [&](uint64_t x) __attribute__((always_inline)) {
+                if (x >= lo && (x & fmask) == prefix && x != 0ull) {
+                    atomicAdd(&h[(uint32_t)(x >> low) & dmask], 1u);
+                }
+            });
+            __syncthreads();
+            uint32_t hb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hb[j] = h[lane * 4 + j];
+            const uint32_t mine = hb[0] + hb[1] + hb[2] + hb[3];
+            const uint32_t incl = wave_incl_scan(mine);
+            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+            if (pass == 0) {
+                n = total;
+                if (n <= k) break;   // every candidate is kept
+            }
+            uint32_t above = total - incl;
+            int hit = -1;
+            uint32_t hit_above = 0, hit_cnt = 0;
+#pragma unroll
+            for (int j = 3; j >= 0; --j) {
+                if (hit < 0 && above < r && r <= above + hb[j]) {
+                    hit = j;
+                    hit_above = above;
+                    hit_cnt = hb[j];
+                }
+                above += hb[j];
+            }
+            const uint64_t who = __ballot(hit >= 0);
+            const int src = (int)__ffsll((unsigned long long)who) - 1;
+            const uint32_t bin = (uint32_t)__builtin_amdgcn_readlane(
+                (int)(lane * 4 + (uint32_t)(hit < 0 ? 0 : hit)), src);
+            r -= (uint32_t)__builtin_amdgcn_readlane((int)hit_above, src);
+            bin_cnt = (uint32_t)__builtin_amdgcn_readlane((int)hit_cnt, src);
+            prefix |= (uint64_t)bin << low;
+            fmask |= (uint64_t)dmask << low;
+            if (bin_cnt <= (uint32_t)kWave) {
+                for_my_rows(c, w, NW, lane, [&](uint64_t x) __attribute__((always_inline)) {
+                    append_shared(gath, &sh->gcnt, x,
+                                  x >= lo && (x & fmask) == prefix && x != 0ull, lane);
+                });
+                __syncthreads();
+                uint64_t v[1] = {lane < bin_cnt ? gath[lane] : 0ull};
+                wave_sort<1, false>(v, lane);
+                kth = list_word_at<1>(v, r - 1u);
+                break;
+            }
+            top = low - 1;
         }
     }
-    prune_pool<E, SPLIT>(ss, pool, sT, gT, k, hist, gath, lane);
+    for_my_rows(c, w, NW, lane, [&](uint64_t x) __attribute__((always_inline)) {
+        append_shared(fin, &sh->out, x, x >= kth && x != 0ull, lane);
+    });
+    __syncthreads();
+    return n;
 }
 
 // Bitonic sort, descending, of the pool's pc words (zero padded to 64*E) by
@@ -866,17 +1096,16 @@ __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_
 // result in its usual blocked register layout.  Every wave of the workgroup
 // calls this and meets the same barriers; waves with no chunk only wait.
 template <int E, int P>
-__device__ __forceinline__ void wg_sort_impl(uint64_t *x, const uint64_t *pool,
-                                             const uint32_t *pc_p, int chunk, bool sorter,
-                                             uint64_t (&kept)[E], uint32_t lane) {
+__device__ __forceinline__ void wg_sort_impl(uint64_t *x, const uint64_t *pool, uint32_t pc,
+                                             int chunk, bool sorter, uint64_t (&kept)[E],
+                                             uint32_t lane) {
     constexpr int EP = E / P;
     constexpr uint32_t C = 64u * EP, N = 64u * E;
-    __syncthreads();   // the pool and its word count are final
+    // The input and its count are final (the caller's barrier).
     const bool active = chunk >= 0 && chunk < P;
     const uint32_t base = active ? (uint32_t)chunk * C : 0u;
     uint64_t a[EP];
     if (active) {
-        const uint32_t pc = *pc_p;
 #pragma unroll
         for (int e = 0; e < EP; ++e) {
             const uint32_t i = base + lane * EP + (uint32_t)e;
@@ -931,16 +1160,16 @@ __device__ __forceinline__ void wg_sort_impl(uint64_t *x, const uint64_t *pool,
 // The sorter takes chunk 0 and streamer w chunk w+1; four waves share the
 // sort when the workgroup has them, else two.
 template <int E>
-__device__ __forceinline__ void wg_sort(uint64_t *x, const uint64_t *pool, const uint32_t *pc_p,
+__device__ __forceinline__ void wg_sort(uint64_t *x, const uint64_t *pool, uint32_t pc,
                                         uint32_t w, uint32_t NW, bool sorter, uint64_t (&kept)[E],
                                         uint32_t lane) {
     constexpr int P4 = E < 4 ? E : 4;
     constexpr int P2 = E < 2 ? E : 2;
     const int chunk = sorter ? 0 : (int)w + 1;
     if (NW >= 4u) {
-        wg_sort_impl<E, P4>(x, pool, pc_p, chunk, sorter, kept, lane);
+        wg_sort_impl<E, P4>(x, pool, pc, chunk, sorter, kept, lane);
     } else {
-        wg_sort_impl<E, P2>(x, pool, pc_p, chunk, sorter, kept, lane);
+        wg_sort_impl<E, P2>(x, pool, pc, chunk, sorter, kept, lane);
     }
 }
 
@@ -1001,7 +1230,8 @@ __device__ __forceinline__ void merge_lists(uint64_t (&acc)[E], uint64_t *lists,
 template <int E, bool SPLIT>
 __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs p) {
     constexpr int KP = Cfg<E>::KP;
-    extern __shared__ uint64_t trays[];  // [streamers][2][tray_words], pool, gather[64], hist[256]
+    // [streamers][2][tray_words], pool, fin[64*E], gather[64], hist[3][256] (u32)
+    extern __shared__ uint64_t trays[];
     __shared__ uint64_t s_T;                      // workgroup threshold word (a lower bound)
     __shared__ uint64_t s_tau;                    // sampled estimate (0 = none)
     __shared__ uint32_t s_fill[kMaxWaves][2];     // published tray word counts
@@ -1009,6 +1239,10 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     __shared__ uint32_t s_ready;                  // estimate published
     __shared__ uint32_t s_verdict;                // after the first pass: exit or rerun
     __shared__ uint32_t s_pc;                     // pool words at the end of a pass
+    __shared__ uint32_t s_claim;                  // claimed tail steps of the current pass
+    __shared__ EndShared s_end;                   // counters of the end-of-pass selection
+    __shared__ uint32_t s_kmax;                   // largest key the streamers put in a tray
+    __shared__ uint64_t s_hi;                     // bound of the end-of-pass candidates
 
     const uint32_t lane = lane_id();
     const uint32_t w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
@@ -1031,31 +1265,56 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         s_done = 0u;
         s_ready = 0u;
         s_verdict = 0u;
+        s_claim = 0u;
+        s_kmax = 0u;
     }
     if (threadIdx.x < 2 * kMaxWaves) s_fill[threadIdx.x / 2][threadIdx.x % 2] = 0u;
     __syncthreads();
 
     const RowGeom g = row_geometry(p, r);
     const VisitOrder ord = make_visit_order(p.seed, r, g.nb);
+    uint64_t *pool = trays + (size_t)(2 * NS) * CW;            // [PoolCfg<E>::cap]
+    uint64_t *fin = pool + PoolCfg<E>::cap;                     // [KP]
+    uint64_t *gath = fin + KP;                                  // [64]
+    uint32_t *hist = reinterpret_cast<uint32_t *>(gath + kWave);  // [3][256]
+
+    // The end-of-pass selection and the one full sort of the pass, by every
+    // wave: the best min(k, n) of the pool and the trays, sorted into the
+    // sorter's `kept` (the trays hold the sort's exchange buffer).  Returns n.
+    auto end_of_pass = [&](uint64_t (&kept)[E]) __attribute__((always_inline)) {
+        __syncthreads();   // pool, its count, the trays and the bounds are final
+        const Candidates c = make_candidates(pool, lds_load_u32(&s_pc), trays, CW, 2u * NS,
+                                             &s_fill[0][0], lane);
+        const uint64_t lo = lds_load_word(&s_T);
+        const uint64_t hi = lds_load_word(&s_hi);
+        const uint32_t n = end_select(c, lo, hi, k, &s_end, hist, gath, fin, w, NW, w == NS, lane);
+        if (w == NS && lane < 2u * NS) {
+            __hip_atomic_store(&s_fill[lane >> 1][lane & 1u], 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        wg_sort<E>(trays, fin, n < k ? n : k, w, NW, w == NS, kept, lane);
+        return n;
+    };
 
     if (w < NS) {
         // ---- streamer ----
         uint64_t T = 0ull;
-        uint32_t q = s * NS + w, Q = S * NS;
+        uint32_t base = s * NS, Q = S * NS;
         uint32_t entered = 0;
         for (int pass = 0; pass < 2; ++pass) {
             // Pass 0 reads the estimate once its first loads are issued; a
             // rerun streams the whole row without it.
-            entered += stream_share<E, SPLIT>(g, ord, q, Q, 0ull, pass == 0 ? &s_ready : nullptr,
-                                              &s_tau, T, trays, w, CW,
-                                              (uint32_t)p.watermark, &s_T, s_fill, gT, lane);
+            entered += stream_share<E, SPLIT>(g, ord, base, Q, NS, &s_claim, 0ull,
+                                              pass == 0 ? &s_ready : nullptr, &s_tau, T, trays, w, CW,
+                                              (uint32_t)p.watermark, &s_T, s_fill, gT, &s_kmax,
+                                              lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             if (lane == 0) {
                 __hip_atomic_fetch_add(&s_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
             {
                 uint64_t unused[E];
-                wg_sort<E>(trays, trays + (size_t)(2 * NS) * CW, &s_pc, w, NW, false, unused, lane);
+                end_of_pass(unused);
             }
             if (pass == 1) break;
             uint32_t verdict;
@@ -1063,7 +1322,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
             if (verdict != kVerdictRerun) break;
             // Stream the whole row again, without the estimate.
-            q = w;
+            base = 0u;
             Q = NS;
         }
         if (p.stats && lane == 0 && entered > 0) {
@@ -1073,9 +1332,6 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     }
 
     // ---- sorter (wave NS) ----
-    uint64_t *pool = trays + (size_t)(2 * NS) * CW;            // [PoolCfg<E>::cap]
-    uint64_t *gath = pool + PoolCfg<E>::cap;                    // [64]
-    uint32_t *hist = reinterpret_cast<uint32_t *>(gath + kWave);  // [256]
     const uint64_t tau = estimate_threshold(g, p.seed, r, k, p.flags, lane);
     if (lane == 0) {
         s_tau = tau;
@@ -1094,7 +1350,11 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     // threshold stays (it is a valid bound of the row's k-th best).
     auto start_rerun = [&]() __attribute__((always_inline)) {
         reset_sorter(ss, hist, lane);
-        if (lane == 0) __hip_atomic_store(&s_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (lane == 0) {
+            __hip_atomic_store(&s_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(&s_claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(&s_kmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
         set_verdict(kVerdictRerun);
     };
 
@@ -1102,14 +1362,28 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     bool rerun = false;
     for (int pass = 0; pass < 2; ++pass) {
         collect<E, SPLIT>(ss, pool, trays, CW, NS, s_fill, &s_done, &s_T, gT, k, hist, gath, lane);
-        if (lane == 0) s_pc = ss.pc;
-        // The one full sort of this pass, shared with the streamer waves
-        // (they are done streaming); the trays hold the exchange buffer.
-        wg_sort<E>(trays, pool, &s_pc, NS, NW, true, kept_sorted, lane);
+        if constexpr (SPLIT) ss.T = umax64(ss.T, uniform64(ss.gnext));
+        // Every candidate's key is at most the larger of the pool's and the
+        // streamers' largest keys.
+        const uint32_t kx = max(ss.kmax, lds_load_u32(&s_kmax));
+        if (lane == 0) {
+            __hip_atomic_fetch_max(&s_T, ss.T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            s_pc = ss.pc;
+            s_end.gcnt = 0u;
+            s_end.out = 0u;
+            s_hi = ((uint64_t)kx << 32) | 0xFFFFFFFFull;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
+        const uint32_t n = end_of_pass(kept_sorted);
+        if (n > k) {
+            raise_threshold<SPLIT>(ss, list_word_at<E>(kept_sorted, k - 1), &s_T, gT, lane);
+            ++ss.sorts;
+        }
         if (!SPLIT || rerun) {
             // With an estimate in use, fewer than k admitted scores means
             // some of the row's best k may lie below it: stream again.
-            if (!rerun && tau != 0ull && ss.pc < k) {
+            if (!rerun && tau != 0ull && n < k) {
                 rerun = true;
                 start_rerun();
                 continue;

@@ -123,8 +123,10 @@ Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cu
     p.tray = p.watermark + kBlock;  // a tray below the mark never overflows in one block
     const int streamers = p.waves - 1;
     // trays, then the sorter's candidate pool (list + one 1,024-word tray
-    // piece), gather buffer and key histogram
-    p.lds = (size_t)8 * (size_t)(2 * streamers * p.tray + list_words + 1024 + kWave) + 4 * 256;
+    // piece), the end-of-pass selection's output list, gather buffer and three
+    // key histograms
+    p.lds = (size_t)8 * (size_t)(2 * streamers * p.tray + 2 * list_words + 1024 + kWave) +
+            4 * 3 * 256;
 
     if (o && o->split) {
         p.split = o->split;

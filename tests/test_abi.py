@@ -117,7 +117,8 @@ def test_plan_list_sizes_and_lds(lib):
                      (2048, 2048)]:
         p = _plan(lib, 4, 1 << 16, k)
         assert p.list_words == words
-        assert p.lds_bytes == 8 * (2 * (p.waves - 1) * p.tray_words + words + 1024 + 64) + 4 * 256
+        assert p.lds_bytes == (8 * (2 * (p.waves - 1) * p.tray_words + 2 * words + 1024 + 64)
+                               + 4 * 3 * 256)
         assert p.lds_bytes <= 160 * 1024
         assert p.tray_words == p.watermark + 1024
 
