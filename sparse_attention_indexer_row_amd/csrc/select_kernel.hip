@@ -84,10 +84,18 @@ __device__ __forceinline__ uint64_t lds_load_word(uint64_t *p) {
 
 // Kept lists are stored "transposed": list position lane*E + e sits at word
 // e*64 + lane, so a wave moves a whole list with coalesced 64-lane accesses.
+// The list's base address is pinned to scalar registers where it is used, so
+// the compiler keeps no per-element vector addresses alive across the kernel.
+__device__ __forceinline__ uint64_t *scalar_base(uint64_t *p) {
+    asm volatile("" : "+s"(p));
+    return p;
+}
+
 template <int E>
 __device__ __forceinline__ void store_list(uint64_t *dst, const uint64_t (&a)[E], uint32_t lane) {
+    uint64_t *d = scalar_base(dst);
 #pragma unroll
-    for (int e = 0; e < E; ++e) dst[e * kWave + lane] = a[e];
+    for (int e = 0; e < E; ++e) d[e * kWave + lane] = a[e];
 }
 
 // Loads a descending transposed list reversed, i.e. ascending, into the
@@ -95,8 +103,9 @@ __device__ __forceinline__ void store_list(uint64_t *dst, const uint64_t (&a)[E]
 template <int E>
 __device__ __forceinline__ void load_list_reversed(uint64_t (&a)[E], const uint64_t *src,
                                                    uint32_t lane) {
+    const uint64_t *s = scalar_base(const_cast<uint64_t *>(src));
 #pragma unroll
-    for (int e = 0; e < E; ++e) a[e] = src[(E - 1 - e) * kWave + (kWave - 1 - lane)];
+    for (int e = 0; e < E; ++e) a[e] = s[(E - 1 - e) * kWave + (kWave - 1 - lane)];
 }
 
 // Writes one output slot from a packed word (0 = empty slot).
@@ -651,7 +660,8 @@ constexpr uint32_t kFlagNoEstimate = 1u;
 constexpr uint32_t kFlagForceRerun = 2u;
 
 __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t seed, uint32_t r,
-                                                       uint32_t k, uint32_t flags, uint32_t lane) {
+                                                       uint32_t k, uint32_t flags, uint32_t *hist,
+                                                       uint64_t *gath, uint32_t lane) {
     if ((flags & kFlagNoEstimate) || g.L == 0u) return 0ull;
     const float lam = (float)k * (float)kSampleWords / (float)g.L;
     const float jf = ceilf(lam + 6.0f * sqrtf(lam) + 6.0f);
@@ -690,98 +700,74 @@ __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t
         }
     }
     // The j-th best group maximum is at most the j-th best sampled word (the
-    // maxima are a subset of the sample), so it admits at least as much.
-    wave_sort<kSampleGroups, false>(gm, lane);
-    return list_word_at<kSampleGroups>(gm, jn - 1u);
+    // maxima are a subset of the sample), so it admits at least as much.  It
+    // is found by the pool's radix selection over the 256 distinct maxima.
+    uint64_t lmin = gm[0], lmax = gm[0];
+#pragma unroll
+    for (int q = 1; q < kSampleGroups; ++q) {
+        lmin = umin64(lmin, gm[q]);
+        lmax = umax64(lmax, gm[q]);
+    }
+    const uint64_t none[1] = {0ull};
+    return select_rth(gm, none, jn, ~wave_max64(~lmin, lane), wave_max64(lmax, lane), hist, gath,
+                      lane);
 }
 
-// Streams a workgroup's steps of a row's visit order once.  Step j of the
-// workgroup is visit position base + j % NS + (j / NS) * Q, for the j whose
-// position is below the row's block count.  Each of the NS streamer waves
-// takes the steps j = w, w + NS, ... of the first ts * NS, computed ahead;
-// the rest are claimed one at a time from the workgroup's LDS counter
-// `claim` (zero at the start of the pass), so waves that ran faster take
-// more of the tail and all of them finish close together.  Scores whose word
-// beats max(threshold, estimate) go to the tray; full trays are published
-// to the sorter, the last one marked final.  Returns the number of scores
-// that entered a tray and raises *tray_kmax to the largest key put in a
-// tray.  With tau_ready set, the estimate is read from
-// tau_src once the sorter flags it, after the first loads are issued.
+// Streams this wave's share of a row's blocks once: visit positions q, q+Q,
+// ... of the row's visit order.  Scores whose word beats max(threshold,
+// estimate) go to the tray; full trays are published to the sorter.  Returns
+// the number of scores that entered a tray and raises *tray_kmax to the
+// largest key put in a tray; the last tray is marked final.  With tau_ready
+// set, the estimate is read from tau_src once the sorter flags it, after the
+// first loads are issued.
 //
-// Per block the wave does little besides the loads: the static steps' visit
-// order is computed 64 blocks ahead by the vector unit (one permutation step
-// per lane) and read back with one v_readlane; interior blocks are loaded
-// from a wave-uniform base plus a fixed per-lane offset; the shared
-// threshold is read from LDS early and folded in after the block's tests.
+// Per block the wave does little besides the loads: the visit order is
+// computed 64 blocks ahead by the vector unit (one permutation step per
+// lane) and read back with one v_readlane; interior blocks are loaded from a
+// wave-uniform base plus a fixed per-lane offset; the shared threshold is
+// read from LDS early and folded in after the block's tests.
 constexpr uint32_t kTrayFinal = 0x80000000u;   // fill flag: the stream's last tray
 
 template <int E, bool SPLIT>
 __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOrder &ord,
-                                                 uint32_t base, uint32_t Q, uint32_t NS,
-                                                 uint32_t *claim, uint64_t tau,
+                                                 uint32_t q, uint32_t Q, uint64_t tau,
                                                  uint32_t *tau_ready,
                                                  uint64_t *tau_src, uint64_t &T, uint64_t *trays,
                                                  uint32_t w, uint32_t CW, uint32_t Wm,
                                                  uint64_t *sT, uint32_t (*fill)[2], uint64_t *gT,
                                                  uint32_t *tray_kmax, uint32_t lane) {
     constexpr int D = Cfg<E>::D;
-    // Steps of the workgroup (positions grow with j).
-    uint32_t M = 0;
-    if (g.nb > base) {
-        const uint32_t rem = g.nb - base;
-        M = (rem / Q) * NS + min(rem % Q, NS);
-    }
-    // About an eighth of the steps, and at least two per wave, are claimed.
-    const uint32_t dyn = max(M / 8u, 2u * NS);
-    const uint32_t ts = M > dyn ? (M - dyn) / NS : 0u;
-    const uint32_t j0 = ts * NS;
-    const uint32_t q = base + w;
+    const uint32_t mine = q < g.nb ? (g.nb - 1u - q) / Q + 1u : 0u;
     uint32_t cur = 0, cnt = 0, entered = 0;
     uint32_t kmx = 0;  // this lane's largest key put in a tray
     uint32_t lk[E];   // this lane's E best keys seen, descending (0 = none)
 #pragma unroll
     for (int i = 0; i < E; ++i) lk[i] = 0u;
     uint64_t *tray = trays + (size_t)(2 * w) * CW;
-    if (M == 0u) return 0u;
+    if (mine == 0u) return 0u;
 
-    // Visit list: lane j holds the block of this wave's static step c0 + j.
+    // Visit list: lane j holds the block of this stream's step c0 + j.
     uint32_t c0 = 0;
     auto visit_chunk = [&](uint32_t first) __attribute__((always_inline)) {
         const uint32_t t = first + lane;
-        return t < ts ? visit_block(ord, q + t * Q) : 0u;
+        return t < mine ? visit_block(ord, q + t * Q) : 0u;
     };
     uint32_t vis = visit_chunk(0);
-    uint32_t t_next = 0;      // next static step
-    bool claiming = true;     // the counter may still hold steps
-    // Next block of this wave; false once its steps are exhausted.
-    auto next_block = [&](uint32_t &b) __attribute__((always_inline)) {
-        if (t_next < ts) {
-            if (t_next - c0 >= (uint32_t)kWave) {   // next chunk of the visit list
-                c0 = t_next & ~(uint32_t)(kWave - 1);
-                vis = visit_chunk(c0);
-            }
-            b = (uint32_t)__builtin_amdgcn_readlane((int)vis, (int)(t_next - c0));
-            ++t_next;
-            return true;
-        }
-        if (!claiming) return false;
-        uint32_t j = 0;
-        if (lane == 0) {
-            j = __hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-        j = j0 + (uint32_t)__builtin_amdgcn_readfirstlane((int)j);
-        if (j >= M) {
-            claiming = false;
-            return false;
-        }
-        b = visit_block(ord, base + j % NS + (j / NS) * Q);
-        return true;
-    };
 
     float4 buf[D][kLoadsPerBlock];
     uint32_t bid[D];
-    bool live[D];
     uint64_t gbuf[D];
+    // Block of step u; past the stream's end the last block is read again:
+    // every slot issues exactly one set of loads per visit, so the wait
+    // before each slot is the same static count every time.
+    auto block_of = [&](uint32_t u) __attribute__((always_inline)) {
+        const uint32_t tt = u < mine ? u : mine - 1u;
+        if (tt - c0 >= (uint32_t)kWave) {   // next chunk of the visit list
+            c0 = tt & ~(uint32_t)(kWave - 1);
+            vis = visit_chunk(c0);
+        }
+        return (uint32_t)__builtin_amdgcn_readlane((int)vis, (int)(tt - c0));
+    };
     auto issue = [&](float4 (&dst)[kLoadsPerBlock], uint32_t b, uint64_t &g_out)
         __attribute__((always_inline)) {
         if constexpr (SPLIT) {
@@ -804,15 +790,8 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
         }
     };
 #pragma unroll
-    for (int d = 0; d < D; ++d) live[d] = next_block(bid[d]);
-    if (!live[0]) return 0u;   // slots fill in order: no step left for this wave
-    // A slot without a step reads its previous block again (the first
-    // slot's at the start): every slot issues exactly one set of loads per
-    // visit, so the wait before each slot is the same static count every
-    // time.
-#pragma unroll
     for (int d = 0; d < D; ++d) {
-        if (!live[d]) bid[d] = bid[0];
+        bid[d] = block_of((uint32_t)d);
         issue(buf[d], bid[d], gbuf[d]);
     }
     // The first blocks are in flight while the sorter computes the estimate.
@@ -823,13 +802,13 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
     }
     const bool lane_bounds = tau == 0ull;   // the estimate, when present, is far tighter
 
-    for (bool more = true; more;) {
-        more = false;
+    for (uint32_t t0 = 0; t0 < mine; t0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
+            const uint32_t t = t0 + (uint32_t)d;
             const uint64_t shared_T = __hip_atomic_load(sT, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (live[d]) {
+            if (t < mine) {
                 if constexpr (SPLIT) T = umax64(T, uniform64(gbuf[d]));
                 const uint64_t F = umax64(T, tau);
                 const int32_t tb = prefilter_bound(F);
@@ -860,11 +839,8 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                         }
                     }
                 }
-                uint32_t nb = 0;
-                live[d] = next_block(nb);
-                if (live[d]) bid[d] = nb;
             }
-            more |= live[d];
+            bid[d] = block_of(t + (uint32_t)D);
             issue(buf[d], bid[d], gbuf[d]);
             T = umax64(T, uniform64(shared_T));
             if (cnt >= Wm) {
@@ -1011,7 +987,6 @@ __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo,
     // The counters in *sh and hist3[0] are zero and the candidates final
     // (the caller's barrier).
     uint32_t n = 0;
-    uint64_t kth = lo;
     if (hi >= lo) {
         int top = hi == lo ? 0 : 63 - __clzll(lo ^ hi);
         uint64_t fmask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
@@ -1063,22 +1038,30 @@ __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo,
             bin_cnt = (uint32_t)__builtin_amdgcn_readlane((int)hit_cnt, src);
             prefix |= (uint64_t)bin << low;
             fmask |= (uint64_t)dmask << low;
-            if (bin_cnt <= (uint32_t)kWave) {
-                for_my_rows(c, w, NW, lane, [&](uint64_t x) __attribute__((always_inline)) {
-                    append_shared(gath, &sh->gcnt, x,
-                                  x >= lo && (x & fmask) == prefix && x != 0ull, lane);
-                });
-                __syncthreads();
+            if (bin_cnt <= (uint32_t)kWave) break;
+            top = low - 1;
+        }
+        if (n > k) {
+            // Words above the final bin are kept (k - r of them); the bin's
+            // words are gathered and ranked, and its best r complete the list.
+            for_my_rows(c, w, NW, lane, [&](uint64_t x) __attribute__((always_inline)) {
+                const bool in = x >= lo && x != 0ull;
+                const uint64_t xm = x & fmask;
+                append_shared(fin, &sh->out, x, in && xm > prefix, lane);
+                append_shared(gath, &sh->gcnt, x, in && xm == prefix, lane);
+            });
+            __syncthreads();
+            if (zeroer) {
                 uint64_t v[1] = {lane < bin_cnt ? gath[lane] : 0ull};
                 wave_sort<1, false>(v, lane);
-                kth = list_word_at<1>(v, r - 1u);
-                break;
+                if (lane < r) fin[k - r + lane] = v[0];
             }
-            top = low - 1;
+            __syncthreads();
+            return n;
         }
     }
     for_my_rows(c, w, NW, lane, [&](uint64_t x) __attribute__((always_inline)) {
-        append_shared(fin, &sh->out, x, x >= kth && x != 0ull, lane);
+        append_shared(fin, &sh->out, x, x >= lo && x != 0ull, lane);
     });
     __syncthreads();
     return n;
@@ -1239,7 +1222,6 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     __shared__ uint32_t s_ready;                  // estimate published
     __shared__ uint32_t s_verdict;                // after the first pass: exit or rerun
     __shared__ uint32_t s_pc;                     // pool words at the end of a pass
-    __shared__ uint32_t s_claim;                  // claimed tail steps of the current pass
     __shared__ EndShared s_end;                   // counters of the end-of-pass selection
     __shared__ uint32_t s_kmax;                   // largest key the streamers put in a tray
     __shared__ uint64_t s_hi;                     // bound of the end-of-pass candidates
@@ -1265,7 +1247,6 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         s_done = 0u;
         s_ready = 0u;
         s_verdict = 0u;
-        s_claim = 0u;
         s_kmax = 0u;
     }
     if (threadIdx.x < 2 * kMaxWaves) s_fill[threadIdx.x / 2][threadIdx.x % 2] = 0u;
@@ -1299,13 +1280,13 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     if (w < NS) {
         // ---- streamer ----
         uint64_t T = 0ull;
-        uint32_t base = s * NS, Q = S * NS;
+        uint32_t q = s * NS + w, Q = S * NS;
         uint32_t entered = 0;
         for (int pass = 0; pass < 2; ++pass) {
             // Pass 0 reads the estimate once its first loads are issued; a
             // rerun streams the whole row without it.
-            entered += stream_share<E, SPLIT>(g, ord, base, Q, NS, &s_claim, 0ull,
-                                              pass == 0 ? &s_ready : nullptr, &s_tau, T, trays, w, CW,
+            entered += stream_share<E, SPLIT>(g, ord, q, Q, 0ull, pass == 0 ? &s_ready : nullptr,
+                                              &s_tau, T, trays, w, CW,
                                               (uint32_t)p.watermark, &s_T, s_fill, gT, &s_kmax,
                                               lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -1322,7 +1303,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
             if (verdict != kVerdictRerun) break;
             // Stream the whole row again, without the estimate.
-            base = 0u;
+            q = w;
             Q = NS;
         }
         if (p.stats && lane == 0 && entered > 0) {
@@ -1332,7 +1313,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     }
 
     // ---- sorter (wave NS) ----
-    const uint64_t tau = estimate_threshold(g, p.seed, r, k, p.flags, lane);
+    const uint64_t tau = estimate_threshold(g, p.seed, r, k, p.flags, hist, gath, lane);
     if (lane == 0) {
         s_tau = tau;
         __hip_atomic_store(&s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1352,7 +1333,6 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         reset_sorter(ss, hist, lane);
         if (lane == 0) {
             __hip_atomic_store(&s_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            __hip_atomic_store(&s_claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __hip_atomic_store(&s_kmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         set_verdict(kVerdictRerun);
