@@ -84,48 +84,55 @@ __device__ __forceinline__ uint64_t lds_load_word(uint64_t *p) {
 
 // Kept lists are stored "transposed": list position lane*E + e sits at word
 // e*64 + lane, so a wave moves a whole list with coalesced 64-lane accesses.
-// The list's base address is pinned to scalar registers where it is used, so
-// the compiler keeps no per-element vector addresses alive across the kernel.
-__device__ __forceinline__ uint64_t *scalar_base(uint64_t *p) {
-    asm volatile("" : "+s"(p));
-    return p;
+// Word offset of list slot `slot`, made opaque where it is used: the
+// compiler then addresses the list from scalar registers at each access
+// instead of keeping per-element vector addresses alive across the kernel.
+template <int E>
+__device__ __forceinline__ uint32_t list_offset(uint32_t slot) {
+    uint32_t off = slot * (uint32_t)(kWave * E);
+    asm volatile("" : "+s"(off));
+    return off;
 }
 
 template <int E>
-__device__ __forceinline__ void store_list(uint64_t *dst, const uint64_t (&a)[E], uint32_t lane) {
-    uint64_t *d = scalar_base(dst);
+__device__ __forceinline__ void store_list(uint64_t *lists, uint32_t slot, const uint64_t (&a)[E],
+                                           uint32_t lane) {
+    const uint32_t off = list_offset<E>(slot);
 #pragma unroll
-    for (int e = 0; e < E; ++e) d[e * kWave + lane] = a[e];
+    for (int e = 0; e < E; ++e) lists[off + (uint32_t)(e * kWave) + lane] = a[e];
 }
 
 // Loads a descending transposed list reversed, i.e. ascending, into the
 // blocked register layout.
 template <int E>
-__device__ __forceinline__ void load_list_reversed(uint64_t (&a)[E], const uint64_t *src,
-                                                   uint32_t lane) {
-    const uint64_t *s = scalar_base(const_cast<uint64_t *>(src));
+__device__ __forceinline__ void load_list_reversed(uint64_t (&a)[E], const uint64_t *lists,
+                                                   uint32_t slot, uint32_t lane) {
+    const uint32_t off = list_offset<E>(slot);
 #pragma unroll
-    for (int e = 0; e < E; ++e) a[e] = s[(E - 1 - e) * kWave + (kWave - 1 - lane)];
-}
-
-// Writes one output slot from a packed word (0 = empty slot).
-__device__ __forceinline__ void write_slot(float *vals, int32_t *idx, uint32_t i, uint64_t w) {
-    if (w != 0) {
-        vals[i] = __uint_as_float(key_bits((uint32_t)(w >> 32)));
-        idx[i] = (int32_t)word_pos(w);
-    } else {
-        vals[i] = -__builtin_inff();
-        idx[i] = -1;
+    for (int e = 0; e < E; ++e) {
+        a[e] = lists[off + (uint32_t)((E - 1 - e) * kWave) + (uint32_t)(kWave - 1) - lane];
     }
 }
 
+// Writes the first k positions of a descending list (blocked layout) as
+// values and indices; an empty word (0) becomes -inf and -1.  The list goes
+// through the LDS buffer x (64*E words) so that consecutive lanes write
+// consecutive positions.
 template <int E>
 __device__ __forceinline__ void write_row(float *vals, int32_t *idx, uint32_t k,
-                                          const uint64_t (&kept)[E], uint32_t lane) {
+                                          const uint64_t (&kept)[E], uint64_t *x, uint32_t lane) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[lane * E + (uint32_t)e] = kept[e];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const uint32_t i = lane * E + (uint32_t)e;
-        if (i < k) write_slot(vals, idx, i, kept[e]);
+        const uint32_t i = (uint32_t)(e * kWave) + lane;
+        if (i < k) {
+            const uint64_t w = x[i];
+            vals[i] = w != 0ull ? __uint_as_float(key_bits((uint32_t)(w >> 32)))
+                                : -__builtin_inff();
+            idx[i] = w != 0ull ? (int32_t)word_pos(w) : -1;
+        }
     }
 }
 
@@ -1185,7 +1192,6 @@ template <int E>
 __device__ __forceinline__ void merge_lists(uint64_t (&acc)[E], uint64_t *lists, uint32_t first,
                                             uint32_t count, uint32_t stride, uint32_t skip,
                                             uint32_t lane) {
-    constexpr int KP = Cfg<E>::KP;
     uint64_t zero[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) zero[e] = 0ull;
@@ -1198,13 +1204,13 @@ __device__ __forceinline__ void merge_lists(uint64_t (&acc)[E], uint64_t *lists,
         for (uint32_t a = 0; a < kB; ++a) {
             slot[a] = first + (t + a) * stride;
             use[a] = t + a < count && slot[a] != skip;
-            if (use[a]) load_list_reversed<E>(nb[a], lists + (size_t)slot[a] * KP, lane);
+            if (use[a]) load_list_reversed<E>(nb[a], lists, slot[a], lane);
         }
 #pragma unroll
         for (uint32_t a = 0; a < kB; ++a) {
             if (use[a]) {
                 keep_best<E>(acc, nb[a], lane);
-                store_list<E>(lists + (size_t)slot[a] * KP, zero, lane);
+                store_list<E>(lists, slot[a], zero, lane);
             }
         }
     }
@@ -1383,7 +1389,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         const uint32_t grp = s / G, g0 = grp * G;
         const uint32_t gsz = S - g0 < G ? S - g0 : G;
         uint32_t *gticket = p.ws_groups + (size_t)r * ng + grp;
-        store_list<E>(lists + (size_t)s * KP, kept_sorted, lane);
+        store_list<E>(lists, s, kept_sorted, lane);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         uint32_t old = 0;
         if (lane == 0) {
@@ -1400,11 +1406,11 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
             uint64_t zero[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) zero[e] = 0ull;
-            store_list<E>(lists + (size_t)own * KP, zero, lane);
+            store_list<E>(lists, own, zero, lane);
             merge_lists<E>(kept_sorted, lists, first, count, stride, own, lane);
             if (level == 1 || ng == 1u) break;
             if (lane == 0) __hip_atomic_store(gticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            store_list<E>(lists + (size_t)g0 * KP, kept_sorted, lane);
+            store_list<E>(lists, g0, kept_sorted, lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             if (lane == 0) {
                 old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1438,7 +1444,8 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     if (p.stats && lane == 0 && ss.sorts > 0) {
         atomicAdd(p.stats + 2 * (size_t)r + 1, (unsigned long long)ss.sorts);
     }
-    write_row<E>(p.out_vals + (size_t)r * k, p.out_idx + (size_t)r * k, k, kept_sorted, lane);
+    write_row<E>(p.out_vals + (size_t)r * k, p.out_idx + (size_t)r * k, k, kept_sorted, trays,
+                 lane);
     if constexpr (SPLIT) {
         // Leave this row's part of the workspace all zero (the lists were
         // cleared behind the merge), so the next call may use the same
