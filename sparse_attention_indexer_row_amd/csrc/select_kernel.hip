@@ -160,6 +160,39 @@ __device__ __forceinline__ void insert_lane_key(uint32_t (&lk)[E], uint32_t v) {
     }
 }
 
+// The E-th best key among this lane's 16 scores of an interior block (E <=
+// 16): an in-register bitonic sort, descending.  Over the wave, at least
+// 64*E >= k of the block's scores have keys at or above the smallest lane's
+// answer, so that key is a lower bound of the row's k-th best.
+template <int E>
+__device__ __forceinline__ uint32_t block_rank_key(const float4 (&x)[kLoadsPerBlock]) {
+    uint32_t v[16];
+#pragma unroll
+    for (int u = 0; u < kLoadsPerBlock; ++u) {
+        v[4 * u + 0] = order_key(__float_as_uint(x[u].x));
+        v[4 * u + 1] = order_key(__float_as_uint(x[u].y));
+        v[4 * u + 2] = order_key(__float_as_uint(x[u].z));
+        v[4 * u + 3] = order_key(__float_as_uint(x[u].w));
+    }
+#pragma unroll
+    for (int size = 2; size <= 16; size <<= 1) {
+#pragma unroll
+        for (int j = size >> 1; j > 0; j >>= 1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const uint32_t hi = max(v[i], v[l]), lo = min(v[i], v[l]);
+                    const bool desc = (i & size) == 0 || size == 16;
+                    v[i] = desc ? hi : lo;
+                    v[l] = desc ? lo : hi;
+                }
+            }
+        }
+    }
+    return v[E - 1];
+}
+
 // Test and tray compaction of one block already in registers.  Cheap tests
 // first, all on the integer bits against `tb`: the lane's whole block (when
 // an estimate filters the stream, so most blocks stop there), then each
@@ -833,6 +866,25 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                                                        g.vend, lk, kmx, lane);
                 }
                 entered += cnt - before;
+                if constexpr (E <= 16) {
+                    if (!ragged && cnt - before >= (uint32_t)(kWave * E)) {
+                        // This block alone filled a kept list's worth of the
+                        // tray (a sorted run, say): bound the k-th best by it.
+                        const uint32_t kb = wave_min32(block_rank_key<E>(buf[d]), lane);
+                        const uint64_t lb = (uint64_t)kb << 32;
+                        if (lb > T) {
+                            T = lb;
+                            if (lane == 0) {
+                                __hip_atomic_fetch_max(sT, lb, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                                if constexpr (SPLIT) {
+                                    __hip_atomic_fetch_max(gT, lb, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                                }
+                            }
+                        }
+                    }
+                }
                 if (lane_bounds && cnt != before) {
                     // 64*E >= k distinct elements have keys >= the smallest
                     // lane's E-th best key: a lower bound of the k-th best.

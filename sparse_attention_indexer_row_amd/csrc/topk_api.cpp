@@ -17,12 +17,11 @@ using topk::kBlock;
 using topk::kWave;
 
 constexpr size_t kAlign = 256;
-// Default waves per workgroup: six streamers and one sorter, one workgroup
-// per compute unit (the trays fill most of its LDS), when the rows alone do
-// not outnumber the compute units; otherwise (and for lists of 2,048 words,
-// whose registers allow one wave per SIMD) four waves, so more rows run at
-// once.
-constexpr int kDefaultWaves = 7;
+// Default waves per workgroup: when the rows alone do not outnumber the
+// compute units, as many as the LDS holds trays for, up to eight (seven
+// streamers and one sorter, one workgroup per compute unit); otherwise (and
+// for lists of 2,048 words, whose registers allow one wave per SIMD) four
+// waves, so more rows run at once.
 constexpr int kDefaultWavesWide = 4;
 constexpr int kDefaultWatermark = 256;
 constexpr int kMaxDevices = 64;
@@ -116,17 +115,28 @@ Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cu
     p.cus = cus;
     p.E = list_multiplier(k);
     const int list_words = 64 * p.E;
-    p.waves = (o && o->waves) ? o->waves
-                              : (p.E >= 32 || rows > cus ? kDefaultWavesWide : kDefaultWaves);
     p.watermark = (o && o->watermark) ? o->watermark : kDefaultWatermark;
     if (p.watermark < 64) p.watermark = 64;
     p.tray = p.watermark + kBlock;  // a tray below the mark never overflows in one block
-    const int streamers = p.waves - 1;
     // trays, then the sorter's candidate pool (list + one 1,024-word tray
     // piece), the end-of-pass selection's output list, gather buffer and three
     // key histograms
-    p.lds = (size_t)8 * (size_t)(2 * streamers * p.tray + 2 * list_words + 1024 + kWave) +
-            4 * 3 * 256;
+    auto lds_for = [&](int waves) {
+        return (size_t)8 * (size_t)(2 * (waves - 1) * p.tray + 2 * list_words + 1024 + kWave) +
+               4 * 3 * 256;
+    };
+    if (o && o->waves) {
+        p.waves = o->waves;
+    } else if (p.E >= 32 || rows > cus) {
+        p.waves = kDefaultWavesWide;
+    } else {
+        p.waves = topk::kMaxWaves;
+        while (p.waves > kDefaultWavesWide &&
+               lds_for(p.waves) + kStaticLdsBound > kLdsPerWorkgroup) {
+            --p.waves;
+        }
+    }
+    p.lds = lds_for(p.waves);
 
     if (o && o->split) {
         p.split = o->split;
@@ -139,7 +149,7 @@ Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cu
             1, (int64_t)((kLdsPerWorkgroup - kStaticLdsBound) / std::max<size_t>(p.lds, 1)));
         const int64_t target = per_cu * (int64_t)cus;
         int64_t s = rows > 0 ? (target + rows - 1) / rows : 1;
-        int64_t cap = nb / (4 * (int64_t)streamers);
+        int64_t cap = nb / (4 * (int64_t)(p.waves - 1));
         if (cap < 1) cap = 1;
         if (s > cap) s = cap;
         if (s > TOPK_MAX_SPLIT) s = TOPK_MAX_SPLIT;
