@@ -740,13 +740,20 @@ __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t
         }
     }
     // The j-th best group maximum is at most the j-th best sampled word (the
-    // maxima are a subset of the sample), so it admits at least as much.  It
-    // is found by the pool's radix selection over the 256 distinct maxima.
+    // maxima are a subset of the sample), so it admits at least as much.
+    // For j <= 64 the j-th best of the 64 lane maxima (a subset again) is
+    // used, which one 64-word sort finds; otherwise the pool's radix
+    // selection over the 256 distinct group maxima.
     uint64_t lmin = gm[0], lmax = gm[0];
 #pragma unroll
     for (int q = 1; q < kSampleGroups; ++q) {
         lmin = umin64(lmin, gm[q]);
         lmax = umax64(lmax, gm[q]);
+    }
+    if (jn <= (uint32_t)kWave) {
+        uint64_t v[1] = {lmax};
+        wave_sort<1, false>(v, lane);
+        return list_word_at<1>(v, jn - 1u);
     }
     const uint64_t none[1] = {0ull};
     return select_rth(gm, none, jn, ~wave_max64(~lmin, lane), wave_max64(lmax, lane), hist, gath,
