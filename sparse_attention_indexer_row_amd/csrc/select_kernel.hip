@@ -358,6 +358,24 @@ __device__ __forceinline__ uint32_t write_ge(uint64_t *dst, uint32_t n, const ui
     return n;
 }
 
+// Bits that hold a position: 0xFFFFFFFF - position, for positions below 2^b,
+// has ones in bits b..31 in every word of a row of length L.
+__device__ __forceinline__ int position_bits(uint32_t L) {
+    return L > 2u ? 32 - __clz(L - 1u) : 1;
+}
+
+// Radix selection over packed words: when the next digit would fall inside
+// the low half's all-ones bits, fixes them at once and moves below them.
+__device__ __forceinline__ void skip_fixed_bits(int &top, uint64_t &fmask, uint64_t &prefix,
+                                                int pbits) {
+    if (top < 32 && top >= pbits) {
+        const uint64_t ones = ((2ull << top) - 1ull) & ~((1ull << pbits) - 1ull);
+        fmask |= ones;
+        prefix |= ones;
+        top = pbits - 1;
+    }
+}
+
 template <int N>
 __device__ __forceinline__ void count_digits(const uint64_t (&a)[N], uint64_t fmask,
                                              uint64_t prefix, int low, uint32_t dmask,
@@ -393,12 +411,13 @@ __device__ __forceinline__ uint32_t gather_prefix(const uint64_t (&a)[N], uint64
 // 64-word register sort.
 template <int NA, int NB>
 __device__ __forceinline__ uint64_t select_rth(const uint64_t (&a)[NA], const uint64_t (&b)[NB],
-                                               uint32_t r, uint64_t lo, uint64_t hi,
+                                               uint32_t r, uint64_t lo, uint64_t hi, int pbits,
                                                uint32_t *hist, uint64_t *gath, uint32_t lane) {
     int top = 63 - __clzll(lo ^ hi);
     uint64_t fmask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
     uint64_t prefix = hi & fmask;
     for (;;) {
+        skip_fixed_bits(top, fmask, prefix, pbits);
         const int low = top >= 7 ? top - 7 : 0;
         const uint32_t dmask = (2u << (top - low)) - 1u;
 #pragma unroll
@@ -462,6 +481,7 @@ struct SorterState {
     uint32_t kmax;    // largest key ever added to the pool
     uint32_t sorts;   // exact selections run
     uint64_t gnext;   // split rows: the row's threshold word, read one tray piece ahead
+    int pbits;        // position bits of the row (see position_bits)
 };
 
 // Bucket of key x (x >= base); the top bucket is open-ended.
@@ -566,7 +586,7 @@ __device__ __forceinline__ void prune_pool(SorterState &ss, uint64_t *pool, uint
     }
     uint64_t nt = 0ull;
     if (n > k) {
-        nt = select_rth(a, b, k, ss.T, wave_max64(lmx, lane), hist, gath, lane);
+        nt = select_rth(a, b, k, ss.T, wave_max64(lmx, lane), ss.pbits, hist, gath, lane);
         ++ss.sorts;
     }
     const uint32_t w = write_ge(pool, 0, a, nt, lane);
@@ -756,8 +776,8 @@ __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t
         return list_word_at<1>(v, jn - 1u);
     }
     const uint64_t none[1] = {0ull};
-    return select_rth(gm, none, jn, ~wave_max64(~lmin, lane), wave_max64(lmax, lane), hist, gath,
-                      lane);
+    return select_rth(gm, none, jn, ~wave_max64(~lmin, lane), wave_max64(lmax, lane),
+                      position_bits(g.L), hist, gath, lane);
 }
 
 // Streams this wave's share of a row's blocks once: visit positions q, q+Q,
@@ -865,12 +885,20 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                 if (ragged) {
                     cnt = admit_block<E, false, true>(tray, cnt, F, tb, buf[d], vbase, g.off0,
                                                       g.vend, lk, kmx, lane);
-                } else if (lane_bounds) {
-                    cnt = admit_block<E, true, false>(tray, cnt, F, tb, buf[d], vbase, g.off0,
-                                                      g.vend, lk, kmx, lane);
                 } else {
-                    cnt = admit_block<E, false, false>(tray, cnt, F, tb, buf[d], vbase, g.off0,
-                                                       g.vend, lk, kmx, lane);
+                    // A score equal in value to the threshold's beats it only
+                    // below the threshold's position, so past that position
+                    // the bit test can be strict (rows with many equal
+                    // values then skip most blocks at the first test).
+                    const bool past = vbase - g.off0 >= 0xFFFFFFFFu - (uint32_t)F;
+                    const int32_t tbi = past && tb != INT32_MIN && tb != INT32_MAX ? tb + 1 : tb;
+                    if (lane_bounds) {
+                        cnt = admit_block<E, true, false>(tray, cnt, F, tbi, buf[d], vbase,
+                                                          g.off0, g.vend, lk, kmx, lane);
+                    } else {
+                        cnt = admit_block<E, false, false>(tray, cnt, F, tbi, buf[d], vbase,
+                                                           g.off0, g.vend, lk, kmx, lane);
+                    }
                 }
                 entered += cnt - before;
                 if constexpr (E <= 16) {
@@ -1047,7 +1075,8 @@ __device__ __forceinline__ void append_shared(uint64_t *dst, uint32_t *ctr, uint
 }
 
 __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo, uint64_t hi,
-                                               uint32_t k, EndShared *sh, uint32_t *hist3,
+                                               int pbits, uint32_t k, EndShared *sh,
+                                               uint32_t *hist3,
                                                uint64_t *gath, uint64_t *fin, uint32_t w,
                                                uint32_t NW, bool zeroer, uint32_t lane) {
     // The counters in *sh and hist3[0] are zero and the candidates final
@@ -1060,6 +1089,7 @@ __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo,
         uint32_t r = k;
         uint32_t bin_cnt = 0;
         for (uint32_t pass = 0;; ++pass) {
+            skip_fixed_bits(top, fmask, prefix, pbits);
             uint32_t *h = hist3 + 256u * (pass % 3u);
             uint32_t *hz = hist3 + 256u * ((pass + 1u) % 3u);
             const int low = top >= 7 ? top - 7 : 0;
@@ -1333,7 +1363,8 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
                                              &s_fill[0][0], lane);
         const uint64_t lo = lds_load_word(&s_T);
         const uint64_t hi = lds_load_word(&s_hi);
-        const uint32_t n = end_select(c, lo, hi, k, &s_end, hist, gath, fin, w, NW, w == NS, lane);
+        const uint32_t n = end_select(c, lo, hi, position_bits(g.L), k, &s_end, hist, gath, fin, w,
+                                      NW, w == NS, lane);
         if (w == NS && lane < 2u * NS) {
             __hip_atomic_store(&s_fill[lane >> 1][lane & 1u], 0u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1387,6 +1418,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     ss.T = 0ull;
     ss.sorts = 0u;
     ss.gnext = 0ull;
+    ss.pbits = position_bits(g.L);
     reset_sorter(ss, hist, lane);
     auto set_verdict = [&](uint32_t v) __attribute__((always_inline)) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
