@@ -552,6 +552,22 @@ __device__ __forceinline__ void raise_threshold(SorterState &ss, uint64_t nt, ui
     }
 }
 
+// Split rows: folds the row's threshold word read earlier (any stale value is
+// still a bound) into the sorter's and the workgroup's, and reads it again;
+// the read is in flight until the next fold.  The streams see the row's
+// word only through the workgroup's, which costs them no global access.
+__device__ __forceinline__ void fold_row_word(SorterState &ss, uint64_t *sT, uint64_t *gT,
+                                              uint32_t lane) {
+    const uint64_t gw = uniform64(ss.gnext);
+    if (gw > ss.T) {
+        ss.T = gw;
+        if (lane == 0) {
+            __hip_atomic_fetch_max(sT, gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+    ss.gnext = __hip_atomic_load(gT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Exact pruning: keeps exactly the k best pool words (if there are more) and
 // sets the threshold to the k-th best.  Pool words are loaded into registers
 // (64*E + kPiece*64 at most) and ranked by select_rth.
@@ -611,11 +627,7 @@ __device__ __forceinline__ void merge_tray(SorterState &ss, uint64_t *pool, cons
     for (uint32_t off = 0; off < c; off += kPieceWords) {
         ss.T = umax64(ss.T, lds_load_word(sT));
         if constexpr (SPLIT) {
-            // The row's word read at the previous piece (any stale value is
-            // still a bound); the next read is in flight while this piece is
-            // folded in.
-            ss.T = umax64(ss.T, uniform64(ss.gnext));
-            ss.gnext = __hip_atomic_load(gT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            fold_row_word(ss, sT, gT, lane);
         }
         const uint32_t piece = c - off < kPieceWords ? c - off : kPieceWords;
         if (ss.pc + piece > PoolCfg<E>::cap) {
@@ -823,7 +835,6 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
 
     float4 buf[D][kLoadsPerBlock];
     uint32_t bid[D];
-    uint64_t gbuf[D];
     // Block of step u; past the stream's end the last block is read again:
     // every slot issues exactly one set of loads per visit, so the wait
     // before each slot is the same static count every time.
@@ -835,11 +846,7 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
         }
         return (uint32_t)__builtin_amdgcn_readlane((int)vis, (int)(tt - c0));
     };
-    auto issue = [&](float4 (&dst)[kLoadsPerBlock], uint32_t b, uint64_t &g_out)
-        __attribute__((always_inline)) {
-        if constexpr (SPLIT) {
-            g_out = __hip_atomic_load(gT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    auto issue = [&](float4 (&dst)[kLoadsPerBlock], uint32_t b) __attribute__((always_inline)) {
         const uint32_t vbase = b * (uint32_t)kBlock;
         if (vbase >= g.off0 && vbase + (uint32_t)kBlock <= g.vend) {
             const float *bp = g.abase + vbase;
@@ -859,7 +866,7 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         bid[d] = block_of((uint32_t)d);
-        issue(buf[d], bid[d], gbuf[d]);
+        issue(buf[d], bid[d]);
     }
     // The first blocks are in flight while the sorter computes the estimate.
     if (tau_ready) {
@@ -876,7 +883,6 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
             const uint64_t shared_T = __hip_atomic_load(sT, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_WORKGROUP);
             if (t < mine) {
-                if constexpr (SPLIT) T = umax64(T, uniform64(gbuf[d]));
                 const uint64_t F = umax64(T, tau);
                 const int32_t tb = prefilter_bound(F);
                 const uint32_t vbase = bid[d] * (uint32_t)kBlock;
@@ -935,7 +941,7 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                 }
             }
             bid[d] = block_of(t + (uint32_t)D);
-            issue(buf[d], bid[d], gbuf[d]);
+            issue(buf[d], bid[d]);
             T = umax64(T, uniform64(shared_T));
             if (cnt >= Wm) {
                 publish_tray(&fill[w][cur], cnt, lane);
@@ -985,7 +991,10 @@ __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_
             }
         }
         if (done == NS) break;
-        if (!worked) __builtin_amdgcn_s_sleep(2);
+        if (!worked) {
+            if constexpr (SPLIT) fold_row_word(ss, sT, gT, lane);
+            __builtin_amdgcn_s_sleep(2);
+        }
     }
 }
 
