@@ -128,6 +128,22 @@ def test_heavy_ties():
         check(x, k, what=f"ties k={k}")
 
 
+@pytest.mark.parametrize("opts", [dict(split=8), dict(split=3), dict(split=1, flags=1),
+                                  dict(split=16, flags=2)],
+                         ids=lambda o: "-".join(f"{k}{v}" for k, v in o.items()))
+def test_ties_across_segments(opts):
+    # The k-th word sits inside a tie of thousands of equal values, so every
+    # selection must resolve it by position (the low half of the word), across
+    # segments and in the rerun path.
+    g = np.random.default_rng(23)
+    x = np.empty((3, 400_000), dtype=np.float32)
+    x[0] = np.float32(g.integers(0, 3, 400_000))
+    x[1] = np.float32(2.5)
+    x[2] = workloads.quantized_levels(g.standard_normal(400_000))
+    for k in (512, 2048):
+        check(x, k, what=f"ties across segments k={k}", **opts)
+
+
 def test_denormals_and_extremes():
     g = np.random.default_rng(10)
     b = g.integers(0, 1 << 23, size=(3, 20_000), dtype=np.uint32)
