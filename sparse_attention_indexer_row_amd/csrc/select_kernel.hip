@@ -16,22 +16,26 @@
 //     depend on the data, so future addresses are known), and appends
 //     survivors to a double-buffered tray in LDS.  When a tray passes the
 //     watermark the streamer publishes it and keeps streaming into the other
-//     buffer.  One sorter wave owns the kept set (the best k words seen so
-//     far, unsorted, in LDS).  For each published tray it finds the k-th
-//     best word of kept set + tray with a radix selection (LDS histogram
-//     passes over 8-bit digits, finished by a 64-word register sort), drops
-//     everything below it and raises the shared threshold to it.  The kept
-//     set is sorted once, at the end, with a register bitonic network.
-//     Streamers never stop for a sort, and the threshold is the k-th best of
-//     everything the workgroup has seen.
+//     buffer.  One sorter wave owns the candidate pool (in LDS).  It folds
+//     each published tray in, keeps a key histogram whose bound raises the
+//     shared threshold, and when the pool is full finds the k-th best word
+//     with a radix selection (LDS histogram passes over 8-bit digits,
+//     finished by a 64-word register sort), dropping everything below it.
+//     Streamers never stop for a sort.
+//   * When every stream is done, all waves together select the best k of the
+//     pool and the trays still published (the same radix selection, with a
+//     shared histogram per pass) and sort them with a bitonic network split
+//     across waves.
 //   * The per-score test is one compare against the threshold's value, done
 //     on the integer maximum of each lane's 16 score bit patterns of a block;
 //     only blocks in which some lane passes take the exact 64-bit word compare
-//     and the ballot/mbcnt compaction into the tray.
+//     and the ballot/mbcnt compaction into the tray.  A block that alone
+//     fills a kept list's worth of the tray bounds the threshold directly.
 //   * Split rows: the row's workgroups publish their threshold words with a
-//     64-bit atomic max in the workspace and streamers read it back with
-//     every block (any stale value is still a lower bound of the row's k-th
-//     word, so it is safe).  Each sorter writes its kept list to the
+//     64-bit atomic max in the workspace, and each sorter folds the row's word
+//     back into its workgroup's threshold (any stale value is still a lower
+//     bound of the row's k-th word, so it is safe; the streams themselves make
+//     no device-scope access).  Each sorter writes its kept list to the
 //     workspace and takes an atomic ticket; the last to arrive merges all
 //     lists, writes the row and resets the row's ticket and threshold words
 //     to zero (an accumulator that is never reset is the failure the
@@ -298,11 +302,12 @@ __device__ __forceinline__ void wait_tray_free(uint32_t *fill) {
 }
 
 // ---------------------------------------------------------------------------
-// Sorter wave: keeps the best k words seen by the workgroup, unsorted, in
-// LDS.  Each published tray is folded in by a selection -- the k-th best
-// word of (kept set + tray) becomes the new threshold and everything below
-// it is dropped -- so the per-score cost of the stream stays a few LDS
-// passes.  The kept words are sorted once, at the end.
+// Sorter wave: keeps the candidates the workgroup has admitted, unsorted, in
+// an LDS pool.  Each published tray is appended above the threshold; when
+// the pool is full a selection finds the k-th best word of it, which becomes
+// the new threshold, and everything below is dropped -- so the per-score
+// cost of the stream stays a few LDS passes.  The final k are selected and
+// sorted once, at the end of the pass, by all waves.
 
 template <int D>
 __device__ __forceinline__ uint64_t max_step(uint64_t v, uint32_t lane) {
