@@ -573,9 +573,42 @@ __device__ __forceinline__ void fold_row_word(SorterState &ss, uint64_t *sT, uin
     ss.gnext = __hip_atomic_load(gT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Rank of the k-th best pool word by the key histogram: the bucket b* the
+// histogram places it in is ranked exactly from the registers (words in
+// higher buckets counted, the bucket's words gathered and sorted when they
+// are at most 64).  Returns 0 when the bucket holds more than 64 words or the
+// histogram was off (it may miss a last tray's words), else the k-th word.
+template <int NA, int NB>
+__device__ __forceinline__ uint64_t rank_by_hist(const uint64_t (&a)[NA], const uint64_t (&b)[NB],
+                                                 uint32_t k, const SorterState &ss,
+                                                 const uint32_t *hist, uint64_t *gath,
+                                                 uint32_t lane) {
+    uint32_t bstar = 0;
+    if (hist_bound(hist, k, ss.base, ss.shift, bstar, lane) == 0ull) return 0ull;
+    uint32_t above = 0, g = 0;
+    auto visit = [&](uint64_t w) __attribute__((always_inline)) {
+        const uint32_t bk = bucket_of((uint32_t)(w >> 32), ss.base, ss.shift);
+        above += (uint32_t)__popcll(__ballot(w != 0ull && bk > bstar));
+        const bool take = w != 0ull && bk == bstar;
+        const uint64_t m = __ballot(take);
+        if (take && g + mbcnt64(m) < (uint32_t)kWave) gath[g + mbcnt64(m)] = w;
+        g += (uint32_t)__popcll(m);
+    };
+#pragma unroll
+    for (int e = 0; e < NA; ++e) visit(a[e]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) visit(b[j]);
+    if (g > (uint32_t)kWave || above >= k || k - above > g) return 0ull;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    uint64_t v[1] = {lane < g ? gath[lane] : 0ull};
+    wave_sort<1, false>(v, lane);
+    return list_word_at<1>(v, k - above - 1u);
+}
+
 // Exact pruning: keeps exactly the k best pool words (if there are more) and
 // sets the threshold to the k-th best.  Pool words are loaded into registers
-// (64*E + kPiece*64 at most) and ranked by select_rth.
+// (64*E + kPiece*64 at most) and ranked by select_rth, for the widest lists
+// first through the key histogram's bucket.
 template <int E, bool SPLIT>
 __device__ __forceinline__ void prune_pool(SorterState &ss, uint64_t *pool, uint64_t *sT,
                                         uint64_t *gT, uint32_t k, uint32_t *hist, uint64_t *gath,
@@ -607,7 +640,12 @@ __device__ __forceinline__ void prune_pool(SorterState &ss, uint64_t *pool, uint
     }
     uint64_t nt = 0ull;
     if (n > k) {
-        nt = select_rth(a, b, k, ss.T, wave_max64(lmx, lane), ss.pbits, hist, gath, lane);
+        // The widest lists prune often enough for the histogram's shortcut
+        // to pay; the narrow ones rarely prune and keep the smaller code.
+        if constexpr (E >= 16) nt = rank_by_hist(a, b, k, ss, hist, gath, lane);
+        if (nt == 0ull) {
+            nt = select_rth(a, b, k, ss.T, wave_max64(lmx, lane), ss.pbits, hist, gath, lane);
+        }
         ++ss.sorts;
     }
     const uint32_t w = write_ge(pool, 0, a, nt, lane);
