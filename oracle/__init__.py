@@ -48,6 +48,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
     ]
+    pool = lib.oracle_block_pool
+    pool.restype = ctypes.c_int
+    pool.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.POINTER(ctypes.c_int64),
+    ]
     return lib
 
 
@@ -94,4 +101,37 @@ def topk(scores: np.ndarray, k: int, lengths: np.ndarray | None = None,
         raise OracleNaN(f"NaN in row {bad.value}")
     if st != OK:
         raise RuntimeError(f"oracle_topk failed with status {st}")
+    return out_v, out_i
+
+
+def block_pool(scores: np.ndarray, group: int, keep: int, pinned: int,
+               lengths: np.ndarray | None = None, lib: ctypes.CDLL | None = None):
+    """Block-max pooled pre-selection of each row of ``scores[rows][n]``.
+
+    Blocks of ``group`` positions score their best value; the newest
+    ``pinned`` blocks are kept, then the best older blocks up to ``keep``.
+    Returns ``(block scores float32 [rows][keep], block indices int32
+    [rows][keep])``, pinned blocks first (newest first), filler (-inf, -1)
+    last.  Raises ``OracleNaN`` if a valid position holds NaN.
+    """
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    if scores.ndim != 2:
+        raise ValueError("scores must be 2-D [rows][n]")
+    rows, n = scores.shape
+    lens_arr = None
+    if lengths is not None:
+        lens_arr = np.ascontiguousarray(lengths, dtype=np.int32)
+        if lens_arr.shape != (rows,):
+            raise ValueError("lengths must have shape [rows]")
+    out_v = np.empty((rows, keep), dtype=np.float32)
+    out_i = np.empty((rows, keep), dtype=np.int32)
+    bad = ctypes.c_int64(-1)
+    lib = lib or _get()
+    st = lib.oracle_block_pool(
+        scores.ctypes.data, lens_arr.ctypes.data if lens_arr is not None else None,
+        rows, n, group, keep, pinned, out_v.ctypes.data, out_i.ctypes.data, ctypes.byref(bad))
+    if st == ENAN:
+        raise OracleNaN(f"NaN in row {bad.value}")
+    if st != OK:
+        raise RuntimeError(f"oracle_block_pool failed with status {st}")
     return out_v, out_i

@@ -194,3 +194,90 @@ int oracle_topk(const float *scores, const int32_t *lengths, int64_t rows, int64
     free(tids);
     return status;
 }
+
+/*
+ * Block-max pooled pre-selection ("The Secret GPU Kernel Behind DeepSeek V4.1
+ * Flash", transcript 7:22-7:46): while it holds a row's scores, the layer
+ * groups positions into blocks of eight, gives each block the best score
+ * inside it, keeps the best 2,000 blocks and always keeps the newest tokens,
+ * so that an old block cannot outvote recency.  Written out plainly:
+ *   - Row r holds positions [0, L) as above.  Block b covers positions
+ *     [b*group, (b+1)*group) cut at L; there are nb = ceil(L / group) blocks.
+ *     A block's score is its best valid score in the value order above.
+ *   - The newest P = min(pinned, nb) blocks (b = nb-1, nb-2, ...) are kept
+ *     whatever their scores.  Reading: the pages do not count the pinned
+ *     tokens; here the caller gives a block count.
+ *   - Of the older blocks [0, nb - P), the best min(keep - P, nb - P) by block
+ *     score are kept, in the value order above, ties to the lower block.
+ *   - Output row r has `keep` slots: the pinned blocks, newest first; then
+ *     the selected older blocks in that order; then filler (value -inf,
+ *     index -1).  Values are bit copies of the block scores.
+ * Requires 1 <= group, 0 <= pinned <= keep, keep >= 1.
+ */
+static int pool_row(const float *row, int64_t L, int64_t group, int64_t keep, int64_t pinned,
+                    float *out_v, int32_t *out_i, pair_t *work) {
+    const int64_t nb = (L + group - 1) / group;
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t lo = b * group;
+        const int64_t hi = lo + group < L ? lo + group : L;
+        float best = row[lo];
+        if (isnan(best)) return ORACLE_ENAN;
+        for (int64_t j = lo + 1; j < hi; ++j) {
+            if (isnan(row[j])) return ORACLE_ENAN;
+            if (value_greater(row[j], best)) best = row[j];
+        }
+        work[b].v = best;
+        work[b].i = (int32_t)b;
+    }
+    const int64_t P = pinned < nb ? pinned : nb;
+    int64_t s = 0;
+    for (; s < P; ++s) {
+        out_v[s] = work[nb - 1 - s].v;
+        out_i[s] = work[nb - 1 - s].i;
+    }
+    const int64_t older = nb - P;
+    qsort(work, (size_t)older, sizeof(pair_t), pair_cmp);
+    const int64_t take = keep - P < older ? keep - P : older;
+    for (int64_t j = 0; j < take; ++j, ++s) {
+        out_v[s] = work[j].v;
+        out_i[s] = work[j].i;
+    }
+    for (; s < keep; ++s) {
+        out_v[s] = -INFINITY;
+        out_i[s] = -1;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * scores, lengths, nthreads, bad_row: as for oracle_topk.
+ * out_vals: host array [rows][keep];  out_idx: host array [rows][keep]
+ * Returns ORACLE_OK, ORACLE_EINVAL, ORACLE_ENAN or ORACLE_ENOMEM.  Rows are
+ * done one after another (the pooled rows are short).
+ */
+int oracle_block_pool(const float *scores, const int32_t *lengths, int64_t rows, int64_t n,
+                      int64_t group, int64_t keep, int64_t pinned, float *out_vals,
+                      int32_t *out_idx, int64_t *bad_row) {
+    if (bad_row) *bad_row = -1;
+    if (rows < 0 || n < 0 || n > INT32_MAX || group < 1 || keep < 1 || pinned < 0 ||
+        pinned > keep) {
+        return ORACLE_EINVAL;
+    }
+    if (rows == 0) return ORACLE_OK;
+    if (!scores || !out_vals || !out_idx) return ORACLE_EINVAL;
+    const int64_t nbmax = (n + group - 1) / group;
+    pair_t *work = (pair_t *)malloc(sizeof(pair_t) * (size_t)(nbmax > 0 ? nbmax : 1));
+    if (!work) return ORACLE_ENOMEM;
+    int status = ORACLE_OK;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t L = row_length(lengths, r, n);
+        status = pool_row(scores + r * n, L, group, keep, pinned, out_vals + r * keep,
+                          out_idx + r * keep, work);
+        if (status != ORACLE_OK) {
+            if (bad_row) *bad_row = r;
+            break;
+        }
+    }
+    free(work);
+    return status;
+}

@@ -14,6 +14,7 @@ sys.path.insert(0, HERE)
 
 import oracle  # noqa: E402
 import oracle_pins  # noqa: E402
+import oracle_pool_pins  # noqa: E402
 
 
 def main(path):
@@ -22,9 +23,13 @@ def main(path):
     def topk(scores, k, lengths):
         return oracle.topk(scores, k, lengths, threads=2, lib=lib)
 
-    for pin in oracle_pins.ALL_PINS:
+    def pool(scores, group, keep, pinned, lengths):
+        return oracle.block_pool(scores, group, keep, pinned, lengths, lib=lib)
+
+    for pin, fn in [(p, topk) for p in oracle_pins.ALL_PINS] + \
+                   [(p, pool) for p in oracle_pool_pins.POOL_PINS]:
         try:
-            pin(topk)
+            pin(fn)
         except (AssertionError, oracle.OracleNaN, RuntimeError) as e:
             print(f"FAILED {pin.__name__}: {str(e)[:200]}")
             return 1

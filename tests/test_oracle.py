@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 import oracle_pins
+import oracle_pool_pins
 from sparse_attention_indexer_row_amd import workloads
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -25,6 +26,25 @@ def _topk(scores, k, lengths):
 @pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
 def test_pin(pin):
     pin(_topk)
+
+
+def _pool(scores, group, keep, pinned, lengths):
+    return oracle.block_pool(scores, group, keep, pinned, lengths)
+
+
+@pytest.mark.parametrize("pin", oracle_pool_pins.POOL_PINS, ids=lambda p: p.__name__)
+def test_pool_pin(pin):
+    pin(_pool)
+
+
+def test_pool_bad_arguments():
+    x = np.zeros((1, 8), dtype=np.float32)
+    for group, keep, pinned in [(0, 4, 0), (2, 0, 0), (2, 4, 5), (2, 4, -1)]:
+        with pytest.raises(RuntimeError):
+            oracle.block_pool(x, group, keep, pinned)
+    x[0, 3] = np.nan
+    with pytest.raises(oracle.OracleNaN):
+        oracle.block_pool(x, 2, 4, 1)
 
 
 def _check_invariants(scores, lengths, k, vals, idx):
@@ -129,6 +149,15 @@ MUTANTS = {
     "off_by_one_count": ("int64_t m = L < k ? L : k;", "int64_t m = L < k ? L : k - 1;"),
     "wrong_index_recorded": ("work[j].i = (int32_t)j;", "work[j].i = (int32_t)(L - 1 - j);"),
     "lengths_ignored": ("if (!lengths) return n;", "if (lengths || !lengths) return n;"),
+    "pool_pins_oldest": ("        out_v[s] = work[nb - 1 - s].v;\n        out_i[s] = work[nb - 1 - s].i;",
+                         "        out_v[s] = work[s].v;\n        out_i[s] = work[s].i;"),
+    "pool_block_one_short": ("const int64_t hi = lo + group < L ? lo + group : L;",
+                             "const int64_t hi = lo + group - 1 < L ? lo + group - 1 : L;"),
+    "pool_first_not_best": ("if (value_greater(row[j], best)) best = row[j];", ""),
+    "pool_pinned_reselected": ("qsort(work, (size_t)older, sizeof(pair_t), pair_cmp);",
+                               "qsort(work, (size_t)nb, sizeof(pair_t), pair_cmp);"),
+    "pool_keeps_one_less": ("const int64_t take = keep - P < older ? keep - P : older;",
+                            "const int64_t take = keep - P - 1 < older ? keep - P - 1 : older;"),
 }
 
 
