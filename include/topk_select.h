@@ -155,6 +155,41 @@ typedef struct {
 
 int topk_plan(int32_t rows, int32_t n, int32_t k, const topk_options *opts, topk_plan_t *out);
 
+/*
+ * topk_block_pool -- block-max pooled pre-selection ("The Secret GPU Kernel
+ * Behind DeepSeek V4.1 Flash", transcript 7:22-7:46): while a layer holds a
+ * row's scores it also keeps a pool of position blocks for the layers above,
+ * chosen by each block's best score, with the newest blocks always in.
+ *
+ *   Row r holds positions [0, L_r) as for topk_select.  Block b covers
+ *   positions [b*group, (b+1)*group) cut at L_r; the row has
+ *   nb_r = ceil(L_r / group) blocks.  A block's score is its largest valid
+ *   score in IEEE-754 total order (-0.0 below +0.0).
+ *   Output row r has `keep` slots:
+ *     - slots [0, P_r), P_r = min(pinned, nb_r): the newest blocks
+ *       nb_r-1, nb_r-2, ... whatever their scores;
+ *     - then the best min(keep - P_r, nb_r - P_r) older blocks (blocks
+ *       [0, nb_r - P_r)), by block score descending, equal scores to the
+ *       lower block;
+ *     - the remaining slots: value -inf, index -1.
+ *   out_vals holds bit copies of the block scores, out_idx the block
+ *   indices (multiply by `group` for the first position of a block).
+ *   The pages do not say how many tokens are pinned; here the caller gives a
+ *   block count.
+ *
+ * group >= 1, keep >= 1, 0 <= pinned <= keep, keep - pinned <= TOPK_MAX_K
+ * (TOPK_EINVAL / TOPK_EK_RANGE otherwise).  out_vals: fp32 [rows][keep],
+ * out_idx: int32 [rows][keep], device pointers owned by the caller.
+ * Work: one pass over the scores writing ceil(n / group) block maxima per row
+ * into a library-owned, grow-only device buffer, then the top-k selection of
+ * topk_select over those maxima.  Like topk_select, the first call that needs
+ * a larger library buffer allocates it (not graph-capturable), and calls
+ * that share the library's buffers must be ordered on one stream.
+ */
+int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
+                    int32_t group, int32_t keep, int32_t pinned, float *out_vals,
+                    int32_t *out_idx, void *stream);
+
 /* Human-readable text for a status code (static storage). */
 const char *topk_strerror(int status);
 

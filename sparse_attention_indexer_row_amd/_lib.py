@@ -34,6 +34,7 @@ EXPORTS = (
     "topk_select_split",
     "topk_select_ex",
     "topk_plan",
+    "topk_block_pool",
     "topk_strerror",
     "topk_visit_order",
     "topk_probe_sink_words",
@@ -78,6 +79,7 @@ SIGNATURES = {
                                       ctypes.POINTER(TopkOptions), _vp, _sz, _vp]),
     "topk_plan": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(TopkOptions),
                                  ctypes.POINTER(TopkPlan)]),
+    "topk_block_pool": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "topk_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "topk_visit_order": (ctypes.c_int, [_u64, _i32, _i32, _vp]),
     "topk_probe_sink_words": (_sz, [_sz]),

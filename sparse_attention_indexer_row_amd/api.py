@@ -150,6 +150,20 @@ def topk_plan(rows: int, n: int, k: int, *, split: int = 0, waves: int = 0,
     return {f: getattr(p, f) for f, _ in TopkPlan._fields_ if f != "reserved"}
 
 
+def topk_block_pool(scores: torch.Tensor, group: int, keep: int, pinned: int,
+                    lengths: torch.Tensor | None = None, out=None, stream=None):
+    """Block-max pooled pre-selection: (block scores, int32 block indices) [rows][keep]."""
+    _check_scores(scores)
+    lp = _check_lengths(lengths, scores)
+    vals, idx = _outputs(scores, keep, out)
+    rows, n = scores.shape
+    st = _lib.load().topk_block_pool(scores.data_ptr(), lp, rows, n, group, keep, pinned,
+                                     vals.data_ptr(), idx.data_ptr(),
+                                     _stream_handle(stream, scores.device))
+    _lib.check(st, "topk_block_pool")
+    return vals, idx
+
+
 def topk_strerror(status: int) -> str:
     return _lib.load().topk_strerror(status).decode()
 

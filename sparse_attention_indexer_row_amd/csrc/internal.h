@@ -20,8 +20,9 @@ struct SelectArgs {
     int32_t split;             // workgroups per row
     int32_t watermark;         // tray words that trigger a sort
     int32_t tray_words;        // tray capacity per wave
-    float *out_vals;           // [rows][k]
-    int32_t *out_idx;          // [rows][k]
+    float *out_vals;           // [rows][out_ld], first k slots of each row written
+    int32_t *out_idx;          // [rows][out_ld]
+    int64_t out_ld;            // output row stride in elements (>= k)
     uint64_t *ws_ctrl;         // [rows][2]: threshold word, arrival ticket (split > 1)
     uint32_t *ws_groups;       // [rows][groups] arrival tickets of segment groups (split > 1)
     uint64_t *ws_lists;        // [rows][split][list_words] (split > 1)
@@ -33,6 +34,26 @@ struct SelectArgs {
 // Launches the selection kernel for list capacity 64*E (E in 1..32).
 hipError_t launch_select(const SelectArgs &a, int E, int waves, size_t lds_bytes,
                          hipStream_t stream);
+
+// Block-max pooled pre-selection, first step: block maxima and pinned slots.
+struct PoolArgs {
+    const float *scores;       // [rows][n]
+    const int32_t *lengths;    // [rows] or null
+    int64_t n;
+    int64_t bm_ld;             // row stride of bm (>= ceil(n / group))
+    int32_t rows;              // rows handled by this launch
+    int32_t row0;
+    int32_t group;             // positions per block
+    int32_t pinned;            // newest blocks kept whatever their scores
+    int32_t keep;              // output slots per row
+    int32_t span;              // work items per row: max(ceil(n / group), pinned)
+    float *bm;                 // [rows][bm_ld] block maxima (blocks < nb_r written)
+    int32_t *older;            // [rows] nb_r - min(pinned, nb_r)
+    float *out_vals;           // [rows][keep]: slots [0, pinned) written
+    int32_t *out_idx;
+};
+
+hipError_t launch_block_max(const PoolArgs &a, hipStream_t stream);
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);

@@ -1587,8 +1587,8 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     if (p.stats && lane == 0 && ss.sorts > 0) {
         atomicAdd(p.stats + 2 * (size_t)r + 1, (unsigned long long)ss.sorts);
     }
-    write_row<E>(p.out_vals + (size_t)r * k, p.out_idx + (size_t)r * k, k, kept_sorted, trays,
-                 lane);
+    write_row<E>(p.out_vals + (size_t)r * (size_t)p.out_ld, p.out_idx + (size_t)r * (size_t)p.out_ld,
+                 k, kept_sorted, trays, lane);
     if constexpr (SPLIT) {
         // Leave this row's part of the workspace all zero (the lists were
         // cleared behind the merge), so the next call may use the same

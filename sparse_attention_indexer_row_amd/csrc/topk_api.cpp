@@ -162,8 +162,9 @@ Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cu
 
 int run(const float *scores, const int32_t *lengths, int32_t rows, int32_t n, int32_t k,
         float *out_vals, int32_t *out_idx, const Plan &pl, void *ws, uint64_t seed,
-        uint32_t flags, unsigned long long *stats, hipStream_t stream) {
+        uint32_t flags, unsigned long long *stats, hipStream_t stream, int64_t out_ld = 0) {
     topk::SelectArgs a{};
+    a.out_ld = out_ld > 0 ? out_ld : k;
     a.scores = scores;
     a.lengths = lengths;
     a.n = n;
@@ -194,35 +195,55 @@ int run(const float *scores, const int32_t *lengths, int32_t rows, int32_t n, in
     return TOPK_OK;
 }
 
-// Library-owned workspace for topk_select: one grow-only buffer per device.
-std::mutex g_ws_mutex;
-void *g_ws[kMaxDevices] = {nullptr};
-size_t g_ws_bytes[kMaxDevices] = {0};
+// Library-owned device buffers: one grow-only buffer per device and purpose.
+struct DeviceBuffers {
+    std::mutex mutex;
+    void *ptr[kMaxDevices] = {nullptr};
+    size_t bytes[kMaxDevices] = {0};
+};
 
-int internal_workspace(size_t need, hipStream_t stream, void **out) {
+// Returns a buffer of at least `need` bytes on the current device, growing
+// it (after a device-wide synchronisation, since earlier calls may still use
+// the old one) when it is too small.  With `zero`, a new buffer is cleared
+// on `stream` before first use.
+int grow_buffer(DeviceBuffers &b, size_t need, bool zero, hipStream_t stream, void **out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TOPK_EDEVICE;
-    std::lock_guard<std::mutex> g(g_ws_mutex);
-    if (g_ws_bytes[dev] < need) {
-        if (g_ws[dev]) {
+    std::lock_guard<std::mutex> g(b.mutex);
+    if (b.bytes[dev] < need) {
+        if (b.ptr[dev]) {
             if (hipDeviceSynchronize() != hipSuccess) return TOPK_EDEVICE;
-            (void)hipFree(g_ws[dev]);
-            g_ws[dev] = nullptr;
-            g_ws_bytes[dev] = 0;
+            (void)hipFree(b.ptr[dev]);
+            b.ptr[dev] = nullptr;
+            b.bytes[dev] = 0;
         }
         size_t bytes = align_up(need, (size_t)1 << 20);
         void *p = nullptr;
         if (hipMalloc(&p, bytes) != hipSuccess) return TOPK_EALLOC;
-        if (topk::launch_fill_zero(p, bytes, stream) != hipSuccess) {
+        if (zero && topk::launch_fill_zero(p, bytes, stream) != hipSuccess) {
             (void)hipFree(p);
             return TOPK_ELAUNCH;
         }
-        g_ws[dev] = p;
-        g_ws_bytes[dev] = bytes;
+        b.ptr[dev] = p;
+        b.bytes[dev] = bytes;
     }
-    *out = g_ws[dev];
+    *out = b.ptr[dev];
     return TOPK_OK;
 }
+
+// Split-row workspace of topk_select (left zeroed by every call).
+DeviceBuffers g_ws;
+int internal_workspace(size_t need, hipStream_t stream, void **out) {
+    return grow_buffer(g_ws, need, true, stream, out);
+}
+
+// Block maxima and older-block counts of topk_block_pool.
+DeviceBuffers g_pool;
+
+// Block-maxima rows hold ceil(n / group) floats padded to whole 256-byte
+// lines, so every row starts aligned.
+constexpr int64_t kPoolRowAlign = 64;
+constexpr int32_t kMaxGridRows = 65535;
 
 }  // namespace
 
@@ -322,6 +343,66 @@ int topk_select(const float *scores, const int32_t *lengths, int32_t rows, int32
     }
     return run(scores, lengths, rows, n, k, out_vals, out_idx, pl, ws, 0, 0u, nullptr,
                (hipStream_t)stream);
+}
+
+int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
+                    int32_t group, int32_t keep, int32_t pinned, float *out_vals,
+                    int32_t *out_idx, void *stream) {
+    if (rows < 0 || n < 1 || group < 1 || keep < 1 || pinned < 0 || pinned > keep)
+        return TOPK_EINVAL;
+    const int32_t older_k = keep - pinned;
+    if (older_k > TOPK_MAX_K) return TOPK_EK_RANGE;
+    if (rows == 0) return TOPK_OK;
+    if (!scores || !out_vals || !out_idx) return TOPK_EINVAL;
+    if (misaligned(scores, 4) || misaligned(out_vals, 4) || misaligned(out_idx, 4) ||
+        (lengths && misaligned(lengths, 4)))
+        return TOPK_EINVAL;
+    const int64_t nbk = ((int64_t)n + group - 1) / group;
+    const int64_t bm_ld = (nbk + kPoolRowAlign - 1) / kPoolRowAlign * kPoolRowAlign;
+    if (bm_ld > INT32_MAX) return TOPK_EINVAL;
+    if (older_k > 0) {
+        int st = check_plan(make_plan(rows, (int32_t)bm_ld, older_k, nullptr, kAssumedCUs));
+        if (st != TOPK_OK) return st;
+    }
+    int cus = 0;
+    int st = device_cus(&cus);
+    if (st != TOPK_OK) return st;
+    const size_t bm_bytes = align_up((size_t)rows * (size_t)bm_ld * 4, kAlign);
+    void *scratch = nullptr;
+    st = grow_buffer(g_pool, bm_bytes + (size_t)rows * 4, false, (hipStream_t)stream, &scratch);
+    if (st != TOPK_OK) return st;
+    float *bm = static_cast<float *>(scratch);
+    int32_t *older = reinterpret_cast<int32_t *>(static_cast<char *>(scratch) + bm_bytes);
+
+    topk::PoolArgs a{};
+    a.scores = scores;
+    a.lengths = lengths;
+    a.n = n;
+    a.bm_ld = bm_ld;
+    a.group = group;
+    a.pinned = pinned;
+    a.keep = keep;
+    a.span = (int32_t)std::max<int64_t>(nbk, pinned);
+    a.bm = bm;
+    a.older = older;
+    a.out_vals = out_vals;
+    a.out_idx = out_idx;
+    for (int32_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
+        a.row0 = r0;
+        a.rows = std::min(kMaxGridRows, rows - r0);
+        if (topk::launch_block_max(a, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
+    }
+    if (older_k == 0) return TOPK_OK;
+    // The best older blocks: a top-k of the block-maxima rows cut at each
+    // row's older-block count, written behind the pinned slots.
+    Plan pl = make_plan(rows, (int32_t)bm_ld, older_k, nullptr, cus);
+    void *ws = nullptr;
+    if (pl.split > 1) {
+        st = internal_workspace(pl.ws_bytes, (hipStream_t)stream, &ws);
+        if (st != TOPK_OK) return st;
+    }
+    return run(bm, older, rows, (int32_t)bm_ld, older_k, out_vals + pinned, out_idx + pinned, pl,
+               ws, 0, 0u, nullptr, (hipStream_t)stream, keep);
 }
 
 const char *topk_strerror(int status) {

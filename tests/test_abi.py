@@ -88,6 +88,25 @@ def test_split_and_ex_argument_errors(lib):
     assert lib.topk_select_ex(*a, ctypes.byref(o), None, 0, None) == _lib.TOPK_EINVAL
 
 
+@pytest.mark.parametrize("args,status", [
+    # scores, lengths, rows, n, group, keep, pinned, out_vals, out_idx, stream
+    ((FAKE, None, -1, 64, 8, 16, 2, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # rows < 0
+    ((FAKE, None, 1, 0, 8, 16, 2, FAKE, FAKE, None), _lib.TOPK_EINVAL),        # n < 1
+    ((FAKE, None, 1, 64, 0, 16, 2, FAKE, FAKE, None), _lib.TOPK_EINVAL),       # group < 1
+    ((FAKE, None, 1, 64, 8, 0, 0, FAKE, FAKE, None), _lib.TOPK_EINVAL),        # keep < 1
+    ((FAKE, None, 1, 64, 8, 16, -1, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # pinned < 0
+    ((FAKE, None, 1, 64, 8, 16, 17, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # pinned > keep
+    ((FAKE, None, 1, 64, 8, 2100, 51, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),  # keep - pinned > max
+    ((None, None, 1, 64, 8, 16, 2, FAKE, FAKE, None), _lib.TOPK_EINVAL),       # null scores
+    ((FAKE, None, 1, 64, 8, 16, 2, None, FAKE, None), _lib.TOPK_EINVAL),       # null out_vals
+    ((FAKE, None, 1, 64, 8, 16, 2, FAKE, None, None), _lib.TOPK_EINVAL),       # null out_idx
+    ((FAKE, FAKE + 2, 1, 64, 8, 16, 2, FAKE, FAKE, None), _lib.TOPK_EINVAL),   # misaligned lengths
+    ((FAKE, None, 0, 64, 8, 16, 2, None, None, None), _lib.TOPK_OK),           # no rows
+])
+def test_block_pool_argument_errors(lib, args, status):
+    assert lib.topk_block_pool(*args) == status
+
+
 def test_workspace_init_and_probe_argument_errors(lib):
     assert lib.topk_workspace_init(None, 256, None) == _lib.TOPK_EWORKSPACE
     assert lib.topk_workspace_init(FAKE + 16, 256, None) == _lib.TOPK_EWORKSPACE
