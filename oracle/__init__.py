@@ -55,6 +55,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.POINTER(ctypes.c_int64),
     ]
+    pooled = lib.oracle_pooled_topk
+    pooled.restype = ctypes.c_int
+    pooled.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.POINTER(ctypes.c_int64),
+    ]
     return lib
 
 
@@ -134,4 +141,42 @@ def block_pool(scores: np.ndarray, group: int, keep: int, pinned: int,
         raise OracleNaN(f"NaN in row {bad.value}")
     if st != OK:
         raise RuntimeError(f"oracle_block_pool failed with status {st}")
+    return out_v, out_i
+
+
+def pooled_topk(pool_scores: np.ndarray, pool_idx: np.ndarray, group: int, k: int, n: int,
+                lengths: np.ndarray | None = None, lib: ctypes.CDLL | None = None):
+    """Top-k inside a block pool.
+
+    ``pool_idx[rows][keep]`` names the pooled blocks (negative: empty slot);
+    ``pool_scores[rows][keep * group]`` holds the score of position
+    ``pool_idx[r][s] * group + j`` at ``[r][s * group + j]``.  Positions at or
+    beyond the row length (``lengths``, else ``n``) are not candidates.
+    Returns ``(values float32 [rows][k], context positions int32 [rows][k])``,
+    equal values to the lower position, filler (-inf, -1) last.
+    """
+    pool_idx = np.ascontiguousarray(pool_idx, dtype=np.int32)
+    if pool_idx.ndim != 2:
+        raise ValueError("pool_idx must be 2-D [rows][keep]")
+    rows, keep = pool_idx.shape
+    pool_scores = np.ascontiguousarray(pool_scores, dtype=np.float32)
+    if pool_scores.shape != (rows, keep * group):
+        raise ValueError("pool_scores must have shape [rows][keep * group]")
+    lens_arr = None
+    if lengths is not None:
+        lens_arr = np.ascontiguousarray(lengths, dtype=np.int32)
+        if lens_arr.shape != (rows,):
+            raise ValueError("lengths must have shape [rows]")
+    out_v = np.empty((rows, k), dtype=np.float32)
+    out_i = np.empty((rows, k), dtype=np.int32)
+    bad = ctypes.c_int64(-1)
+    lib = lib or _get()
+    st = lib.oracle_pooled_topk(
+        pool_scores.ctypes.data, pool_idx.ctypes.data,
+        lens_arr.ctypes.data if lens_arr is not None else None, rows, n, group, keep, k,
+        out_v.ctypes.data, out_i.ctypes.data, ctypes.byref(bad))
+    if st == ENAN:
+        raise OracleNaN(f"NaN in row {bad.value}")
+    if st != OK:
+        raise RuntimeError(f"oracle_pooled_topk failed with status {st}")
     return out_v, out_i

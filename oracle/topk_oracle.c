@@ -281,3 +281,67 @@ int oracle_block_pool(const float *scores, const int32_t *lengths, int64_t rows,
     free(work);
     return status;
 }
+
+/*
+ * Selection inside a block pool ("The Secret GPU Kernel Behind DeepSeek V4.1
+ * Flash", transcript 7:46-8:00): the indexers above the pooling layer score
+ * only the positions of the pooled blocks and keep their own top-k there.
+ * Written out plainly:
+ *   - Row r of the context holds positions [0, L) with L as above (n is the
+ *     context length).  Pool slot s of row r names block b = pool_idx[r][s];
+ *     b < 0 marks an empty slot.  Its positions are b*group + j, j < group.
+ *   - pool_scores[r][s*group + j] is the score of position b*group + j.
+ *   - The candidates are the positions of non-empty slots below L.  The
+ *     output is their top-k in the value order above, equal values to the
+ *     lower POSITION (not the lower slot), then filler (-inf, -1); indices
+ *     are context positions.
+ * Precondition: a row's block indices are distinct (a pool never repeats a
+ * block).  Requires group >= 1, keep >= 1, k >= 1.
+ */
+int oracle_pooled_topk(const float *pool_scores, const int32_t *pool_idx,
+                       const int32_t *lengths, int64_t rows, int64_t n, int64_t group,
+                       int64_t keep, int64_t k, float *out_vals, int32_t *out_idx,
+                       int64_t *bad_row) {
+    if (bad_row) *bad_row = -1;
+    if (rows < 0 || n < 0 || n > INT32_MAX || group < 1 || keep < 1 || k < 1 ||
+        keep * group > INT32_MAX) {
+        return ORACLE_EINVAL;
+    }
+    if (rows == 0) return ORACLE_OK;
+    if (!pool_scores || !pool_idx || !out_vals || !out_idx) return ORACLE_EINVAL;
+    pair_t *work = (pair_t *)malloc(sizeof(pair_t) * (size_t)(keep * group));
+    if (!work) return ORACLE_ENOMEM;
+    int status = ORACLE_OK;
+    for (int64_t r = 0; r < rows && status == ORACLE_OK; ++r) {
+        const int64_t L = row_length(lengths, r, n);
+        const float *sc = pool_scores + r * keep * group;
+        const int32_t *pi = pool_idx + r * keep;
+        int64_t m = 0;
+        for (int64_t s = 0; s < keep; ++s) {
+            if (pi[s] < 0) continue;
+            for (int64_t j = 0; j < group; ++j) {
+                const int64_t pos = (int64_t)pi[s] * group + j;
+                if (pos >= L) break;
+                const float v = sc[s * group + j];
+                if (isnan(v)) {
+                    status = ORACLE_ENAN;
+                    if (bad_row) *bad_row = r;
+                    break;
+                }
+                work[m].v = v;
+                work[m].i = (int32_t)pos;
+                ++m;
+            }
+        }
+        if (status != ORACLE_OK) break;
+        qsort(work, (size_t)m, sizeof(pair_t), pair_cmp);
+        float *ov = out_vals + r * k;
+        int32_t *oi = out_idx + r * k;
+        for (int64_t t = 0; t < k; ++t) {
+            ov[t] = t < m ? work[t].v : -INFINITY;
+            oi[t] = t < m ? work[t].i : -1;
+        }
+    }
+    free(work);
+    return status;
+}

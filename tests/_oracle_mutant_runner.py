@@ -26,8 +26,12 @@ def main(path):
     def pool(scores, group, keep, pinned, lengths):
         return oracle.block_pool(scores, group, keep, pinned, lengths, lib=lib)
 
+    def pooled(pool_scores, pool_idx, group, k, n, lengths):
+        return oracle.pooled_topk(pool_scores, pool_idx, group, k, n, lengths, lib=lib)
+
     for pin, fn in [(p, topk) for p in oracle_pins.ALL_PINS] + \
-                   [(p, pool) for p in oracle_pool_pins.POOL_PINS]:
+                   [(p, pool) for p in oracle_pool_pins.POOL_PINS] + \
+                   [(p, pooled) for p in oracle_pool_pins.POOLED_PINS]:
         try:
             pin(fn)
         except (AssertionError, oracle.OracleNaN, RuntimeError) as e:

@@ -47,6 +47,29 @@ def test_pool_bad_arguments():
         oracle.block_pool(x, 2, 4, 1)
 
 
+def _pooled(pool_scores, pool_idx, group, k, n, lengths):
+    return oracle.pooled_topk(pool_scores, pool_idx, group, k, n, lengths)
+
+
+@pytest.mark.parametrize("pin", oracle_pool_pins.POOLED_PINS, ids=lambda p: p.__name__)
+def test_pooled_pin(pin):
+    pin(_pooled)
+
+
+def test_pooled_bad_arguments():
+    ps = np.zeros((1, 8), dtype=np.float32)
+    pi = np.zeros((1, 4), dtype=np.int32)
+    with pytest.raises(RuntimeError):
+        oracle.pooled_topk(ps, pi, 2, 0, 8)           # k < 1
+    with pytest.raises(ValueError):
+        oracle.pooled_topk(ps, pi, 3, 4, 8)           # scores not [rows][keep * group]
+    ps[0, 5] = np.nan
+    with pytest.raises(oracle.OracleNaN):
+        oracle.pooled_topk(ps, pi, 2, 4, 8)
+    pi[0, 2] = -1                                     # the NaN sits in an empty slot
+    oracle.pooled_topk(ps, pi, 2, 4, 8)
+
+
 def _check_invariants(scores, lengths, k, vals, idx):
     """Properties every correct top-k output has, checked without re-sorting."""
     rows, n = scores.shape
@@ -158,6 +181,15 @@ MUTANTS = {
                                "qsort(work, (size_t)nb, sizeof(pair_t), pair_cmp);"),
     "pool_keeps_one_less": ("const int64_t take = keep - P < older ? keep - P : older;",
                             "const int64_t take = keep - P - 1 < older ? keep - P - 1 : older;"),
+    "pooled_ignores_length": ("                if (pos >= L) break;", ""),
+    "pooled_keeps_empty_slots": ("            if (pi[s] < 0) continue;",
+                                 "            if (pi[s] < -1) continue;"),
+    "pooled_slot_as_index": ("                work[m].i = (int32_t)pos;",
+                             "                work[m].i = (int32_t)(s * group + j);"),
+    "pooled_wrong_score": ("                const float v = sc[s * group + j];",
+                           "                const float v = sc[s * group + (group - 1 - j)];"),
+    "pooled_group_stride": ("const int64_t pos = (int64_t)pi[s] * group + j;",
+                            "const int64_t pos = (int64_t)pi[s] * (group + 1) + j;"),
 }
 
 
