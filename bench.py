@@ -30,24 +30,55 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
+# Sources each bench path's kernels are built from; a traffic summary is
+# stale once any of them changes.
+SELECT_SOURCES = ["select_kernel.hip", "common.h", "wave_sort.h", "internal.h"]
+KERNEL_SOURCES = {
+    "pool": SELECT_SOURCES + ["pool_kernel.hip"],
+    "pooled": SELECT_SOURCES + ["pool_kernel.hip"],
+}
+
+
+def kernel_source_hash(workload: str = "adverse") -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "sparse_attention_indexer_row_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for name in sorted(KERNEL_SOURCES.get(workload, SELECT_SOURCES)):
+        with open(os.path.join(ROOT, "sparse_attention_indexer_row_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()
 
 
+def profile_target(workload: str):
+    """(summary file stem, kernels one call launches, algorithmic read bytes,
+    algorithmic write bytes) of a bench workload; host only, no GPU."""
+    from sparse_attention_indexer_row_amd import workloads
+    if workload == "pooled":
+        w = workloads.pooled()
+        return (traffic_stem(workload),
+                ["pool_order_kernel", "select_kernel", "pool_positions_kernel"],
+                4 * w.pool_scores.size + 4 * w.pool_idx.size, 8 * w.rows * w.k)
+    if workload == "pool":
+        w = workloads.make("adverse")
+        return (traffic_stem(workload), ["block_max_kernel", "select_kernel"],
+                4 * w.valid_elements(), 8 * w.rows * POOL_KEEP)
+    w = workloads.make(workload)
+    return (traffic_stem(workload), ["select_kernel"], 4 * w.valid_elements(), 8 * w.rows * w.k)
+
+
+def traffic_stem(workload: str) -> str:
+    return {"pooled": "topk_pooled_select_pooled",
+            "pool": "topk_block_pool_adverse"}.get(workload, f"topk_select_{workload}")
+
+
 def load_traffic(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    """HBM bytes per call from committed rocprofv3 counter runs, or None
     when the kernel sources changed since the counters were taken."""
-    path = os.path.join(TRAFFIC_DIR, f"topk_select_{workload}_traffic.json")
+    path = os.path.join(TRAFFIC_DIR, f"{traffic_stem(workload)}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != kernel_source_hash():
+    if t.get("kernel_source_sha256") != kernel_source_hash(workload):
         return None
     return t
 
@@ -71,45 +102,43 @@ def _csv_rows(path):
 
 def summarize_profiles(workload: str, trace_dir: str, fetch_dir: str, write_dir: str) -> int:
     """Turns the three rocprofv3 runs of PROFILE_COMMANDS into the committed
-    summaries: profiles/topk_select_<workload>_rocprof.md (kernel statistics)
-    and profiles/topk_select_<workload>_traffic.json (HBM bytes per launch,
-    scaled by the counters' reading for the 1 GiB probe copy)."""
+    summaries: profiles/<entry point>_<workload>_rocprof.md (kernel
+    statistics) and profiles/<entry point>_<workload>_traffic.json (HBM bytes
+    per call, summed over the call's kernels and scaled by the counters'
+    reading for the 1 GiB probe copy)."""
     import numpy as np
 
-    from sparse_attention_indexer_row_amd import workloads
-
+    stem, kernels, algo_read, algo_write = profile_target(workload)
     stats = _csv_rows(os.path.join(trace_dir, "trace_kernel_stats.csv"))
     trace = _csv_rows(os.path.join(trace_dir, "trace_kernel_trace.csv"))
-    sel = [r for r in stats if r["Name"].startswith("select_kernel")]
-    if not sel:
-        print("no select_kernel in the kernel statistics", file=sys.stderr)
+    durs = {kn: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                 for r in trace if r["Kernel_Name"].startswith(kn)] for kn in kernels}
+    if not all(durs.values()):
+        print(f"the kernel trace lacks one of {kernels}", file=sys.stderr)
         return 1
-    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            for r in trace if r["Kernel_Name"].startswith("select_kernel")]
 
     def counter(dirname, prefix, name):
         rows = _csv_rows(os.path.join(dirname, f"{prefix}_counter_collection.csv"))
         pick = lambda kn: [float(r["Counter_Value"]) for r in rows
                            if r["Kernel_Name"].startswith(kn) and r["Counter_Name"] == name]
-        return pick("select_kernel"), pick("probe_copy_kernel")
+        return {kn: pick(kn) for kn in kernels}, pick("probe_copy_kernel")
 
-    f_sel, f_copy = counter(fetch_dir, "fetch", "FETCH_SIZE")
-    w_sel, w_copy = counter(write_dir, "write", "WRITE_SIZE")
-    if not (f_sel and f_copy and w_sel and w_copy):
-        print("counter files lack select_kernel or probe_copy_kernel rows", file=sys.stderr)
+    f_k, f_copy = counter(fetch_dir, "fetch", "FETCH_SIZE")
+    w_k, w_copy = counter(write_dir, "write", "WRITE_SIZE")
+    if not (all(f_k.values()) and f_copy and all(w_k.values()) and w_copy):
+        print("counter files lack a kernel's or probe_copy_kernel's rows", file=sys.stderr)
         return 1
     fetch_scale = (COPY_BYTES / 1024) / float(np.mean(f_copy))
     write_scale = (COPY_BYTES / 1024) / float(np.mean(w_copy))
-    fetch_b = float(np.mean(f_sel)) * 1024 * fetch_scale
-    write_b = float(np.mean(w_sel)) * 1024 * write_scale
-    w = workloads.make(workload)
-    algo_read = 4 * w.valid_elements()
-    algo_write = 8 * w.rows * w.k
+    f_kib = {kn: float(np.mean(v)) for kn, v in f_k.items()}
+    w_kib = {kn: float(np.mean(v)) for kn, v in w_k.items()}
+    fetch_b = sum(f_kib.values()) * 1024 * fetch_scale
+    write_b = sum(w_kib.values()) * 1024 * write_scale
     traffic = {
-        "kernel": "select_kernel", "workload": workload,
-        "kernel_source_sha256": kernel_source_hash(),
-        "fetch_kib_per_dispatch": round(float(np.mean(f_sel)), 3),
-        "write_kib_per_dispatch": round(float(np.mean(w_sel)), 3),
+        "kernels": kernels, "workload": workload,
+        "kernel_source_sha256": kernel_source_hash(workload),
+        "fetch_kib_per_dispatch": {kn: round(v, 3) for kn, v in f_kib.items()},
+        "write_kib_per_dispatch": {kn: round(v, 3) for kn, v in w_kib.items()},
         "copy_bytes": COPY_BYTES,
         "copy_fetch_kib": round(float(np.mean(f_copy)), 3),
         "copy_write_kib": round(float(np.mean(w_copy)), 3),
@@ -121,11 +150,10 @@ def summarize_profiles(workload: str, trace_dir: str, fetch_dir: str, write_dir:
         "commands": {k: v.format(d="<dir>", w=workload) for k, v in PROFILE_COMMANDS.items()},
     }
     os.makedirs(TRAFFIC_DIR, exist_ok=True)
-    with open(os.path.join(TRAFFIC_DIR, f"topk_select_{workload}_traffic.json"), "w") as f:
+    with open(os.path.join(TRAFFIC_DIR, f"{stem}_traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
         f.write("\n")
-    lines = [f"# select_kernel, workload `{workload}`: rocprofv3 summary", "",
-             f"Workload: {w.description}.", "",
+    lines = [f"# {' + '.join(kernels)}, workload `{workload}`: rocprofv3 summary", "",
              "Commands (run from the repository root; `<dir>` is any output directory):", ""]
     lines += [f"    {v.format(d='<dir>', w=workload)}" for v in PROFILE_COMMANDS.values()]
     lines += ["", "Kernel statistics (`--kernel-trace --stats`):", "",
@@ -133,20 +161,24 @@ def summarize_profiles(workload: str, trace_dir: str, fetch_dir: str, write_dir:
     for r in stats:
         lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
-    lines += ["", f"select_kernel dispatch durations: mean {np.mean(durs):.1f} us, median "
-              f"{np.median(durs):.1f} us over {len(durs)} dispatches (includes the warm-up and "
-              f"parity launches).", "",
-              "HBM traffic per select_kernel dispatch (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`):", "",
-              f"- FETCH_SIZE {traffic['fetch_kib_per_dispatch']} KiB; the 1 GiB probe copy reads as "
-              f"{traffic['copy_fetch_kib']} KiB, scale {traffic['fetch_scale']} -> "
-              f"{fetch_b / 1e6:.1f} MB read (algorithmic {algo_read / 1e6:.1f} MB).",
-              f"- WRITE_SIZE {traffic['write_kib_per_dispatch']} KiB; the 1 GiB probe copy writes as "
-              f"{traffic['copy_write_kib']} KiB, scale {traffic['write_scale']} -> "
-              f"{write_b / 1e6:.2f} MB written (algorithmic {algo_write / 1e6:.2f} MB of outputs).",
-              f"- Total {traffic['bytes_per_launch'] / 1e6:.1f} MB per launch, "
+    lines.append("")
+    for kn in kernels:
+        lines.append(f"{kn} dispatch durations: mean {np.mean(durs[kn]):.1f} us, median "
+                     f"{np.median(durs[kn]):.1f} us over {len(durs[kn])} dispatches (includes the "
+                     f"warm-up and parity launches).")
+    lines += ["", "HBM traffic per call (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`; KiB per "
+              "dispatch of each kernel):", ""]
+    for kn in kernels:
+        lines.append(f"- {kn}: FETCH_SIZE {f_kib[kn]:.1f} KiB, WRITE_SIZE {w_kib[kn]:.1f} KiB")
+    lines += [f"- The 1 GiB probe copy reads as {traffic['copy_fetch_kib']} KiB and writes as "
+              f"{traffic['copy_write_kib']} KiB: scales {traffic['fetch_scale']} and "
+              f"{traffic['write_scale']}.",
+              f"- Read {fetch_b / 1e6:.1f} MB per call (algorithmic {algo_read / 1e6:.1f} MB); written "
+              f"{write_b / 1e6:.2f} MB (algorithmic {algo_write / 1e6:.2f} MB of outputs).",
+              f"- Total {traffic['bytes_per_launch'] / 1e6:.1f} MB per call, "
               f"{traffic['bytes_per_launch'] / (algo_read + algo_write):.3f} x the algorithmic bytes.",
               "", f"Kernel sources: sha256 {traffic['kernel_source_sha256']}.", ""]
-    with open(os.path.join(TRAFFIC_DIR, f"topk_select_{workload}_rocprof.md"), "w") as f:
+    with open(os.path.join(TRAFFIC_DIR, f"{stem}_rocprof.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
     return 0
@@ -160,13 +192,131 @@ def host_cores() -> int:
     return max(1, min(n, 16))
 
 
+METRIC_SELECT = "effective HBM read GB/s (and rows/s) for top-512 of 1M fp32 scores/row"
+POOL_GROUP, POOL_KEEP, POOL_PINNED = 8, 2000, 16
+
+
+def make_case(name, dev, np, torch, api, workloads):
+    """Inputs, one step, its parity check and CPU baseline for a workload.
+    The timed region rotates over enough input copies (>= 1.5 GiB) that
+    every step reads cold HBM."""
+    import oracle
+
+    stream = torch.cuda.current_stream(dev)
+    c = {}
+
+    def rotate(base_list, batch_bytes):
+        copies = max(2, -(-(3 << 29) // batch_bytes))
+        return [base_list] + [[t.clone() for t in base_list] for _ in range(copies - 1)], copies
+
+    if name == "pooled":
+        w = workloads.pooled()
+        base = [torch.from_numpy(w.pool_scores).to(dev), torch.from_numpy(w.pool_idx).to(dev)]
+        inputs, copies = rotate(base, base[0].numel() * 4 + base[1].numel() * 4)
+        vals = torch.empty((w.rows, w.k), dtype=torch.float32, device=dev)
+        idx = torch.empty((w.rows, w.k), dtype=torch.int32, device=dev)
+
+        def step(i):
+            ps, pi = inputs[i % len(inputs)]
+            api.topk_pooled_select(ps, pi, w.group, w.k, w.n, out=(vals, idx), stream=stream)
+
+        def parity():
+            sample = sorted({0, 1, w.rows // 2, w.rows - 1})
+            rv, ri = oracle.pooled_topk(w.pool_scores[sample], w.pool_idx[sample], w.group, w.k, w.n)
+            gv, gi = vals.cpu().numpy()[sample], idx.cpu().numpy()[sample]
+            return (np.array_equal(gi, ri) and np.array_equal(gv.view(np.uint32), rv.view(np.uint32)),
+                    sample)
+
+        def cpu(cores):
+            t0 = time.perf_counter()
+            oracle.pooled_topk(w.pool_scores, w.pool_idx, w.group, w.k, w.n)
+            return time.perf_counter() - t0, 4 * w.pool_scores.size, f"all {w.rows} pooled rows"
+
+        read = 4 * w.pool_scores.size
+        c.update(rows=w.rows, read_bytes=read, copies=copies, step=step, parity=parity, cpu=cpu,
+                 cpu_cores=lambda cores: 1,
+                 kernel="pool_order_kernel + select_kernel + pool_positions_kernel (whole call)",
+                 metric="effective HBM read GB/s of pooled scores for top-512 inside "
+                        "2,000-block pools (16,000 candidates per row)",
+                 config={"workload": w.description, "rows": w.rows, "n": w.n, "k": w.k,
+                         "group": w.group, "keep": w.keep})
+        c["set_copies"] = lambda m: None
+        return c
+
+    wname = "adverse" if name == "pool" else name
+    w = workloads.make(wname)
+    rows, n, k = w.rows, w.n, w.k
+    base = torch.from_numpy(w.scores).to(dev)
+    lengths = torch.from_numpy(w.lengths).to(dev) if w.lengths is not None else None
+    inputs, copies = rotate([base], base.numel() * 4)
+
+    def set_copies(m):
+        inputs[:] = [[base]] + [[base.clone()] for _ in range(m - 1)]
+
+    sample = sorted({0, 1, rows // 2, rows - 1})
+    sl = w.lengths[sample] if w.lengths is not None else None
+    if name == "pool":
+        vals = torch.empty((rows, POOL_KEEP), dtype=torch.float32, device=dev)
+        idx = torch.empty((rows, POOL_KEEP), dtype=torch.int32, device=dev)
+
+        def step(i):
+            api.topk_block_pool(inputs[i % len(inputs)][0], POOL_GROUP, POOL_KEEP, POOL_PINNED,
+                                lengths, out=(vals, idx), stream=stream)
+
+        def ref(x, ln, cores):
+            return oracle.block_pool(x, POOL_GROUP, POOL_KEEP, POOL_PINNED, ln)
+
+        kernel = "block_max_kernel + select_kernel (whole call)"
+        metric = ("effective HBM read GB/s of 1M fp32 scores/row for the block-max pool "
+                  f"(blocks of {POOL_GROUP}, {POOL_KEEP:,} kept, {POOL_PINNED} newest pinned)")
+        config = {"workload": w.description + f"; block-max pool, blocks of {POOL_GROUP}, "
+                  f"keep {POOL_KEEP}, {POOL_PINNED} pinned", "rows": rows, "n": n,
+                  "group": POOL_GROUP, "keep": POOL_KEEP, "pinned": POOL_PINNED}
+        cores_used = lambda cores: 1
+    else:
+        vals = torch.empty((rows, k), dtype=torch.float32, device=dev)
+        idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+
+        def step(i):
+            api.topk_select(inputs[i % len(inputs)][0], k, lengths, out=(vals, idx), stream=stream)
+
+        def ref(x, ln, cores):
+            return oracle.topk(x, k, ln, threads=cores)
+
+        kernel = "select_kernel"
+        metric = METRIC_SELECT
+        plan = api.topk_plan(rows, n, k)
+        config = {"workload": w.description, "rows": rows, "n": n, "k": k,
+                  "split": plan["split"], "waves": plan["waves"]}
+        cores_used = lambda cores: cores
+
+    def parity():
+        rv, ri = ref(w.scores[sample], sl, 4)
+        gv, gi = vals.cpu().numpy()[sample], idx.cpu().numpy()[sample]
+        return (np.array_equal(gi, ri) and np.array_equal(gv.view(np.uint32), rv.view(np.uint32)),
+                sample)
+
+    def cpu(cores):
+        t0 = time.perf_counter()
+        ref(w.scores, w.lengths, cores)
+        return (time.perf_counter() - t0, 4 * w.valid_elements(),
+                f"all {rows} rows of the batch")
+
+    c.update(rows=rows, read_bytes=4 * w.valid_elements(), copies=copies, step=step,
+             parity=parity, cpu=cpu, cpu_cores=cores_used, kernel=kernel, metric=metric,
+             config=config, set_copies=set_copies)
+    return c
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="adverse",
-                    choices=["small", "outlier", "one_row", "adverse", "ragged"])
+                    choices=["small", "outlier", "one_row", "adverse", "ragged", "pool", "pooled"],
+                    help="pool: topk_block_pool over the adverse rows (blocks of 8, keep 2,000, "
+                         "16 pinned); pooled: topk_pooled_select over 2,000-block pools")
     ap.add_argument("--copies", type=int, default=0,
                     help="input copies to rotate over (0: enough for >= 1.5 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -196,36 +346,21 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
-    w = workloads.make(args.workload)
-    rows, n, k = w.rows, w.n, w.k
-    valid = w.valid_elements()
-    read_bytes = 4 * valid
-
-    base = torch.from_numpy(w.scores).to(dev)
-    lengths = torch.from_numpy(w.lengths).to(dev) if w.lengths is not None else None
-    batch_bytes = base.numel() * 4
-    copies = args.copies or max(2, -(-(3 << 29) // batch_bytes))
-    inputs = [base] + [base.clone() for _ in range(copies - 1)]
-    vals = torch.empty((rows, k), dtype=torch.float32, device=dev)
-    idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
-    plan = api.topk_plan(rows, n, k)
     stream = torch.cuda.current_stream(dev)
+    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
+    case = make_case(args.workload, dev, np, torch, api, workloads)
+    rows, read_bytes, copies = case["rows"], case["read_bytes"], case["copies"]
+    if args.copies:
+        case["set_copies"](args.copies)
+        copies = args.copies
+    step = case["step"]
 
-    def step(i):
-        api.topk_select(inputs[i % copies], k, lengths, out=(vals, idx), stream=stream)
-
-    # parity on sampled rows of copy 0 (the full-size parity test covers all rows)
+    # parity on sampled rows of copy 0 (the full-size parity tests cover all rows)
     parity = None
     if not args.profile_run:
-        import oracle
         step(0)
         torch.cuda.synchronize()
-        sample = sorted({0, 1, rows // 2, rows - 1})
-        sl = w.lengths[sample] if w.lengths is not None else None
-        rv, ri = oracle.topk(w.scores[sample], k, sl)
-        gv, gi = vals.cpu().numpy()[sample], idx.cpu().numpy()[sample]
-        ok = np.array_equal(gi, ri) and np.array_equal(gv.view(np.uint32), rv.view(np.uint32))
+        ok, sample = case["parity"]()
         parity = f"bit-exact vs oracle on rows {sample}" if ok else "MISMATCH"
         if not ok:
             print("[bench] parity mismatch against the oracle", file=sys.stderr)
@@ -296,22 +431,14 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
         cores = host_cores()
-        sample_rows = rows
-        t0 = time.perf_counter()
-        oracle.topk(w.scores[:sample_rows], k, w.lengths[:sample_rows] if w.lengths is not None else None,
-                    threads=cores)
-        dt = time.perf_counter() - t0
-        sample_valid = (sample_rows * n if w.lengths is None
-                        else int(np.clip(w.lengths[:sample_rows], 0, n).sum()))
-        cpu = {"value": round(4 * sample_valid / dt / 1e9, 3), "unit": "GB/s", "cores": cores,
-               "kind": "oracle",
-               "sample": f"all {sample_rows} rows of the batch, one pass, {dt:.2f} s wall "
-                         f"({sample_rows / dt:.1f} rows/s)"}
+        dt, sample_bytes, sample = case["cpu"](cores)
+        cpu = {"value": round(sample_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": case["cpu_cores"](cores),
+               "kind": "oracle", "sample": f"{sample}, one pass, {dt:.2f} s wall"}
 
     traffic = load_traffic(args.workload)
     roofline = {
+        "kernel": case["kernel"],
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBPS,
@@ -320,7 +447,7 @@ def main() -> int:
         "traffic": traffic["bytes_per_launch"] if traffic else None,
     }
     out = {
-        "metric": "effective HBM read GB/s (and rows/s) for top-512 of 1M fp32 scores/row",
+        "metric": case["metric"],
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -332,9 +459,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.description, "rows": rows, "n": n, "k": k,
-                   "read_bytes_per_step": read_bytes, "split": plan["split"],
-                   "waves": plan["waves"], "input_copies": copies},
+        "config": dict(case["config"], read_bytes_per_step=read_bytes, input_copies=copies),
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
         "kernel_us_mean": round(kern_ms * 1e3, 2),
         "kernel_us_median": round(float(np.median(per_launch_ms)) * 1e3, 2),

@@ -190,6 +190,40 @@ int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, i
                     int32_t group, int32_t keep, int32_t pinned, float *out_vals,
                     int32_t *out_idx, void *stream);
 
+/* Most pool slots topk_pooled_select takes per row. */
+#define TOPK_MAX_POOL_SLOTS 8192
+
+/*
+ * topk_pooled_select -- top-k inside a block pool ("The Secret GPU Kernel
+ * Behind DeepSeek V4.1 Flash", transcript 7:46-8:00): the indexers above the
+ * pooling layer score only the pooled positions and keep their own top-k.
+ *
+ *   pool_idx: int32 [rows][keep], a row's pooled block indices (as written by
+ *   topk_block_pool; negative = empty slot).  Slot s covers context positions
+ *   pool_idx[r][s]*group + j, j < group.
+ *   pool_scores: fp32 [rows][keep*group]; [r][s*group + j] is the score of
+ *   that position.
+ *   Row r of the context has length L_r = clamp(lengths[r], 0, n) (n when
+ *   `lengths` is NULL); positions >= L_r are not candidates.
+ *   Output row r has k slots: the top-k candidates by value descending in
+ *   IEEE-754 total order, equal values to the LOWER CONTEXT POSITION
+ *   (whatever their slot order), then (-inf, -1).  out_idx holds context
+ *   positions, out_vals bit copies of the scores.
+ *
+ * Precondition: a row's block indices are distinct and below 2^31 / group
+ * (a pool never repeats a block); otherwise the output is unspecified but
+ * the call stays memory-safe.  1 <= keep <= TOPK_MAX_POOL_SLOTS, group >= 1
+ * (TOPK_EINVAL otherwise), 1 <= k <= TOPK_MAX_K (TOPK_EK_RANGE).
+ * Work: per row, the pool's blocks are sorted into position order and their
+ * scores gathered into a library-owned, grow-only device buffer; the
+ * selection of topk_select runs over the gathered rows; a last step turns
+ * gathered offsets into positions.  Buffer rules as for topk_block_pool.
+ */
+int topk_pooled_select(const float *pool_scores, const int32_t *pool_idx,
+                       const int32_t *lengths, int32_t rows, int32_t n, int32_t group,
+                       int32_t keep, int32_t k, float *out_vals, int32_t *out_idx,
+                       void *stream);
+
 /* Human-readable text for a status code (static storage). */
 const char *topk_strerror(int status);
 

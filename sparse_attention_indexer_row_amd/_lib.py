@@ -25,6 +25,7 @@ TOPK_MAX_K = 2048
 TOPK_FLAG_NO_ESTIMATE = 1
 TOPK_FLAG_FORCE_RERUN = 2
 TOPK_MAX_SPLIT = 1024
+TOPK_MAX_POOL_SLOTS = 8192
 
 # Every function the header declares, in header order.
 EXPORTS = (
@@ -35,6 +36,7 @@ EXPORTS = (
     "topk_select_ex",
     "topk_plan",
     "topk_block_pool",
+    "topk_pooled_select",
     "topk_strerror",
     "topk_visit_order",
     "topk_probe_sink_words",
@@ -80,6 +82,8 @@ SIGNATURES = {
     "topk_plan": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(TopkOptions),
                                  ctypes.POINTER(TopkPlan)]),
     "topk_block_pool": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "topk_pooled_select": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                          _vp]),
     "topk_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "topk_visit_order": (ctypes.c_int, [_u64, _i32, _i32, _vp]),
     "topk_probe_sink_words": (_sz, [_sz]),

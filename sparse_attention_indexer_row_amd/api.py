@@ -164,6 +164,26 @@ def topk_block_pool(scores: torch.Tensor, group: int, keep: int, pinned: int,
     return vals, idx
 
 
+def topk_pooled_select(pool_scores: torch.Tensor, pool_idx: torch.Tensor, group: int, k: int,
+                       n: int, lengths: torch.Tensor | None = None, out=None, stream=None):
+    """Top-k inside a block pool: (values, int32 context positions) [rows][k]."""
+    if not isinstance(pool_idx, torch.Tensor) or pool_idx.dim() != 2:
+        raise ValueError("pool_idx must be a 2-D tensor [rows][keep]")
+    if pool_idx.dtype != torch.int32 or not pool_idx.is_contiguous():
+        raise ValueError("pool_idx must be a contiguous int32 tensor")
+    _check_scores(pool_scores)
+    rows, keep = pool_idx.shape
+    if pool_scores.shape != (rows, keep * group) or pool_idx.device != pool_scores.device:
+        raise ValueError("pool_scores must be [rows][keep * group] on pool_idx's device")
+    lp = _check_lengths(lengths, pool_scores)
+    vals, idx = _outputs(pool_scores, k, out)
+    st = _lib.load().topk_pooled_select(pool_scores.data_ptr(), pool_idx.data_ptr(), lp, rows, n,
+                                        group, keep, k, vals.data_ptr(), idx.data_ptr(),
+                                        _stream_handle(stream, pool_scores.device))
+    _lib.check(st, "topk_pooled_select")
+    return vals, idx
+
+
 def topk_strerror(status: int) -> str:
     return _lib.load().topk_strerror(status).decode()
 

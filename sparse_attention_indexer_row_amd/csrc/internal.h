@@ -55,6 +55,30 @@ struct PoolArgs {
 
 hipError_t launch_block_max(const PoolArgs &a, hipStream_t stream);
 
+// Selection inside a block pool: the pool's blocks in position order.  The
+// order kernel sorts a row's slots in LDS (8 bytes per slot, rounded up to a
+// power of two), so keep is at most TOPK_MAX_POOL_SLOTS (64 KiB).
+
+struct PooledArgs {
+    const float *pool_scores;  // [rows][keep * group]
+    const int32_t *pool_idx;   // [rows][keep]
+    const int32_t *lengths;    // [rows] or null
+    int64_t n;                 // context length
+    int64_t ld;                // row stride of `gathered` (>= keep * group)
+    int32_t rows;              // rows handled by this launch
+    int32_t row0;
+    int32_t group;
+    int32_t keep;              // pool slots per row, <= TOPK_MAX_POOL_SLOTS
+    int32_t k;
+    float *gathered;           // [rows][ld] scores in ascending position order
+    int32_t *blocks;           // [rows][keep] block of each gathered group (ascending)
+    int32_t *valid;            // [rows] gathered scores below the row length
+    int32_t *out_idx;          // [rows][k] gathered offsets in, context positions out
+};
+
+hipError_t launch_pool_order(const PooledArgs &a, hipStream_t stream);
+hipError_t launch_pool_positions(const PooledArgs &a, hipStream_t stream);
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);

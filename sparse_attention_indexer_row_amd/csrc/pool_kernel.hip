@@ -75,7 +75,120 @@ __global__ __launch_bounds__(kPoolThreads) void block_max_kernel(PoolArgs a) {
     }
 }
 
+// Selection inside a block pool ("The Secret GPU Kernel Behind DeepSeek V4.1
+// Flash", transcript 7:46-8:00): the layers above score only the pooled
+// positions.  The selection kernel gives equal values to the earlier element
+// of its row, so the pool is first laid out in ascending position order:
+// one workgroup per row sorts the (block, slot) pairs by block with a
+// bitonic network in LDS (empty slots last), records the sorted blocks, and
+// copies each block's scores into that order.  Since the blocks are
+// distinct and ascending, the positions along the gathered row increase
+// strictly, so the scores below the row length form a prefix whose length
+// is the selection's row length.  After the selection, a map turns gathered
+// offsets back into context positions.
+constexpr int kOrderThreads = 256;
+
+__global__ __launch_bounds__(kOrderThreads) void pool_order_kernel(PooledArgs a, int p2) {
+    extern __shared__ uint64_t sorted[];  // p2 words: block << 32 | slot
+    __shared__ int32_t count;
+    const int64_t r = (int64_t)a.row0 + blockIdx.x;
+    const int tid = threadIdx.x;
+    const int32_t *pi = a.pool_idx + r * (int64_t)a.keep;
+    for (int i = tid; i < p2; i += kOrderThreads) {
+        uint64_t w = ~0ull;
+        if (i < a.keep) {
+            const int32_t b = pi[i];
+            w = ((uint64_t)(b < 0 ? 0xFFFFFFFFu : (uint32_t)b) << 32) | (uint32_t)i;
+        }
+        sorted[i] = w;
+    }
+    if (tid == 0) count = 0;
+    __syncthreads();
+    for (int size = 2; size <= p2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < (p2 >> 1); t += kOrderThreads) {
+                const int lo = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
+                const int hi = lo + stride;
+                const uint64_t x = sorted[lo], y = sorted[hi];
+                const bool up = (lo & size) == 0;
+                if ((x > y) == up) {
+                    sorted[lo] = y;
+                    sorted[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    int64_t L = a.n;
+    if (a.lengths) {
+        const int64_t l = a.lengths[r];
+        L = l < 0 ? 0 : (l > a.n ? a.n : l);
+    }
+    const int64_t g = a.group;
+    int32_t *blk = a.blocks + r * (int64_t)a.keep;
+    for (int i = tid; i < a.keep; i += kOrderThreads) {
+        const uint32_t b = (uint32_t)(sorted[i] >> 32);
+        blk[i] = b == 0xFFFFFFFFu ? -1 : (int32_t)b;
+    }
+    const float *ps = a.pool_scores + r * (int64_t)a.keep * g;
+    float *out = a.gathered + r * a.ld;
+    // keep * group < 2^31 (checked on the host): 32-bit offsets, and the
+    // (slot, lane) pair of offset c advances by a fixed step per iteration,
+    // so the loop divides nothing.
+    const uint32_t total = (uint32_t)a.keep * (uint32_t)a.group;
+    const uint32_t ug = (uint32_t)a.group;
+    const uint32_t di = (uint32_t)kOrderThreads / ug, dj = (uint32_t)kOrderThreads % ug;
+    uint32_t i = (uint32_t)tid / ug, j = (uint32_t)tid % ug;
+    int mine = 0;
+    for (uint32_t c = (uint32_t)tid; c < total; c += kOrderThreads) {
+        const uint64_t w = sorted[i];
+        const uint32_t b = (uint32_t)(w >> 32);
+        if (b != 0xFFFFFFFFu && (int64_t)b * g + j < L) {
+            out[c] = ps[(size_t)(uint32_t)w * ug + j];
+            ++mine;
+        }
+        i += di;
+        j += dj;
+        if (j >= ug) {
+            j -= ug;
+            ++i;
+        }
+    }
+    if (mine) atomicAdd(&count, mine);
+    __syncthreads();
+    if (tid == 0) a.valid[r] = count;
+}
+
+__global__ __launch_bounds__(256) void pool_positions_kernel(PooledArgs a) {
+    const int64_t r = (int64_t)a.row0 + blockIdx.y;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= a.k) return;
+    int32_t *idx = a.out_idx + r * (int64_t)a.k;
+    const int32_t c = idx[t];
+    if (c < 0) return;
+    const uint32_t g = (uint32_t)a.group;
+    const uint32_t i = (uint32_t)c / g;
+    idx[t] = (int32_t)((uint32_t)a.blocks[r * (int64_t)a.keep + i] * g + ((uint32_t)c - i * g));
+}
+
 }  // namespace
+
+hipError_t launch_pool_order(const PooledArgs &a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    int p2 = 1;
+    while (p2 < a.keep) p2 <<= 1;
+    if (p2 < 2) p2 = 2;
+    hipLaunchKernelGGL(pool_order_kernel, dim3((unsigned)a.rows), dim3(kOrderThreads),
+                       (size_t)p2 * 8, stream, a, p2);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_positions(const PooledArgs &a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((a.k + 255) / 256), (unsigned)a.rows);
+    hipLaunchKernelGGL(pool_positions_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_block_max(const PoolArgs &a, hipStream_t stream) {
     if (a.rows <= 0 || a.span <= 0) return hipSuccess;

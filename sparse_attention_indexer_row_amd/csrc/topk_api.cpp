@@ -405,6 +405,69 @@ int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, i
                ws, 0, 0u, nullptr, (hipStream_t)stream, keep);
 }
 
+int topk_pooled_select(const float *pool_scores, const int32_t *pool_idx,
+                       const int32_t *lengths, int32_t rows, int32_t n, int32_t group,
+                       int32_t keep, int32_t k, float *out_vals, int32_t *out_idx,
+                       void *stream) {
+    if (rows < 0 || n < 1 || group < 1 || keep < 1 || keep > TOPK_MAX_POOL_SLOTS)
+        return TOPK_EINVAL;
+    if (k < 1 || k > TOPK_MAX_K) return TOPK_EK_RANGE;
+    const int64_t total = (int64_t)keep * group;
+    const int64_t ld = (total + kPoolRowAlign - 1) / kPoolRowAlign * kPoolRowAlign;
+    if (ld > INT32_MAX) return TOPK_EINVAL;
+    if (rows == 0) return TOPK_OK;
+    if (!pool_scores || !pool_idx || !out_vals || !out_idx) return TOPK_EINVAL;
+    if (misaligned(pool_scores, 4) || misaligned(pool_idx, 4) || misaligned(out_vals, 4) ||
+        misaligned(out_idx, 4) || (lengths && misaligned(lengths, 4)))
+        return TOPK_EINVAL;
+    int st = check_plan(make_plan(rows, (int32_t)ld, k, nullptr, kAssumedCUs));
+    if (st != TOPK_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != TOPK_OK) return st;
+    const size_t gathered_bytes = align_up((size_t)rows * (size_t)ld * 4, kAlign);
+    const size_t blocks_bytes = align_up((size_t)rows * (size_t)keep * 4, kAlign);
+    void *scratch = nullptr;
+    st = grow_buffer(g_pool, gathered_bytes + blocks_bytes + (size_t)rows * 4, false,
+                     (hipStream_t)stream, &scratch);
+    if (st != TOPK_OK) return st;
+    char *base = static_cast<char *>(scratch);
+    topk::PooledArgs a{};
+    a.pool_scores = pool_scores;
+    a.pool_idx = pool_idx;
+    a.lengths = lengths;
+    a.n = n;
+    a.ld = ld;
+    a.group = group;
+    a.keep = keep;
+    a.k = k;
+    a.gathered = reinterpret_cast<float *>(base);
+    a.blocks = reinterpret_cast<int32_t *>(base + gathered_bytes);
+    a.valid = reinterpret_cast<int32_t *>(base + gathered_bytes + blocks_bytes);
+    a.out_idx = out_idx;
+    for (int32_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
+        a.row0 = r0;
+        a.rows = std::min(kMaxGridRows, rows - r0);
+        if (topk::launch_pool_order(a, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
+    }
+    Plan pl = make_plan(rows, (int32_t)ld, k, nullptr, cus);
+    void *ws = nullptr;
+    if (pl.split > 1) {
+        st = internal_workspace(pl.ws_bytes, (hipStream_t)stream, &ws);
+        if (st != TOPK_OK) return st;
+    }
+    st = run(a.gathered, a.valid, rows, (int32_t)ld, k, out_vals, out_idx, pl, ws, 0, 0u,
+             nullptr, (hipStream_t)stream);
+    if (st != TOPK_OK) return st;
+    for (int32_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
+        a.row0 = r0;
+        a.rows = std::min(kMaxGridRows, rows - r0);
+        if (topk::launch_pool_positions(a, (hipStream_t)stream) != hipSuccess)
+            return TOPK_ELAUNCH;
+    }
+    return TOPK_OK;
+}
+
 const char *topk_strerror(int status) {
     switch (status) {
         case TOPK_OK: return "ok";

@@ -19,6 +19,15 @@ Named workloads (rows x n, k):
                                     odd rows quantized to 256 levels
   ragged    256 x 262,144, k=2048 lengths uniform in [1, 262,144], scores
                                     N(0,1) + 0.5*log1p(position), -inf padding
+
+Pooled workload (``pooled``): the rows an indexer above the pooling layer
+sees (transcript 7:22-7:46: blocks of 8 positions, 2,000 blocks kept, the
+newest pinned, about 16,000 candidates of a long context).  128 query rows
+over a 1,048,576-position context; each row's pool has 2,000 slots of 8
+positions: the 16 newest blocks first (newest first), then 1,984 distinct
+older blocks drawn uniformly, and N(0,1) scores for the 16,000 pooled
+positions; top-512.  The blocks are drawn at random rather than chosen by a
+pooling pass, so this module stays free of the method's arithmetic.
 """
 
 from __future__ import annotations
@@ -123,6 +132,52 @@ def ragged(seed: int = 105, rows: int = 256, n: int = 262144, k: int = 2048) -> 
     return Workload("ragged", out, lengths, k, seed,
                     f"{rows} ragged rows, lengths uniform in [1, {n:,}], padded to {n:,} "
                     f"with -inf, scores N(0,1)+0.5*log1p(position), k={k}")
+
+
+@dataclass
+class PooledWorkload:
+    name: str
+    pool_scores: np.ndarray       # float32 [rows][keep * group]
+    pool_idx: np.ndarray          # int32 [rows][keep], -1 = empty slot
+    lengths: np.ndarray | None    # int32 [rows] context lengths or None (all n)
+    n: int                        # context length
+    group: int
+    k: int
+    seed: int
+    description: str
+
+    @property
+    def rows(self) -> int:
+        return self.pool_idx.shape[0]
+
+    @property
+    def keep(self) -> int:
+        return self.pool_idx.shape[1]
+
+
+def random_pool(g: np.random.Generator, L: int, group: int, keep: int, pinned: int) -> np.ndarray:
+    """Pool slots for one row of length L: the newest min(pinned, nb) blocks,
+    newest first, then distinct older blocks drawn uniformly, then -1
+    (at most `keep` slots in all)."""
+    nb = -(-L // group)
+    P = min(pinned, nb, keep)
+    out = np.full(keep, -1, dtype=np.int32)
+    out[:P] = np.arange(nb - 1, nb - 1 - P, -1)
+    m = min(keep - P, nb - P)
+    if m > 0:
+        out[P:P + m] = g.choice(nb - P, size=m, replace=False)
+    return out
+
+
+def pooled(seed: int = 106, rows: int = 128, n: int = 1 << 20, group: int = 8,
+           keep: int = 2000, pinned: int = 16, k: int = 512) -> PooledWorkload:
+    g = _rng(seed)
+    idx = np.stack([random_pool(g, n, group, keep, pinned) for _ in range(rows)])
+    sc = g.standard_normal((rows, keep * group)).astype(np.float32)
+    return PooledWorkload("pooled", sc, idx, None, n, group, k, seed,
+                          f"{rows} rows over a {n:,}-position context; pools of {keep:,} blocks "
+                          f"of {group} ({pinned} newest pinned, the rest drawn uniformly), "
+                          f"N(0,1) scores for the {keep * group:,} pooled positions, k={k}")
 
 
 WORKLOADS = {

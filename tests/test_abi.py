@@ -38,7 +38,8 @@ def test_every_declared_symbol_is_exported(lib):
 def test_constants_match_header():
     text = open(HEADER).read()
     for cname in ("TOPK_OK", "TOPK_EINVAL", "TOPK_EK_RANGE", "TOPK_EWORKSPACE", "TOPK_ESPLIT",
-                  "TOPK_ELAUNCH", "TOPK_EDEVICE", "TOPK_EALLOC", "TOPK_MAX_K", "TOPK_MAX_SPLIT"):
+                  "TOPK_ELAUNCH", "TOPK_EDEVICE", "TOPK_EALLOC", "TOPK_MAX_K", "TOPK_MAX_SPLIT",
+                  "TOPK_MAX_POOL_SLOTS"):
         m = re.search(rf"#define {cname} \(?(-?\d+)\)?", text)
         assert m and int(m.group(1)) == getattr(_lib, cname), cname
 
@@ -105,6 +106,26 @@ def test_split_and_ex_argument_errors(lib):
 ])
 def test_block_pool_argument_errors(lib, args, status):
     assert lib.topk_block_pool(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # pool_scores, pool_idx, lengths, rows, n, group, keep, k, out_vals, out_idx, stream
+    ((FAKE, FAKE, None, -1, 64, 8, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),     # rows < 0
+    ((FAKE, FAKE, None, 1, 0, 8, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),       # n < 1
+    ((FAKE, FAKE, None, 1, 64, 0, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # group < 1
+    ((FAKE, FAKE, None, 1, 64, 8, 0, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),       # keep < 1
+    ((FAKE, FAKE, None, 1, 64, 8, 8193, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),    # keep > max
+    ((FAKE, FAKE, None, 1, 64, 1 << 20, 4096, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),  # too long
+    ((FAKE, FAKE, None, 1, 64, 8, 16, 0, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),    # k < 1
+    ((FAKE, FAKE, None, 1, 64, 8, 16, 2049, FAKE, FAKE, None), _lib.TOPK_EK_RANGE), # k > max
+    ((None, FAKE, None, 1, 64, 8, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # null scores
+    ((FAKE, None, None, 1, 64, 8, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # null pool
+    ((FAKE, FAKE, None, 1, 64, 8, 16, 4, None, FAKE, None), _lib.TOPK_EINVAL),      # null out
+    ((FAKE, FAKE + 1, None, 1, 64, 8, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),  # misaligned
+    ((FAKE, FAKE, None, 0, 64, 8, 16, 4, None, None, None), _lib.TOPK_OK),          # no rows
+])
+def test_pooled_select_argument_errors(lib, args, status):
+    assert lib.topk_pooled_select(*args) == status
 
 
 def test_workspace_init_and_probe_argument_errors(lib):

@@ -131,3 +131,69 @@ def test_repeated_calls_grow_and_shrink():
     for rows, n in [(2, 1000), (40, 200_000), (3, 5000)]:
         x = workloads.normal_rows(rows, n, seed=rows + n)
         check(x, 8, 1000, 8, what=f"{rows}x{n}")
+
+
+# ---- selection inside a pool -------------------------------------------------
+
+def check_pooled(pool_scores, pool_idx, group, k, n, lengths=None, what=""):
+    print(f"[case] pooled {what} rows={pool_idx.shape[0]} keep={pool_idx.shape[1]} "
+          f"group={group} k={k} n={n}", flush=True)
+    ln = H.to_dev(lengths) if lengths is not None else None
+    gv, gi = api.topk_pooled_select(H.to_dev(pool_scores), H.to_dev(pool_idx), group, k, n, ln)
+    torch.cuda.synchronize()
+    rv, ri = oracle.pooled_topk(pool_scores, pool_idx, group, k, n, lengths)
+    H.assert_same(gv, gi, rv, ri, f"pooled {what}")
+
+
+def test_pooled_full_size():
+    w = workloads.pooled()
+    check_pooled(w.pool_scores, w.pool_idx, w.group, w.k, w.n, w.lengths, what="pooled")
+
+
+def test_pool_then_select_end_to_end():
+    # pool built on the GPU from the adverse rows, then the upper layer's
+    # scores (quantized, so ties between slots are common) selected inside it
+    w = workloads.make("adverse")
+    s = H.to_dev(w.scores)
+    pv, pi = api.topk_block_pool(s, 8, 2000, 16)
+    torch.cuda.synchronize()
+    ov, oi = oracle.block_pool(w.scores, 8, 2000, 16)
+    H.assert_same(pv, pi, ov, oi, "pool stage")
+    up = workloads.quantized_levels(workloads.normal_rows(w.rows, 2000 * 8, seed=77))
+    check_pooled(up, oi, 8, 512, w.n, what="end to end")
+
+
+@pytest.mark.parametrize("group,keep,k", [(1, 1, 1), (1, 5000, 2048), (8, 2000, 2048),
+                                          (3, 777, 100), (8, 8192, 512), (16, 64, 512)])
+def test_pooled_shapes(group, keep, k):
+    g = np.random.Generator(np.random.PCG64(group * 1000 + keep))
+    n = 200_003
+    rows = 6
+    idx = np.stack([workloads.random_pool(g, n, group, keep, 4) for _ in range(rows)])
+    sc = g.standard_normal((rows, keep * group)).astype(np.float32)
+    check_pooled(sc, idx, group, k, n, what=f"group={group} keep={keep} k={k}")
+
+
+def test_pooled_lengths_empty_slots_and_ties():
+    g = np.random.Generator(np.random.PCG64(31))
+    n, group, keep = 4000, 8, 300
+    rows = 10
+    lengths = np.array([0, 1, 7, 8, 9, 100, 2399, 3001, 4000, 5000], dtype=np.int32)
+    idx = np.full((rows, keep), -1, dtype=np.int32)
+    for r in range(rows):
+        L = int(np.clip(lengths[r], 0, n))
+        # pools drawn for the whole context, so some blocks lie past the row
+        idx[r] = workloads.random_pool(g, n, group, keep, 3)
+        if L:
+            idx[r, -5:] = -1
+    sc = np.float32(g.integers(-2, 3, size=(rows, keep * group))) / np.float32(2.0)
+    sc[g.random(sc.shape) < 0.05] = np.float32(-0.0)
+    sc[g.random(sc.shape) < 0.01] = np.float32(-np.inf)
+    check_pooled(sc, idx, group, 512, n, lengths, what="lengths and ties")
+    # scores past each row's length are +inf: any read of them would show
+    bigger = sc.copy()
+    for r in range(rows):
+        L = int(np.clip(lengths[r], 0, n))
+        pos = idx[r][:, None].astype(np.int64) * group + np.arange(group)[None, :]
+        bigger[r].reshape(keep, group)[(idx[r][:, None] >= 0) & (pos >= L)] = np.inf
+    check_pooled(bigger, idx, group, 512, n, lengths, what="masked +inf")
