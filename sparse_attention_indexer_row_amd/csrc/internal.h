@@ -55,6 +55,22 @@ struct PoolArgs {
 
 hipError_t launch_block_max(const PoolArgs &a, hipStream_t stream);
 
+// Best `k` of each row of block maxima: an exact radix selection over the
+// rows' 64-bit (key, position) words, one workgroup per row.
+struct RadixArgs {
+    const float *vals;         // [rows][ld], 16-byte aligned, ld a multiple of 4
+    const int32_t *count;      // [rows] valid elements per row (<= ld)
+    int64_t ld;
+    int32_t rows;              // rows handled by this launch
+    int32_t row0;
+    int32_t k;                 // <= TOPK_MAX_K
+    float *out_vals;           // [rows][out_ld], first k slots of each row written
+    int32_t *out_idx;
+    int64_t out_ld;
+};
+
+hipError_t launch_radix_select(const RadixArgs &a, hipStream_t stream);
+
 // Selection inside a block pool: the pool's blocks in position order.  The
 // order kernel sorts a row's slots in LDS (8 bytes per slot, rounded up to a
 // power of two), so keep is at most TOPK_MAX_POOL_SLOTS (64 KiB).

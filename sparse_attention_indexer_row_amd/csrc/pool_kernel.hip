@@ -171,7 +171,399 @@ __global__ __launch_bounds__(256) void pool_positions_kernel(PooledArgs a) {
     idx[t] = (int32_t)((uint32_t)a.blocks[r * (int64_t)a.keep + i] * g + ((uint32_t)c - i * g));
 }
 
+// Best k of a row of block maxima by radix selection.  The row is short
+// (one value per block of positions) and fully written before the selection
+// starts, so instead of streaming it through trays, one workgroup per row
+// finds the k-th largest 64-bit word (order key above the complemented
+// position, as everywhere in the library) digit by digit, most significant
+// first: each step histograms one digit of the words that match the digits
+// fixed so far and keeps the bin that holds the k-th word.  While that bin
+// is larger than the LDS candidate buffer, the steps re-read the row; once
+// it fits, one pass collects the words above the bin (certain winners) and
+// the bin itself, and the remaining steps run in LDS.  The winners (exactly
+// min(k, count) words, all distinct) are sorted by a bitonic network in LDS
+// and written out.  Words are unique, so the result does not depend on the
+// order of any step.
+constexpr int kRadixThreads = 1024;
+constexpr int kRadixBins = 2048;
+constexpr int kRadixCand = 6144;
+constexpr int kRadixSel = 2048;
+constexpr int kRadixLevels = 6;
+constexpr size_t kRadixLds = kRadixBins * 4 + kRadixSel * 8 + kRadixCand * 8;
+
+__device__ __forceinline__ int radix_shift(int level) {
+    // digits of 11, 11, 10 bits over the key, then over the position half
+    return level == 0 ? 53 : level == 1 ? 42 : level == 2 ? 32 : level == 3 ? 21 : level == 4 ? 10 : 0;
+}
+
+__device__ __forceinline__ uint64_t radix_word(float v, uint32_t i) {
+    return pack_word(order_key(__float_as_uint(v)), i);
+}
+
+// Calls fn(word, valid) for every element of a row of m floats (16-byte
+// aligned start, readable up to m rounded up to 4): eight float4 loads in
+// flight per thread, neighbouring threads on neighbouring 16 bytes.  Every
+// lane of a wave makes the same calls (`valid` is false past the row), so
+// fn may use wave-wide ballots.
+template <class F>
+__device__ __forceinline__ void for_each_word(const float *row, uint32_t m, F &&fn) {
+    constexpr uint32_t U = 8;
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const float4 *r4 = reinterpret_cast<const float4 *>(row);
+    const uint32_t n4 = (m + 3u) / 4u;
+    for (uint32_t base = threadIdx.x; base - lane < n4; base += U * kRadixThreads) {
+        float4 v[U];
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            const uint32_t q = base + u * kRadixThreads;
+            v[u] = q < n4 ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            const uint32_t i = 4u * (base + u * kRadixThreads);
+            fn(radix_word(v[u].x, i), i < m);
+            fn(radix_word(v[u].y, i + 1), i + 1 < m);
+            fn(radix_word(v[u].z, i + 2), i + 2 < m);
+            fn(radix_word(v[u].w, i + 3), i + 3 < m);
+        }
+    }
+}
+
+// Appends every word of the row with w >= lo to buf: per group of eight
+// float4 loads each thread counts its admitted words, one shuffle scan and
+// one atomic per wave place them, and the thread writes them at its offset.
+// Slots at or past `cap` are dropped; *counter still counts every word.
+__device__ __forceinline__ void append_at_least(const float *row, uint32_t m, uint64_t lo,
+                                                uint64_t *buf, uint32_t *counter, uint32_t cap) {
+    constexpr uint32_t U = 8;
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const float4 *r4 = reinterpret_cast<const float4 *>(row);
+    const uint32_t n4 = (m + 3u) / 4u;
+    for (uint32_t base = threadIdx.x; base - lane < n4; base += U * kRadixThreads) {
+        float4 v[U];
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            const uint32_t q = base + u * kRadixThreads;
+            v[u] = q < n4 ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        uint32_t mine = 0;
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            const uint32_t i = 4u * (base + u * kRadixThreads);
+            mine += (i < m && radix_word(v[u].x, i) >= lo);
+            mine += (i + 1 < m && radix_word(v[u].y, i + 1) >= lo);
+            mine += (i + 2 < m && radix_word(v[u].z, i + 2) >= lo);
+            mine += (i + 3 < m && radix_word(v[u].w, i + 3) >= lo);
+        }
+        // exclusive prefix of `mine` over the wave, and the wave's total
+        uint32_t incl = mine;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint32_t t = (uint32_t)__shfl_up((int)incl, off);
+            if ((int)lane >= off) incl += t;
+        }
+        const uint32_t total = (uint32_t)__shfl((int)incl, kWave - 1);
+        if (total == 0) continue;
+        uint32_t at = 0;
+        if (lane == kWave - 1) at = atomicAdd(counter, total);
+        at = (uint32_t)__shfl((int)at, kWave - 1) + incl - mine;
+        if (mine == 0) continue;
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            const uint32_t i = 4u * (base + u * kRadixThreads);
+            const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (uint32_t c = 0; c < 4; ++c) {
+                const uint64_t w = radix_word(e[c], i + c);
+                if (i + c < m && w >= lo) {
+                    if (at < cap) buf[at] = w;
+                    ++at;
+                }
+            }
+        }
+    }
+}
+
+// Histogram increment with the wave's most common bins merged first: rows
+// of block maxima crowd into few bins, and LDS atomics on one address
+// serialise.  Up to two rounds add the count of the lanes that share the
+// first remaining lane's bin with one atomic; the rest add one each.  All
+// lanes of the wave must call it together.
+__device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t bin, bool on) {
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+        const uint64_t act = __ballot(on);
+        if (act == 0ull) return;
+        const int leader = __ffsll((unsigned long long)act) - 1;
+        const uint32_t lb = (uint32_t)__shfl((int)bin, leader);
+        const uint64_t same = __ballot(on && bin == lb);
+        if ((int)lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+        if (on && bin == lb) on = false;
+    }
+    if (on) atomicAdd(&hist[bin], 1u);
+}
+
+// Appends w for the lanes where `take` holds: one atomic per wave, slots
+// by lane rank.  Slots at or past `cap` are dropped (never reached when the
+// counts are exact).  All lanes of the wave must call it together.
+__device__ __forceinline__ void wave_append(uint64_t *buf, uint32_t *counter, uint32_t cap,
+                                            uint64_t w, bool take) {
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint64_t mask = __ballot(take);
+    if (mask == 0ull) return;
+    const int leader = __ffsll((unsigned long long)mask) - 1;
+    uint32_t base = 0;
+    if ((int)lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
+    base = (uint32_t)__shfl((int)base, leader);
+    if (take) {
+        const uint32_t at = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+        if (at < cap) buf[at] = w;
+    }
+}
+
+// State of one radix search, shared by the workgroup.
+struct RadixShared {
+    uint32_t wave_sum[kRadixThreads / kWave];
+    uint32_t t, above, h, nsel, ncand;
+};
+
+// Finds the top-most histogram bin whose suffix count reaches `need`.
+// Each thread holds two neighbouring bins; suffix sums run from the top
+// bin down: a shuffle scan inside each wave, then the totals of the waves
+// above.  The one thread whose bin crosses `need` publishes it; everyone
+// reads it after the barrier.
+__device__ __forceinline__ void radix_pick(const uint32_t *hist, uint32_t need, RadixShared &sh) {
+    static_assert(kRadixBins == 2 * kRadixThreads, "two bins per thread");
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wv = tid / kWave;
+    const uint32_t h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
+    uint32_t suf = h0 + h1;  // becomes the sum of this lane's bins and every bin above
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_down((int)suf, off);
+        if (lane + off < kWave) suf += v;
+    }
+    if (lane == 0) sh.wave_sum[wv] = suf;
+    __syncthreads();
+    for (int u = wv + 1; u < kRadixThreads / kWave; ++u) suf += sh.wave_sum[u];
+    // suf = S(2 tid); S(2 tid + 1) = suf - h0; S(b) counts bins >= b
+    const uint32_t s1 = suf - h0;
+    if (s1 >= need && s1 - h1 < need) {
+        sh.t = (uint32_t)(2 * tid + 1);
+        sh.above = s1 - h1;
+        sh.h = h1;
+    } else if (suf >= need && suf - h0 < need) {
+        sh.t = (uint32_t)(2 * tid);
+        sh.above = suf - h0;
+        sh.h = h0;
+    }
+    __syncthreads();
+}
+
+// Exact radix search in LDS: for `need` <= n distinct words buf[0, n),
+// returns (shift, thr) such that exactly `need` of them satisfy
+// (w >> shift) >= thr.  All threads of the workgroup call it together.
+__device__ void lds_radix(const uint64_t *buf, uint32_t n, uint32_t need, uint32_t *hist,
+                          RadixShared &sh, int &thr_shift, uint64_t &thr) {
+    const int tid = threadIdx.x;
+    const uint32_t lane = (uint32_t)tid & (kWave - 1);
+    uint64_t pfx = 0;
+    for (int level = 0;; ++level) {
+        const int s = radix_shift(level);
+        const int ps = level == 0 ? 64 : radix_shift(level - 1);
+        const uint32_t dmask = (1u << (ps - s)) - 1u;
+        for (int b = tid; b < kRadixBins; b += kRadixThreads) hist[b] = 0u;
+        __syncthreads();
+        for (uint32_t c = tid; c - lane < n; c += kRadixThreads) {
+            const uint64_t w = c < n ? buf[c] : 0ull;
+            hist_add(hist, (uint32_t)(w >> s) & dmask, c < n && (level == 0 || (w >> ps) == pfx));
+        }
+        __syncthreads();
+        radix_pick(hist, need, sh);
+        const uint32_t t = sh.t, above = sh.above, h = sh.h;
+        __syncthreads();  // everyone has read the pick before the next scan writes it
+        need -= above;
+        pfx = level == 0 ? (uint64_t)t : ((pfx << (ps - s)) | t);
+        if (h == need || level == kRadixLevels - 1) {
+            thr_shift = s;
+            thr = pfx;
+            return;
+        }
+    }
+}
+
+// Sample size of the threshold estimate: 128 chunks of 64 consecutive
+// elements spread evenly over the row.
+constexpr uint32_t kSampleChunks = 128;
+constexpr uint32_t kSampleWords = kSampleChunks * kWave;
+constexpr uint32_t kEstimateMinRow = 4 * kSampleWords;
+
+__global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a) {
+    extern __shared__ uint64_t lds[];
+    uint64_t *sel = lds;                                  // kRadixSel
+    uint64_t *cand = lds + kRadixSel;                     // kRadixCand
+    uint32_t *hist = reinterpret_cast<uint32_t *>(lds + kRadixSel + kRadixCand);  // kRadixBins
+    __shared__ RadixShared sh;
+
+    const int64_t r = (int64_t)a.row0 + blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint32_t lane = (uint32_t)tid & (kWave - 1);
+    int64_t m64 = a.count[r];
+    m64 = m64 < 0 ? 0 : (m64 > a.ld ? a.ld : m64);
+    const uint32_t m = (uint32_t)m64;
+    const uint32_t k = (uint32_t)a.k;
+    const float *row = a.vals + r * a.ld;
+
+    if (tid == 0) {
+        sh.nsel = 0;
+        sh.ncand = 0;
+    }
+    __syncthreads();
+    int thr_shift = 0;
+    uint64_t thr = 0;          // winners: (w >> thr_shift) >= thr
+    bool done = false;
+    if (m <= k) {
+        // every word wins (thr = 0 admits all)
+        for_each_word(row, m, [&](uint64_t w, bool valid) {
+            wave_append(sel, &sh.nsel, kRadixSel, w, valid);
+        });
+        done = true;
+    } else if (m >= kEstimateMinRow) {
+        // Estimate: the j-th best word of an evenly spread sample, with j
+        // about four standard deviations above its expected count, admits
+        // a little more than k words; one pass appends every word at or
+        // above it to LDS.  When at least k and at most the buffer's
+        // capacity arrive, the winners are found among them exactly.
+        const float lam = (float)k * (float)kSampleWords / (float)m;
+        const uint32_t j = (uint32_t)ceilf(lam + 4.0f * sqrtf(lam) + 4.0f);
+        if (j < kSampleWords) {
+            for (uint32_t q = tid; q < kSampleWords; q += kRadixThreads) {
+                const uint32_t c = q / kWave, o = q % kWave;
+                const uint32_t i = (uint32_t)(((uint64_t)c * m) / kSampleChunks) + o;
+                cand[q] = radix_word(row[i], i);
+            }
+            __syncthreads();
+            int es = 0;
+            uint64_t et = 0;
+            lds_radix(cand, kSampleWords, j, hist, sh, es, et);
+            const uint64_t est = et << es;   // words >= est: j in the sample
+            append_at_least(row, m, est, cand, &sh.ncand, kRadixCand);
+            __syncthreads();
+            const uint32_t nc = sh.ncand;
+            if (nc >= k && nc <= (uint32_t)kRadixCand) {
+                lds_radix(cand, nc, k, hist, sh, thr_shift, thr);
+                for (uint32_t c = tid; c - lane < nc; c += kRadixThreads) {
+                    const uint64_t w = c < nc ? cand[c] : 0ull;
+                    wave_append(sel, &sh.nsel, kRadixSel, w, c < nc && (w >> thr_shift) >= thr);
+                }
+                done = true;
+            } else {
+                __syncthreads();
+                if (tid == 0) sh.ncand = 0;
+                __syncthreads();
+            }
+        }
+    }
+    if (!done) {
+        // Digit by digit over the row until the k-th word's bin fits in
+        // LDS (or is decided), then in LDS.
+        uint32_t need = k;
+        uint64_t pfx = 0;
+        for (int level = 0;; ++level) {
+            const int s = radix_shift(level);
+            const int ps = level == 0 ? 64 : radix_shift(level - 1);
+            const uint32_t dmask = (1u << (ps - s)) - 1u;
+            for (int b = tid; b < kRadixBins; b += kRadixThreads) hist[b] = 0u;
+            __syncthreads();
+            if (level == 0) {
+                for_each_word(row, m, [&](uint64_t w, bool valid) {
+                    hist_add(hist, (uint32_t)(w >> s) & dmask, valid);
+                });
+            } else {
+                for_each_word(row, m, [&](uint64_t w, bool valid) {
+                    hist_add(hist, (uint32_t)(w >> s) & dmask, valid && (w >> ps) == pfx);
+                });
+            }
+            __syncthreads();
+            radix_pick(hist, need, sh);
+            const uint32_t t = sh.t, above = sh.above, h = sh.h;
+            __syncthreads();
+            need -= above;
+            pfx = level == 0 ? (uint64_t)t : ((pfx << (ps - s)) | t);
+            if (h == need || level == kRadixLevels - 1) {
+                // the whole bin wins: winners are the words at or above it
+                // (after the last level the bin is one word)
+                for_each_word(row, m, [&](uint64_t w, bool valid) {
+                    wave_append(sel, &sh.nsel, kRadixSel, w, valid && (w >> s) >= pfx);
+                });
+                break;
+            }
+            if (h <= (uint32_t)kRadixCand) {
+                // words above the bin win; the bin goes to LDS
+                for_each_word(row, m, [&](uint64_t w, bool valid) {
+                    const uint64_t top = w >> s;
+                    wave_append(sel, &sh.nsel, kRadixSel, w, valid && top > pfx);
+                    wave_append(cand, &sh.ncand, kRadixCand, w, valid && top == pfx);
+                });
+                __syncthreads();
+                const uint32_t nc = sh.ncand;
+                lds_radix(cand, nc, need, hist, sh, thr_shift, thr);
+                for (uint32_t c = tid; c - lane < nc; c += kRadixThreads) {
+                    const uint64_t w = c < nc ? cand[c] : 0ull;
+                    wave_append(sel, &sh.nsel, kRadixSel, w, c < nc && (w >> thr_shift) >= thr);
+                }
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t ns = sh.nsel < (uint32_t)kRadixSel ? sh.nsel : (uint32_t)kRadixSel;
+    uint32_t p2 = 2;
+    while (p2 < ns) p2 <<= 1;
+    for (uint32_t c = ns + tid; c < p2; c += kRadixThreads) sel[c] = 0ull;
+    __syncthreads();
+    // bitonic sort, descending
+    for (uint32_t size = 2; size <= p2; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t t = tid; t < (p2 >> 1); t += kRadixThreads) {
+                const uint32_t lo = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
+                const uint32_t hi = lo + stride;
+                const uint64_t x = sel[lo], y = sel[hi];
+                const bool down = (lo & size) == 0;
+                if ((x < y) == down) {
+                    sel[lo] = y;
+                    sel[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    float *ov = a.out_vals + r * a.out_ld;
+    int32_t *oi = a.out_idx + r * a.out_ld;
+    for (uint32_t t = tid; t < k; t += kRadixThreads) {
+        const uint64_t w = t < ns ? sel[t] : 0ull;
+        ov[t] = w != 0ull ? __uint_as_float(key_bits((uint32_t)(w >> 32))) : -__builtin_inff();
+        oi[t] = w != 0ull ? (int32_t)word_pos(w) : -1;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_radix_select(const RadixArgs &a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    static bool raised = false;
+    if (!raised) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&radix_select_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)kRadixLds);
+        if (e != hipSuccess) return e;
+        raised = true;
+    }
+    hipLaunchKernelGGL(radix_select_kernel, dim3((unsigned)a.rows), dim3(kRadixThreads), kRadixLds,
+                       stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_pool_order(const PooledArgs &a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;

@@ -360,16 +360,9 @@ int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, i
     const int64_t nbk = ((int64_t)n + group - 1) / group;
     const int64_t bm_ld = (nbk + kPoolRowAlign - 1) / kPoolRowAlign * kPoolRowAlign;
     if (bm_ld > INT32_MAX) return TOPK_EINVAL;
-    if (older_k > 0) {
-        int st = check_plan(make_plan(rows, (int32_t)bm_ld, older_k, nullptr, kAssumedCUs));
-        if (st != TOPK_OK) return st;
-    }
-    int cus = 0;
-    int st = device_cus(&cus);
-    if (st != TOPK_OK) return st;
     const size_t bm_bytes = align_up((size_t)rows * (size_t)bm_ld * 4, kAlign);
     void *scratch = nullptr;
-    st = grow_buffer(g_pool, bm_bytes + (size_t)rows * 4, false, (hipStream_t)stream, &scratch);
+    int st = grow_buffer(g_pool, bm_bytes + (size_t)rows * 4, false, (hipStream_t)stream, &scratch);
     if (st != TOPK_OK) return st;
     float *bm = static_cast<float *>(scratch);
     int32_t *older = reinterpret_cast<int32_t *>(static_cast<char *>(scratch) + bm_bytes);
@@ -393,16 +386,22 @@ int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, i
         if (topk::launch_block_max(a, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
     }
     if (older_k == 0) return TOPK_OK;
-    // The best older blocks: a top-k of the block-maxima rows cut at each
-    // row's older-block count, written behind the pinned slots.
-    Plan pl = make_plan(rows, (int32_t)bm_ld, older_k, nullptr, cus);
-    void *ws = nullptr;
-    if (pl.split > 1) {
-        st = internal_workspace(pl.ws_bytes, (hipStream_t)stream, &ws);
-        if (st != TOPK_OK) return st;
+    // The best older blocks: an exact radix selection over each block-maxima
+    // row cut at its older-block count, written behind the pinned slots.
+    topk::RadixArgs x{};
+    x.vals = bm;
+    x.count = older;
+    x.ld = bm_ld;
+    x.k = older_k;
+    x.out_vals = out_vals + pinned;
+    x.out_idx = out_idx + pinned;
+    x.out_ld = keep;
+    for (int32_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
+        x.row0 = r0;
+        x.rows = std::min(kMaxGridRows, rows - r0);
+        if (topk::launch_radix_select(x, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
     }
-    return run(bm, older, rows, (int32_t)bm_ld, older_k, out_vals + pinned, out_idx + pinned, pl,
-               ws, 0, 0u, nullptr, (hipStream_t)stream, keep);
+    return TOPK_OK;
 }
 
 int topk_pooled_select(const float *pool_scores, const int32_t *pool_idx,
