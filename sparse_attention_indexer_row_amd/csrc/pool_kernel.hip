@@ -75,6 +75,40 @@ __global__ __launch_bounds__(kPoolThreads) void block_max_kernel(PoolArgs a) {
     }
 }
 
+// Bitonic sort of p2 (a power of two, >= 2) words in LDS by all THREADS
+// threads of the workgroup, ascending or descending.  A stage with stride
+// at most 64 pairs elements inside the 128-element segment of one wave
+// (thread t handles lo = 2t - t mod stride, and the wave's threads cover one
+// segment per round), so consecutive such stages need only the wave's own
+// LDS ordering; a workgroup barrier is needed around the wider stages.
+// The caller syncs before; the function ends with a barrier.
+template <int THREADS, bool DESC>
+__device__ void lds_bitonic(uint64_t *x, uint32_t p2) {
+    const uint32_t tid = threadIdx.x;
+    for (uint32_t size = 2; size <= p2; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t t = tid; t < (p2 >> 1); t += THREADS) {
+                const uint32_t lo = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
+                const uint32_t hi = lo + stride;
+                const uint64_t a = x[lo], b = x[hi];
+                const bool first_big = ((lo & size) == 0) == DESC;
+                if (first_big ? a < b : a > b) {
+                    x[lo] = b;
+                    x[hi] = a;
+                }
+            }
+            const uint32_t next = stride > 1 ? stride >> 1 : size;
+            if (stride > (uint32_t)kWave || next > (uint32_t)kWave) {
+                __syncthreads();
+            } else {
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+    }
+    __syncthreads();
+}
+
 // Selection inside a block pool ("The Secret GPU Kernel Behind DeepSeek V4.1
 // Flash", transcript 7:46-8:00): the layers above score only the pooled
 // positions.  The selection kernel gives equal values to the earlier element
@@ -86,7 +120,7 @@ __global__ __launch_bounds__(kPoolThreads) void block_max_kernel(PoolArgs a) {
 // strictly, so the scores below the row length form a prefix whose length
 // is the selection's row length.  After the selection, a map turns gathered
 // offsets back into context positions.
-constexpr int kOrderThreads = 256;
+constexpr int kOrderThreads = 1024;
 
 __global__ __launch_bounds__(kOrderThreads) void pool_order_kernel(PooledArgs a, int p2) {
     extern __shared__ uint64_t sorted[];  // p2 words: block << 32 | slot
@@ -104,21 +138,7 @@ __global__ __launch_bounds__(kOrderThreads) void pool_order_kernel(PooledArgs a,
     }
     if (tid == 0) count = 0;
     __syncthreads();
-    for (int size = 2; size <= p2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < (p2 >> 1); t += kOrderThreads) {
-                const int lo = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
-                const int hi = lo + stride;
-                const uint64_t x = sorted[lo], y = sorted[hi];
-                const bool up = (lo & size) == 0;
-                if ((x > y) == up) {
-                    sorted[lo] = y;
-                    sorted[hi] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
+    lds_bitonic<kOrderThreads, false>(sorted, (uint32_t)p2);
     int64_t L = a.n;
     if (a.lengths) {
         const int64_t l = a.lengths[r];
@@ -133,25 +153,43 @@ __global__ __launch_bounds__(kOrderThreads) void pool_order_kernel(PooledArgs a,
     const float *ps = a.pool_scores + r * (int64_t)a.keep * g;
     float *out = a.gathered + r * a.ld;
     // keep * group < 2^31 (checked on the host): 32-bit offsets, and the
-    // (slot, lane) pair of offset c advances by a fixed step per iteration,
-    // so the loop divides nothing.
+    // (slot, lane) pair of offset c advances by a fixed step, so the loop
+    // divides nothing.  Four loads are issued before their stores.
+    constexpr uint32_t U = 4;
     const uint32_t total = (uint32_t)a.keep * (uint32_t)a.group;
     const uint32_t ug = (uint32_t)a.group;
     const uint32_t di = (uint32_t)kOrderThreads / ug, dj = (uint32_t)kOrderThreads % ug;
     uint32_t i = (uint32_t)tid / ug, j = (uint32_t)tid % ug;
     int mine = 0;
-    for (uint32_t c = (uint32_t)tid; c < total; c += kOrderThreads) {
-        const uint64_t w = sorted[i];
-        const uint32_t b = (uint32_t)(w >> 32);
-        if (b != 0xFFFFFFFFu && (int64_t)b * g + j < L) {
-            out[c] = ps[(size_t)(uint32_t)w * ug + j];
-            ++mine;
+    for (uint32_t c0 = (uint32_t)tid; c0 < total; c0 += U * kOrderThreads) {
+        float v[U];
+        uint32_t at[U];
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            const uint32_t c = c0 + u * kOrderThreads;
+            at[u] = 0xFFFFFFFFu;
+            v[u] = 0.f;
+            if (c < total) {
+                const uint64_t w = sorted[i];
+                const uint32_t b = (uint32_t)(w >> 32);
+                if (b != 0xFFFFFFFFu && (int64_t)b * g + j < L) {
+                    v[u] = ps[(size_t)(uint32_t)w * ug + j];
+                    at[u] = c;
+                }
+            }
+            i += di;
+            j += dj;
+            if (j >= ug) {
+                j -= ug;
+                ++i;
+            }
         }
-        i += di;
-        j += dj;
-        if (j >= ug) {
-            j -= ug;
-            ++i;
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            if (at[u] != 0xFFFFFFFFu) {
+                out[at[u]] = v[u];
+                ++mine;
+            }
         }
     }
     if (mine) atomicAdd(&count, mine);
@@ -523,22 +561,7 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
     while (p2 < ns) p2 <<= 1;
     for (uint32_t c = ns + tid; c < p2; c += kRadixThreads) sel[c] = 0ull;
     __syncthreads();
-    // bitonic sort, descending
-    for (uint32_t size = 2; size <= p2; size <<= 1) {
-        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-            for (uint32_t t = tid; t < (p2 >> 1); t += kRadixThreads) {
-                const uint32_t lo = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
-                const uint32_t hi = lo + stride;
-                const uint64_t x = sel[lo], y = sel[hi];
-                const bool down = (lo & size) == 0;
-                if ((x < y) == down) {
-                    sel[lo] = y;
-                    sel[hi] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
+    lds_bitonic<kRadixThreads, true>(sel, p2);
     float *ov = a.out_vals + r * a.out_ld;
     int32_t *oi = a.out_idx + r * a.out_ld;
     for (uint32_t t = tid; t < k; t += kRadixThreads) {
