@@ -34,6 +34,7 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 # stale once any of them changes.
 SELECT_SOURCES = ["select_kernel.hip", "common.h", "wave_sort.h", "internal.h"]
 KERNEL_SOURCES = {
+    "vocab": ["pool_kernel.hip", "common.h", "internal.h"],
     "pool": SELECT_SOURCES + ["pool_kernel.hip"],
     "pooled": SELECT_SOURCES + ["pool_kernel.hip"],
 }
@@ -62,11 +63,14 @@ def profile_target(workload: str):
         return (traffic_stem(workload), ["block_max_kernel", "radix_select_kernel"],
                 4 * w.valid_elements(), 8 * w.rows * POOL_KEEP)
     w = workloads.make(workload)
+    if workload == "vocab":
+        return (traffic_stem(workload), ["radix_select_kernel"], 4 * w.valid_elements(),
+                8 * w.rows * w.k)
     return (traffic_stem(workload), ["select_kernel"], 4 * w.valid_elements(), 8 * w.rows * w.k)
 
 
 def traffic_stem(workload: str) -> str:
-    return {"pooled": "topk_pooled_select_pooled",
+    return {"pooled": "topk_pooled_select_pooled", "vocab": "topk_select_radix_vocab",
             "pool": "topk_block_pool_adverse"}.get(workload, f"topk_select_{workload}")
 
 
@@ -273,6 +277,21 @@ def make_case(name, dev, np, torch, api, workloads):
                   f"keep {POOL_KEEP}, {POOL_PINNED} pinned", "rows": rows, "n": n,
                   "group": POOL_GROUP, "keep": POOL_KEEP, "pinned": POOL_PINNED}
         cores_used = lambda cores: 1
+    elif name == "vocab":
+        vals = torch.empty((rows, k), dtype=torch.float32, device=dev)
+        idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+
+        def step(i):
+            api.topk_select_radix(inputs[i % len(inputs)][0], k, lengths, out=(vals, idx),
+                                  stream=stream)
+
+        def ref(x, ln, cores):
+            return oracle.topk(x, k, ln, threads=cores)
+
+        kernel = "radix_select_kernel"
+        metric = f"effective HBM read GB/s (and rows/s) for top-{k:,} of {n:,} fp32 scores/row"
+        config = {"workload": w.description, "rows": rows, "n": n, "k": k}
+        cores_used = lambda cores: cores
     else:
         vals = torch.empty((rows, k), dtype=torch.float32, device=dev)
         idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
@@ -314,9 +333,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="adverse",
-                    choices=["small", "outlier", "one_row", "adverse", "ragged", "pool", "pooled"],
+                    choices=["small", "outlier", "one_row", "adverse", "ragged", "pool", "pooled",
+                             "vocab"],
                     help="pool: topk_block_pool over the adverse rows (blocks of 8, keep 2,000, "
-                         "16 pinned); pooled: topk_pooled_select over 2,000-block pools")
+                         "16 pinned); pooled: topk_pooled_select over 2,000-block pools; "
+                         "vocab: topk_select_radix, top-4,096 of 129,000-score rows")
     ap.add_argument("--copies", type=int, default=0,
                     help="input copies to rotate over (0: enough for >= 1.5 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -190,6 +190,30 @@ int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, i
                     int32_t group, int32_t keep, int32_t pinned, float *out_vals,
                     int32_t *out_idx, void *stream);
 
+/* Largest k of topk_select_radix. */
+#define TOPK_MAX_K_RADIX 8192
+
+/*
+ * topk_select_radix -- the same result as topk_select (see the top of this
+ * file) for 1 <= k <= TOPK_MAX_K_RADIX, by an exact per-row radix selection
+ * instead of the streaming filter.  The pages test the selection up to
+ * vocabulary-sized rows and k = 1,000, and the page's own kernel stops near
+ * k = 4,000 ("The Secret GPU Kernel Behind DeepSeek V4.1 Flash", transcript
+ * 5:45 and 8:00-8:14); this entry point serves larger k.
+ *
+ * One workgroup per row: an evenly spread 8,192-score sample gives a
+ * threshold a little below the k-th score; one pass over the row copies
+ * every score at or above it into LDS; an 11-bit-digit radix selection in
+ * LDS finds the k-th (value, position) word exactly, and the winners are
+ * sorted in LDS.  When the sample's threshold admits fewer than k scores or
+ * more than the LDS holds, the row is instead narrowed digit by digit with
+ * passes over it.  Rows of any length and 4-byte alignment; nothing past a
+ * row's length is read.  Allocates nothing, launches one kernel; status
+ * codes as for topk_select (TOPK_EK_RANGE for k outside [1, 8192]).
+ */
+int topk_select_radix(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
+                      int32_t k, float *out_vals, int32_t *out_idx, void *stream);
+
 /* Most pool slots topk_pooled_select takes per row. */
 #define TOPK_MAX_POOL_SLOTS 8192
 

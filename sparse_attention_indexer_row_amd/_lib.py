@@ -26,6 +26,7 @@ TOPK_FLAG_NO_ESTIMATE = 1
 TOPK_FLAG_FORCE_RERUN = 2
 TOPK_MAX_SPLIT = 1024
 TOPK_MAX_POOL_SLOTS = 8192
+TOPK_MAX_K_RADIX = 8192
 
 # Every function the header declares, in header order.
 EXPORTS = (
@@ -36,6 +37,7 @@ EXPORTS = (
     "topk_select_ex",
     "topk_plan",
     "topk_block_pool",
+    "topk_select_radix",
     "topk_pooled_select",
     "topk_strerror",
     "topk_visit_order",
@@ -81,6 +83,7 @@ SIGNATURES = {
                                       ctypes.POINTER(TopkOptions), _vp, _sz, _vp]),
     "topk_plan": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(TopkOptions),
                                  ctypes.POINTER(TopkPlan)]),
+    "topk_select_radix": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "topk_block_pool": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "topk_pooled_select": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                           _vp]),

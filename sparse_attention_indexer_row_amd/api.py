@@ -150,6 +150,19 @@ def topk_plan(rows: int, n: int, k: int, *, split: int = 0, waves: int = 0,
     return {f: getattr(p, f) for f, _ in TopkPlan._fields_ if f != "reserved"}
 
 
+def topk_select_radix(scores: torch.Tensor, k: int, lengths: torch.Tensor | None = None,
+                      out=None, stream=None):
+    """Top-k by per-row radix selection, k up to 8,192 (values, int32 indices)."""
+    _check_scores(scores)
+    lp = _check_lengths(lengths, scores)
+    vals, idx = _outputs(scores, k, out)
+    rows, n = scores.shape
+    st = _lib.load().topk_select_radix(scores.data_ptr(), lp, rows, n, k, vals.data_ptr(),
+                                       idx.data_ptr(), _stream_handle(stream, scores.device))
+    _lib.check(st, "topk_select_radix")
+    return vals, idx
+
+
 def topk_block_pool(scores: torch.Tensor, group: int, keep: int, pinned: int,
                     lengths: torch.Tensor | None = None, out=None, stream=None):
     """Block-max pooled pre-selection: (block scores, int32 block indices) [rows][keep]."""

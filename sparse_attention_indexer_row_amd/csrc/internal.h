@@ -55,15 +55,17 @@ struct PoolArgs {
 
 hipError_t launch_block_max(const PoolArgs &a, hipStream_t stream);
 
-// Best `k` of each row of block maxima: an exact radix selection over the
-// rows' 64-bit (key, position) words, one workgroup per row.
+// Best `k` of each row: an exact radix selection over the rows' 64-bit
+// (key, position) words, one workgroup per row.
+constexpr int kRadixMaxK = 8192;
+
 struct RadixArgs {
-    const float *vals;         // [rows][ld], 16-byte aligned, ld a multiple of 4
-    const int32_t *count;      // [rows] valid elements per row (<= ld)
+    const float *vals;         // [rows][ld], any 4-byte alignment
+    const int32_t *count;      // [rows] valid elements per row (clamped to [0, ld]) or null (ld)
     int64_t ld;
     int32_t rows;              // rows handled by this launch
     int32_t row0;
-    int32_t k;                 // <= TOPK_MAX_K
+    int32_t k;                 // 1..kRadixMaxK
     float *out_vals;           // [rows][out_ld], first k slots of each row written
     int32_t *out_idx;
     int64_t out_ld;

@@ -224,10 +224,19 @@ __global__ __launch_bounds__(256) void pool_positions_kernel(PooledArgs a) {
 // order of any step.
 constexpr int kRadixThreads = 1024;
 constexpr int kRadixBins = 2048;
-constexpr int kRadixCand = 6144;
-constexpr int kRadixSel = 2048;
 constexpr int kRadixLevels = 6;
-constexpr size_t kRadixLds = kRadixBins * 4 + kRadixSel * 8 + kRadixCand * 8;
+
+// LDS capacities: SEL winners (>= k) and CAND candidates.  Lists up to
+// 2,048 take 72 KiB (two workgroups per compute unit); lists up to 8,192
+// take 158 KiB, the most one workgroup may have.
+template <int SEL, int CAND>
+struct RadixCap {
+    static constexpr int kSel = SEL;
+    static constexpr int kCand = CAND;
+    static constexpr size_t kLds = (size_t)kRadixBins * 4 + (size_t)(SEL + CAND) * 8;
+};
+using RadixSmall = RadixCap<2048, 6144>;
+using RadixLarge = RadixCap<8192, 11008>;
 
 __device__ __forceinline__ int radix_shift(int level) {
     // digits of 11, 11, 10 bits over the key, then over the position half
@@ -238,60 +247,99 @@ __device__ __forceinline__ uint64_t radix_word(float v, uint32_t i) {
     return pack_word(order_key(__float_as_uint(v)), i);
 }
 
-// Calls fn(word, valid) for every element of a row of m floats (16-byte
-// aligned start, readable up to m rounded up to 4): eight float4 loads in
-// flight per thread, neighbouring threads on neighbouring 16 bytes.  Every
-// lane of a wave makes the same calls (`valid` is false past the row), so
-// fn may use wave-wide ballots.
+// A row of m floats at any 4-byte alignment: `head` scalars up to the
+// first 16-byte boundary, `n4` aligned float4s, then `tail` scalars.
+// Nothing past the row is read.
+struct RowParts {
+    uint32_t head, n4, tail;
+    const float4 *body;
+};
+
+__device__ __forceinline__ RowParts row_parts(const float *row, uint32_t m) {
+    RowParts p;
+    const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(row) & 15u) / 4u;
+    p.head = mis ? 4u - mis : 0u;
+    if (p.head > m) p.head = m;
+    p.n4 = (m - p.head) / 4u;
+    p.tail = m - p.head - 4u * p.n4;
+    p.body = reinterpret_cast<const float4 *>(row + p.head);
+    return p;
+}
+
+// Calls fn(word, valid) once per thread for the head and tail scalars
+// (thread t takes the t-th of them; valid is false for the rest).
+template <class F>
+__device__ __forceinline__ void for_each_scalar(const float *row, RowParts p, F &&fn) {
+    const uint32_t t = threadIdx.x;
+    const uint32_t i = t < p.head ? t : p.head + 4u * p.n4 + (t - p.head);
+    const bool valid = t < p.head + p.tail;
+    float x = 0.f;
+    if (valid) x = row[i];
+    fn(radix_word(x, i), valid);
+}
+
+// Calls fn(word, valid) for every element of a row of m floats: eight
+// float4 loads in flight per thread, neighbouring threads on neighbouring
+// 16 bytes, the unaligned ends one scalar per thread.  Every lane of a wave
+// makes the same calls (`valid` is false where there is no element), so fn
+// may use wave-wide ballots.
 template <class F>
 __device__ __forceinline__ void for_each_word(const float *row, uint32_t m, F &&fn) {
     constexpr uint32_t U = 8;
     const uint32_t lane = threadIdx.x & (kWave - 1);
-    const float4 *r4 = reinterpret_cast<const float4 *>(row);
-    const uint32_t n4 = (m + 3u) / 4u;
-    for (uint32_t base = threadIdx.x; base - lane < n4; base += U * kRadixThreads) {
+    const RowParts p = row_parts(row, m);
+    for (uint32_t base = threadIdx.x; base - lane < p.n4; base += U * kRadixThreads) {
         float4 v[U];
 #pragma unroll
         for (uint32_t u = 0; u < U; ++u) {
             const uint32_t q = base + u * kRadixThreads;
-            v[u] = q < n4 ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[u] = q < p.n4 ? p.body[q] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (uint32_t u = 0; u < U; ++u) {
-            const uint32_t i = 4u * (base + u * kRadixThreads);
-            fn(radix_word(v[u].x, i), i < m);
-            fn(radix_word(v[u].y, i + 1), i + 1 < m);
-            fn(radix_word(v[u].z, i + 2), i + 2 < m);
-            fn(radix_word(v[u].w, i + 3), i + 3 < m);
+            const uint32_t q = base + u * kRadixThreads;
+            const uint32_t i = p.head + 4u * q;
+            const bool ok = q < p.n4;
+            fn(radix_word(v[u].x, i), ok);
+            fn(radix_word(v[u].y, i + 1), ok);
+            fn(radix_word(v[u].z, i + 2), ok);
+            fn(radix_word(v[u].w, i + 3), ok);
         }
     }
+    for_each_scalar(row, p, fn);
 }
 
 // Appends every word of the row with w >= lo to buf: per group of eight
 // float4 loads each thread counts its admitted words, one shuffle scan and
-// one atomic per wave place them, and the thread writes them at its offset.
-// Slots at or past `cap` are dropped; *counter still counts every word.
+// one atomic per wave place them, and the thread writes them at its offset
+// (the unaligned ends go through wave_append).  Slots at or past `cap` are
+// dropped; *counter still counts every word.
+__device__ __forceinline__ void wave_append(uint64_t *buf, uint32_t *counter, uint32_t cap,
+                                            uint64_t w, bool take);
+
 __device__ __forceinline__ void append_at_least(const float *row, uint32_t m, uint64_t lo,
                                                 uint64_t *buf, uint32_t *counter, uint32_t cap) {
     constexpr uint32_t U = 8;
     const uint32_t lane = threadIdx.x & (kWave - 1);
-    const float4 *r4 = reinterpret_cast<const float4 *>(row);
-    const uint32_t n4 = (m + 3u) / 4u;
-    for (uint32_t base = threadIdx.x; base - lane < n4; base += U * kRadixThreads) {
+    const RowParts p = row_parts(row, m);
+    for (uint32_t base = threadIdx.x; base - lane < p.n4; base += U * kRadixThreads) {
         float4 v[U];
 #pragma unroll
         for (uint32_t u = 0; u < U; ++u) {
             const uint32_t q = base + u * kRadixThreads;
-            v[u] = q < n4 ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[u] = q < p.n4 ? p.body[q] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         uint32_t mine = 0;
 #pragma unroll
         for (uint32_t u = 0; u < U; ++u) {
-            const uint32_t i = 4u * (base + u * kRadixThreads);
-            mine += (i < m && radix_word(v[u].x, i) >= lo);
-            mine += (i + 1 < m && radix_word(v[u].y, i + 1) >= lo);
-            mine += (i + 2 < m && radix_word(v[u].z, i + 2) >= lo);
-            mine += (i + 3 < m && radix_word(v[u].w, i + 3) >= lo);
+            const uint32_t q = base + u * kRadixThreads;
+            const uint32_t i = p.head + 4u * q;
+            if (q < p.n4) {
+                mine += radix_word(v[u].x, i) >= lo;
+                mine += radix_word(v[u].y, i + 1) >= lo;
+                mine += radix_word(v[u].z, i + 2) >= lo;
+                mine += radix_word(v[u].w, i + 3) >= lo;
+            }
         }
         // exclusive prefix of `mine` over the wave, and the wave's total
         uint32_t incl = mine;
@@ -308,18 +356,22 @@ __device__ __forceinline__ void append_at_least(const float *row, uint32_t m, ui
         if (mine == 0) continue;
 #pragma unroll
         for (uint32_t u = 0; u < U; ++u) {
-            const uint32_t i = 4u * (base + u * kRadixThreads);
+            const uint32_t q = base + u * kRadixThreads;
+            const uint32_t i = p.head + 4u * q;
             const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
             for (uint32_t c = 0; c < 4; ++c) {
                 const uint64_t w = radix_word(e[c], i + c);
-                if (i + c < m && w >= lo) {
+                if (q < p.n4 && w >= lo) {
                     if (at < cap) buf[at] = w;
                     ++at;
                 }
             }
         }
     }
+    for_each_scalar(row, p, [&](uint64_t w, bool valid) {
+        wave_append(buf, counter, cap, w, valid && w >= lo);
+    });
 }
 
 // Histogram increment with the wave's most common bins merged first: rows
@@ -437,7 +489,10 @@ constexpr uint32_t kSampleChunks = 128;
 constexpr uint32_t kSampleWords = kSampleChunks * kWave;
 constexpr uint32_t kEstimateMinRow = 4 * kSampleWords;
 
+template <class Cap>
 __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a) {
+    constexpr int kRadixSel = Cap::kSel;
+    constexpr int kRadixCand = Cap::kCand;
     extern __shared__ uint64_t lds[];
     uint64_t *sel = lds;                                  // kRadixSel
     uint64_t *cand = lds + kRadixSel;                     // kRadixCand
@@ -447,7 +502,7 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
     const int64_t r = (int64_t)a.row0 + blockIdx.x;
     const int tid = threadIdx.x;
     const uint32_t lane = (uint32_t)tid & (kWave - 1);
-    int64_t m64 = a.count[r];
+    int64_t m64 = a.count ? (int64_t)a.count[r] : a.ld;
     m64 = m64 < 0 ? 0 : (m64 > a.ld ? a.ld : m64);
     const uint32_t m = (uint32_t)m64;
     const uint32_t k = (uint32_t)a.k;
@@ -573,19 +628,26 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
 
 }  // namespace
 
-hipError_t launch_radix_select(const RadixArgs &a, hipStream_t stream) {
-    if (a.rows <= 0) return hipSuccess;
+template <class Cap>
+hipError_t launch_radix_cap(const RadixArgs &a, hipStream_t stream) {
     static bool raised = false;
     if (!raised) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&radix_select_kernel),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&radix_select_kernel<Cap>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)kRadixLds);
+                                           (int)Cap::kLds);
         if (e != hipSuccess) return e;
         raised = true;
     }
-    hipLaunchKernelGGL(radix_select_kernel, dim3((unsigned)a.rows), dim3(kRadixThreads), kRadixLds,
-                       stream, a);
+    hipLaunchKernelGGL(radix_select_kernel<Cap>, dim3((unsigned)a.rows), dim3(kRadixThreads),
+                       Cap::kLds, stream, a);
     return hipGetLastError();
+}
+
+hipError_t launch_radix_select(const RadixArgs &a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    if (a.k <= RadixSmall::kSel) return launch_radix_cap<RadixSmall>(a, stream);
+    if (a.k <= RadixLarge::kSel) return launch_radix_cap<RadixLarge>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_pool_order(const PooledArgs &a, hipStream_t stream) {

@@ -404,6 +404,31 @@ int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, i
     return TOPK_OK;
 }
 
+int topk_select_radix(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
+                      int32_t k, float *out_vals, int32_t *out_idx, void *stream) {
+    if (rows < 0 || n < 1) return TOPK_EINVAL;
+    if (k < 1 || k > TOPK_MAX_K_RADIX) return TOPK_EK_RANGE;
+    if (rows == 0) return TOPK_OK;
+    if (!scores || !out_vals || !out_idx) return TOPK_EINVAL;
+    if (misaligned(scores, 4) || misaligned(out_vals, 4) || misaligned(out_idx, 4) ||
+        (lengths && misaligned(lengths, 4)))
+        return TOPK_EINVAL;
+    topk::RadixArgs x{};
+    x.vals = scores;
+    x.count = lengths;
+    x.ld = n;
+    x.k = k;
+    x.out_vals = out_vals;
+    x.out_idx = out_idx;
+    x.out_ld = k;
+    for (int32_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
+        x.row0 = r0;
+        x.rows = std::min(kMaxGridRows, rows - r0);
+        if (topk::launch_radix_select(x, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
+    }
+    return TOPK_OK;
+}
+
 int topk_pooled_select(const float *pool_scores, const int32_t *pool_idx,
                        const int32_t *lengths, int32_t rows, int32_t n, int32_t group,
                        int32_t keep, int32_t k, float *out_vals, int32_t *out_idx,

@@ -20,6 +20,10 @@ Named workloads (rows x n, k):
   ragged    256 x 262,144, k=2048 lengths uniform in [1, 262,144], scores
                                     N(0,1) + 0.5*log1p(position), -inf padding
 
+Vocabulary-sized workload (``vocab``): 128 rows of 129,000 N(0,1) scores
+(the page's test file sweeps a vocabulary of 129,000, transcript 8:00) with
+k = 4,096, above the page's own kernel's limit of about 4,000 (5:45).
+
 Pooled workload (``pooled``): the rows an indexer above the pooling layer
 sees (transcript 7:22-7:46: blocks of 8 positions, 2,000 blocks kept, the
 newest pinned, about 16,000 candidates of a long context).  128 query rows
@@ -180,7 +184,13 @@ def pooled(seed: int = 106, rows: int = 128, n: int = 1 << 20, group: int = 8,
                           f"N(0,1) scores for the {keep * group:,} pooled positions, k={k}")
 
 
+def vocab(seed: int = 107, rows: int = 128, n: int = 129_000, k: int = 4096) -> Workload:
+    return Workload("vocab", normal_rows(rows, n, seed), None, k, seed,
+                    f"{rows} rows x {n:,} fp32 N(0,1), k={k:,}")
+
+
 WORKLOADS = {
+    "vocab": vocab,
     "small": small,
     "outlier": outlier,
     "one_row": one_row,

@@ -39,7 +39,7 @@ def test_constants_match_header():
     text = open(HEADER).read()
     for cname in ("TOPK_OK", "TOPK_EINVAL", "TOPK_EK_RANGE", "TOPK_EWORKSPACE", "TOPK_ESPLIT",
                   "TOPK_ELAUNCH", "TOPK_EDEVICE", "TOPK_EALLOC", "TOPK_MAX_K", "TOPK_MAX_SPLIT",
-                  "TOPK_MAX_POOL_SLOTS"):
+                  "TOPK_MAX_POOL_SLOTS", "TOPK_MAX_K_RADIX"):
         m = re.search(rf"#define {cname} \(?(-?\d+)\)?", text)
         assert m and int(m.group(1)) == getattr(_lib, cname), cname
 
@@ -126,6 +126,20 @@ def test_block_pool_argument_errors(lib, args, status):
 ])
 def test_pooled_select_argument_errors(lib, args, status):
     assert lib.topk_pooled_select(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, None, -1, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # rows < 0
+    ((FAKE, None, 1, 0, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),        # n < 1
+    ((FAKE, None, 1, 16, 0, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),     # k < 1
+    ((FAKE, None, 1, 16, 8193, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),  # k > 8192
+    ((None, None, 1, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),       # null scores
+    ((FAKE, None, 1, 16, 4, None, FAKE, None), _lib.TOPK_EINVAL),       # null out_vals
+    ((FAKE + 2, None, 1, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),   # misaligned scores
+    ((FAKE, None, 0, 16, 8192, None, None, None), _lib.TOPK_OK),        # no rows
+])
+def test_radix_argument_errors(lib, args, status):
+    assert lib.topk_select_radix(*args) == status
 
 
 def test_workspace_init_and_probe_argument_errors(lib):
