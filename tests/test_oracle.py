@@ -13,7 +13,9 @@ import pytest
 
 import oracle
 import oracle_pins
+import oracle_decode_pins
 import oracle_pool_pins
+from oracle import decode as decode_oracle
 from sparse_attention_indexer_row_amd import workloads
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +70,40 @@ def test_pooled_bad_arguments():
         oracle.pooled_topk(ps, pi, 2, 4, 8)
     pi[0, 2] = -1                                     # the NaN sits in an empty slot
     oracle.pooled_topk(ps, pi, 2, 4, 8)
+
+
+@pytest.mark.parametrize("pin", oracle_decode_pins.DECODE_PINS, ids=lambda p: p.__name__)
+def test_decode_pin(pin):
+    pin(decode_oracle.sparse_decode)
+
+
+DECODE_MUTANTS = {
+    "decode_no_scale": ("s = scale * (K @ q[r, h].astype(np.float64))",
+                        "s = (K @ q[r, h].astype(np.float64))"),
+    "decode_values_shifted": ("out[r, h] = p @ K[:, :dv]", "out[r, h] = p @ K[:, 1:dv + 1]"),
+    "decode_duplicates_once": ("sel = [int(j) for j in idx[r] if 0 <= int(j) < n]",
+                               "sel = sorted({int(j) for j in idx[r] if 0 <= int(j) < n})"),
+    "decode_keeps_out_of_range": ("if 0 <= int(j) < n]", "if 0 <= int(j)]"),
+    "decode_uniform_weights": ("p = w / w.sum()", "p = np.ones_like(w) / len(w)"),
+    "decode_first_head_query": ("q[r, h].astype", "q[r, 0].astype"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_MUTANTS))
+def test_decode_planted_mistake_is_caught(name):
+    old, new = DECODE_MUTANTS[name]
+    src = open(decode_oracle.__file__).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    ns = {}
+    exec(compile(src.replace(old, new), "decode_mutant", "exec"), ns)
+    caught = False
+    for pin in oracle_decode_pins.DECODE_PINS:
+        try:
+            pin(ns["sparse_decode"])
+        except Exception:
+            caught = True
+            break
+    assert caught, f"mutant {name} passed every pin"
 
 
 def _check_invariants(scores, lengths, k, vals, idx):
