@@ -217,6 +217,32 @@ int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, i
 int topk_select_radix(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
                       int32_t k, float *out_vals, int32_t *out_idx, void *stream);
 
+/*
+ * topk_sparse_decode -- attention over the selected positions only, the
+ * consumer of the indices ("The Secret GPU Kernel Behind DeepSeek V4.1
+ * Flash", transcript 1:48-2:13: the indexer chooses which positions the
+ * expensive attention reads; the third page's sparse-MLA decode kernel splits
+ * the top-k dimension and merges the parts by log-sum-exp).
+ *
+ *   q:   bf16 [rows][heads][dqk] (raw bits, 16-byte aligned)
+ *   kv:  bf16 [n_kv][dqk], one latent cache shared by every head (16-byte
+ *        aligned); a head's values are the first dv channels of each entry
+ *   idx: int32 [rows][k], the selected positions (e.g. topk_select's out_idx);
+ *        entries < 0 or >= n_kv select nothing, a repeated entry counts twice
+ *   out: fp32 [rows][heads][dv]:
+ *        out[r][h] = sum_j softmax_j(scale * q[r][h] . kv[j]) * kv[j][0:dv]
+ *        over the selected j; rows with nothing selected give zeros.
+ * Arithmetic: bf16 products summed in fp32 on MFMA; weights rounded to bf16
+ * for the value product (the running sums add the rounded weights).
+ * heads a multiple of 16; dqk a multiple of 16, <= 1024; dv a multiple of
+ * 64, <= min(dqk, 1024); 1 <= k <= TOPK_MAX_K_RADIX (TOPK_EK_RANGE
+ * otherwise); scale finite.  Partial results go to a library-owned,
+ * grow-only device buffer (same rules as topk_block_pool).
+ */
+int topk_sparse_decode(const void *q, const void *kv, const int32_t *idx, int32_t rows,
+                       int32_t heads, int64_t n_kv, int32_t k, int32_t dqk, int32_t dv,
+                       float scale, float *out, void *stream);
+
 /* Most pool slots topk_pooled_select takes per row. */
 #define TOPK_MAX_POOL_SLOTS 8192
 

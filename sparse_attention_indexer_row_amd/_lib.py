@@ -38,6 +38,7 @@ EXPORTS = (
     "topk_plan",
     "topk_block_pool",
     "topk_select_radix",
+    "topk_sparse_decode",
     "topk_pooled_select",
     "topk_strerror",
     "topk_visit_order",
@@ -84,6 +85,8 @@ SIGNATURES = {
     "topk_plan": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(TopkOptions),
                                  ctypes.POINTER(TopkPlan)]),
     "topk_select_radix": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "topk_sparse_decode": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, ctypes.c_int64, _i32, _i32,
+                                          _i32, ctypes.c_float, _vp, _vp]),
     "topk_block_pool": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "topk_pooled_select": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                           _vp]),

@@ -163,6 +163,32 @@ def topk_select_radix(scores: torch.Tensor, k: int, lengths: torch.Tensor | None
     return vals, idx
 
 
+def topk_sparse_decode(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, dv: int,
+                       scale: float, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Attention over selected positions: q bf16 [rows][heads][dqk], kv bf16 [n][dqk],
+    idx int32 [rows][k] -> fp32 [rows][heads][dv]."""
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
+        raise ValueError("q and kv must be bfloat16")
+    if q.dim() != 3 or kv.dim() != 2 or idx.dim() != 2 or idx.dtype != torch.int32:
+        raise ValueError("expected q [rows][heads][dqk], kv [n][dqk], idx int32 [rows][k]")
+    if not (q.is_cuda and kv.device == q.device and idx.device == q.device):
+        raise ValueError("q, kv and idx must be on one GPU")
+    if not (q.is_contiguous() and kv.is_contiguous() and idx.is_contiguous()):
+        raise ValueError("q, kv and idx must be contiguous")
+    rows, heads, dqk = q.shape
+    if kv.shape[1] != dqk or idx.shape[0] != rows:
+        raise ValueError("shape mismatch between q, kv and idx")
+    if out is None:
+        out = torch.empty((rows, heads, dv), dtype=torch.float32, device=q.device)
+    elif out.shape != (rows, heads, dv) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [rows][heads][dv] tensor")
+    st = _lib.load().topk_sparse_decode(q.data_ptr(), kv.data_ptr(), idx.data_ptr(), rows, heads,
+                                        kv.shape[0], idx.shape[1], dqk, dv, float(scale),
+                                        out.data_ptr(), _stream_handle(stream, q.device))
+    _lib.check(st, "topk_sparse_decode")
+    return out
+
+
 def topk_block_pool(scores: torch.Tensor, group: int, keep: int, pinned: int,
                     lengths: torch.Tensor | None = None, out=None, stream=None):
     """Block-max pooled pre-selection: (block scores, int32 block indices) [rows][keep]."""

@@ -1,0 +1,269 @@
+// Sparse-attention decode over the selected positions: the consumer of the
+// top-k indices ("The Secret GPU Kernel Behind DeepSeek V4.1 Flash",
+// transcript 1:48-2:13: the indexer picks which positions the expensive
+// attention reads; the third page's sparse-MLA decode kernel splits the
+// top-k dimension across workgroups and merges the parts by log-sum-exp).
+//
+// Layout (the pages give none): one latent cache kv[n][dqk] in bf16 shared
+// by every head, values = its first dv channels; queries q[rows][heads][dqk]
+// in bf16; idx[rows][k] from the selection (-1 and out-of-range entries
+// select nothing).
+//
+// decode_partial_kernel: workgroup (split s, 16-head group, row r), four
+// waves.  Its share of the row's selected positions is walked in tiles of
+// 32: the tile's cache rows are gathered into LDS (16-byte loads), the
+// scores S = Q K^T (16 heads x 32 positions) come from bf16 MFMA 16x16x16
+// with the dqk dimension spread over the four waves and summed through LDS,
+// an online softmax updates each head's running maximum and sum, and
+// O += P V runs on MFMA with each wave owning a quarter of the dv columns
+// (P rounded to bf16, and the running sum adds the rounded weights, so the
+// weights stay normalised).  The split writes (O, max, sum) per head.
+// decode_combine_kernel merges the splits by their log-sum-exp.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace topk {
+namespace {
+
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDecThreads = 256;
+constexpr int kDecTile = 32;       // selected positions per tile
+constexpr int kDecHeads = 16;      // heads per workgroup (MFMA rows)
+constexpr int kDecMaxSteps = kMaxDecodeDqk / 16 / 4;   // dqk steps per wave
+constexpr int kDecMaxVTiles = kMaxDecodeDv / 64;       // 16-column tiles per wave
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    // round to nearest even (weights are finite and non-negative)
+    const uint32_t b = __float_as_uint(x);
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int ldk = a.dqk + 8;  // padded row (16-byte multiple) against bank conflicts
+    uint16_t *kt = reinterpret_cast<uint16_t *>(smem);                        // [32][ldk]
+    float *sred = reinterpret_cast<float *>(smem + (size_t)kDecTile * ldk * 2);  // [4][16][32]
+    uint16_t *pw = reinterpret_cast<uint16_t *>(sred + 4 * kDecHeads * kDecTile);  // [16][32]
+    float *alpha = reinterpret_cast<float *>(pw + kDecHeads * kDecTile);       // [16]
+    float *mrun = alpha + kDecHeads;
+    float *lrun = mrun + kDecHeads;
+    __shared__ int32_t pos[kDecTile];
+
+    const int s = blockIdx.x;
+    const int h0 = blockIdx.y * kDecHeads;
+    const int64_t r = (int64_t)a.row0 + blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int col16 = lane & 15, grp = lane >> 4;
+    const int t0 = s * a.per_split;
+    const int t1 = min(a.k, t0 + a.per_split);
+    const int nks = a.dqk / 16;
+    const int nvt = a.dv / 64;
+
+    // This wave's query operands: k-steps ks = wv, wv + 4, ... (A layout:
+    // lane holds row col16, k = 4 grp .. 4 grp + 3 of the step).
+    bf16x4_t qa[kDecMaxSteps];
+    const uint16_t *qrow = a.q + ((size_t)r * a.heads + h0 + col16) * a.dqk;
+#pragma unroll
+    for (int i = 0; i < kDecMaxSteps; ++i) {
+        const int ks = wv + 4 * i;
+        bf16x4_t v = {0, 0, 0, 0};
+        if (ks < nks) v = *reinterpret_cast<const bf16x4_t *>(qrow + ks * 16 + grp * 4);
+        qa[i] = v;
+    }
+    f32x4_t acc[kDecMaxVTiles];
+#pragma unroll
+    for (int i = 0; i < kDecMaxVTiles; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (tid < kDecHeads) {
+        mrun[tid] = -__builtin_inff();
+        lrun[tid] = 0.f;
+    }
+
+    for (int tb = t0; tb < t1; tb += kDecTile) {
+        if (tid < kDecTile) {
+            const int t = tb + tid;
+            int32_t j = -1;
+            if (t < t1) {
+                j = a.idx[(size_t)r * a.k + t];
+                if (j < 0 || (int64_t)j >= a.n_kv) j = -1;
+            }
+            pos[tid] = j;
+        }
+        __syncthreads();
+        // gather the tile's cache rows (zeros for empty slots)
+        const int cpr = a.dqk / 8;
+        for (int c = tid; c < kDecTile * cpr; c += kDecThreads) {
+            const int row = c / cpr, cc = c - row * cpr;
+            const int32_t j = pos[row];
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (j >= 0) v = *reinterpret_cast<const uint4 *>(a.kv + (size_t)j * a.dqk + cc * 8);
+            *reinterpret_cast<uint4 *>(kt + row * ldk + cc * 8) = v;
+        }
+        __syncthreads();
+        // partial scores over this wave's k-steps (B layout: lane holds
+        // column col16 of the n-tile, k = 4 grp .. 4 grp + 3)
+        f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int i = 0; i < kDecMaxSteps; ++i) {
+            const int ks = wv + 4 * i;
+            if (ks < nks) {
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const bf16x4_t b = *reinterpret_cast<const bf16x4_t *>(
+                        kt + (nt * 16 + col16) * ldk + ks * 16 + grp * 4);
+                    sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qa[i], b, sacc[nt], 0, 0, 0);
+                }
+            }
+        }
+        // D layout: lane holds rows 4 grp + e, column col16
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sred[(wv * kDecHeads + grp * 4 + e) * kDecTile + nt * 16 + col16] = sacc[nt][e];
+            }
+        }
+        __syncthreads();
+        // online softmax: 16 threads per head (one 16-lane group), two
+        // positions each
+        {
+            const int hh = tid >> 4, c0 = (tid & 15) * 2;
+            float sv[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int c = c0 + e;
+                float x = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) x += sred[(w * kDecHeads + hh) * kDecTile + c];
+                sv[e] = pos[c] >= 0 ? x * a.scale : -__builtin_inff();
+            }
+            float mx = fmaxf(sv[0], sv[1]);
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            const float mold = mrun[hh];
+            const float mnew = fmaxf(mold, mx);
+            float al = 1.f, p[2] = {0.f, 0.f};
+            if (mnew != -__builtin_inff()) {
+                al = expf(mold - mnew);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    if (sv[e] != -__builtin_inff()) p[e] = from_bf16(to_bf16(expf(sv[e] - mnew)));
+                }
+            }
+            float ps = p[0] + p[1];
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+            pw[hh * kDecTile + c0] = to_bf16(p[0]);
+            pw[hh * kDecTile + c0 + 1] = to_bf16(p[1]);
+            if ((tid & 15) == 0) {
+                mrun[hh] = mnew;
+                lrun[hh] = lrun[hh] * al + ps;
+                alpha[hh] = al;
+            }
+        }
+        __syncthreads();
+        // O = alpha O + P V over this wave's column tiles
+        float al[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) al[e] = alpha[grp * 4 + e];
+#pragma unroll
+        for (int nt = 0; nt < kDecMaxVTiles; ++nt) {
+            if (nt < nvt) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[nt][e] *= al[e];
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < kDecTile / 16; ++kk) {
+            const bf16x4_t pa = *reinterpret_cast<const bf16x4_t *>(pw + col16 * kDecTile + kk * 16 + grp * 4);
+#pragma unroll
+            for (int nt = 0; nt < kDecMaxVTiles; ++nt) {
+                if (nt < nvt) {
+                    const int col = wv * (a.dv / 4) + nt * 16 + col16;
+                    const uint16_t *vp = kt + (kk * 16 + grp * 4) * ldk + col;
+                    const bf16x4_t b = {(short)vp[0], (short)vp[ldk], (short)vp[2 * ldk],
+                                        (short)vp[3 * ldk]};
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, b, acc[nt], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // this split's (O, max, sum) per head
+#pragma unroll
+    for (int nt = 0; nt < kDecMaxVTiles; ++nt) {
+        if (nt < nvt) {
+            const int col = wv * (a.dv / 4) + nt * 16 + col16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int head = h0 + grp * 4 + e;
+                a.part_o[(((size_t)r * a.heads + head) * a.splits + s) * a.dv + col] = acc[nt][e];
+            }
+        }
+    }
+    if (tid < kDecHeads) {
+        float *ml = a.part_ml + (((size_t)r * a.heads + h0 + tid) * a.splits + s) * 2;
+        ml[0] = mrun[tid];
+        ml[1] = lrun[tid];
+    }
+}
+
+// One workgroup per (row, head): out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s.
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+    const int64_t rh = blockIdx.x;   // r * heads + h
+    const float *ml = a.part_ml + (size_t)rh * a.splits * 2;
+    float M = -__builtin_inff();
+    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, ml[2 * s]);
+    float *out = a.out + (size_t)rh * a.dv;
+    if (M == -__builtin_inff()) {
+        for (int c = threadIdx.x; c < a.dv; c += blockDim.x) out[c] = 0.f;
+        return;
+    }
+    float L = 0.f;
+    for (int s = 0; s < a.splits; ++s) L += expf(ml[2 * s] - M) * ml[2 * s + 1];
+    const float inv = 1.f / L;
+    const float *po = a.part_o + (size_t)rh * a.splits * a.dv;
+    for (int c = threadIdx.x; c < a.dv; c += blockDim.x) {
+        float o = 0.f;
+        for (int s = 0; s < a.splits; ++s) o += expf(ml[2 * s] - M) * po[(size_t)s * a.dv + c];
+        out[c] = o * inv;
+    }
+}
+
+}  // namespace
+
+size_t decode_lds_bytes(int dqk) {
+    return (size_t)kDecTile * (dqk + 8) * 2 + (size_t)4 * kDecHeads * kDecTile * 4 +
+           (size_t)kDecHeads * kDecTile * 2 + 3 * kDecHeads * 4;
+}
+
+hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    static bool raised = false;
+    if (!raised) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_partial_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)decode_lds_bytes(kMaxDecodeDqk));
+        if (e != hipSuccess) return e;
+        raised = true;
+    }
+    const dim3 grid((unsigned)a.splits, (unsigned)(a.heads / kDecHeads), (unsigned)a.rows);
+    hipLaunchKernelGGL(decode_partial_kernel, grid, dim3(kDecThreads), decode_lds_bytes(a.dqk),
+                       stream, a);
+    return hipGetLastError();
+}
+
+// Combines every row of the call (a.rows is the total; row0 unused).
+hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((int64_t)a.rows * a.heads)), dim3(256),
+                       0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace topk

@@ -97,6 +97,33 @@ struct PooledArgs {
 hipError_t launch_pool_order(const PooledArgs &a, hipStream_t stream);
 hipError_t launch_pool_positions(const PooledArgs &a, hipStream_t stream);
 
+// Sparse-attention decode over selected positions.
+constexpr int kMaxDecodeDqk = 1024;
+constexpr int kMaxDecodeDv = 1024;
+
+struct DecodeArgs {
+    const uint16_t *q;         // [rows][heads][dqk] bf16 bits, 16-byte aligned
+    const uint16_t *kv;        // [n_kv][dqk] bf16 bits, 16-byte aligned; values = first dv
+    const int32_t *idx;        // [rows][k]
+    int64_t n_kv;
+    int32_t rows;              // rows of this launch (partial kernel: grid z)
+    int32_t row0;              // first row of this launch
+    int32_t heads;             // multiple of 16
+    int32_t k;
+    int32_t dqk;               // multiple of 16, <= kMaxDecodeDqk
+    int32_t dv;                // multiple of 64, <= min(dqk, kMaxDecodeDv)
+    int32_t splits;            // workgroups per (row, 16 heads) along the k selected positions
+    int32_t per_split;         // positions per split, a multiple of 32
+    float scale;
+    float *part_o;             // [rows][heads][splits][dv]
+    float *part_ml;            // [rows][heads][splits][2] running max, sum
+    float *out;                // [rows][heads][dv]
+};
+
+size_t decode_lds_bytes(int dqk);
+hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream);
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);

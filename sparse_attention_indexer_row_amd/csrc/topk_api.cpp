@@ -239,6 +239,8 @@ int internal_workspace(size_t need, hipStream_t stream, void **out) {
 
 // Block maxima and older-block counts of topk_block_pool.
 DeviceBuffers g_pool;
+// Per-split partial results of topk_sparse_decode.
+DeviceBuffers g_decode;
 
 // Block-maxima rows hold ceil(n / group) floats padded to whole 256-byte
 // lines, so every row starts aligned.
@@ -438,6 +440,62 @@ int topk_select_radix(const float *scores, const int32_t *lengths, int32_t rows,
         x.rows = std::min(kMaxGridRows, rows - r0);
         if (topk::launch_radix_select(x, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
     }
+    return TOPK_OK;
+}
+
+int topk_sparse_decode(const void *q, const void *kv, const int32_t *idx, int32_t rows,
+                       int32_t heads, int64_t n_kv, int32_t k, int32_t dqk, int32_t dv,
+                       float scale, float *out, void *stream) {
+    if (rows < 0 || heads < 16 || heads % 16 != 0 || n_kv < 1 || dqk < 16 || dqk % 16 != 0 ||
+        dqk > topk::kMaxDecodeDqk || dv < 64 || dv % 64 != 0 || dv > dqk ||
+        dv > topk::kMaxDecodeDv || !(scale == scale))
+        return TOPK_EINVAL;
+    if (k < 1 || k > TOPK_MAX_K_RADIX) return TOPK_EK_RANGE;
+    if ((int64_t)rows * heads > INT32_MAX) return TOPK_EINVAL;
+    if (rows == 0) return TOPK_OK;
+    if (!q || !kv || !idx || !out) return TOPK_EINVAL;
+    if (misaligned(q, 16) || misaligned(kv, 16) || misaligned(idx, 4) || misaligned(out, 4))
+        return TOPK_EINVAL;
+    int cus = 0;
+    int st = device_cus(&cus);
+    if (st != TOPK_OK) return st;
+    // Split the selected positions so that about two workgroups per compute
+    // unit run, in multiples of 32 positions.
+    const int64_t groups = (int64_t)rows * (heads / 16);
+    int64_t splits = (2 * (int64_t)cus + groups - 1) / groups;
+    const int64_t tiles = (k + 31) / 32;
+    if (splits > tiles) splits = tiles;
+    if (splits < 1) splits = 1;
+    const int32_t per_split = (int32_t)(((tiles + splits - 1) / splits) * 32);
+    splits = (k + per_split - 1) / per_split;
+    const size_t part_o = align_up((size_t)rows * heads * splits * dv * 4, kAlign);
+    const size_t part_ml = (size_t)rows * heads * splits * 2 * 4;
+    void *scratch = nullptr;
+    st = grow_buffer(g_decode, part_o + part_ml, false, (hipStream_t)stream, &scratch);
+    if (st != TOPK_OK) return st;
+    topk::DecodeArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.kv = static_cast<const uint16_t *>(kv);
+    a.idx = idx;
+    a.n_kv = n_kv;
+    a.heads = heads;
+    a.k = k;
+    a.dqk = dqk;
+    a.dv = dv;
+    a.splits = (int32_t)splits;
+    a.per_split = per_split;
+    a.scale = scale;
+    a.part_o = static_cast<float *>(scratch);
+    a.part_ml = reinterpret_cast<float *>(static_cast<char *>(scratch) + part_o);
+    a.out = out;
+    for (int32_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
+        a.row0 = r0;
+        a.rows = std::min(kMaxGridRows, rows - r0);
+        if (topk::launch_decode_partial(a, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
+    }
+    a.row0 = 0;
+    a.rows = rows;
+    if (topk::launch_decode_combine(a, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
     return TOPK_OK;
 }
 

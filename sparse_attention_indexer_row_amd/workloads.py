@@ -189,6 +189,39 @@ def vocab(seed: int = 107, rows: int = 128, n: int = 129_000, k: int = 4096) -> 
                     f"{rows} rows x {n:,} fp32 N(0,1), k={k:,}")
 
 
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16 (ties to even), as float32."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return b.astype(np.uint32).view(np.float32)
+
+
+@dataclass
+class DecodeWorkload:
+    name: str
+    q: np.ndarray       # float32 [rows][heads][dqk], values exact in bfloat16
+    kv: np.ndarray      # float32 [n][dqk], values exact in bfloat16
+    idx: np.ndarray     # int32 [rows][k]
+    dv: int
+    scale: float
+    seed: int
+    description: str
+
+
+def decode(seed: int = 108, rows: int = 128, heads: int = 16, n: int = 1 << 20, k: int = 512,
+           dqk: int = 576, dv: int = 512) -> DecodeWorkload:
+    """Sparse-attention decode inputs: N(0,1) queries and cache entries rounded
+    to bfloat16, k distinct positions per row drawn uniformly (standing in for
+    the indexer's picks), softmax scale 1/sqrt(dqk)."""
+    g = _rng(seed)
+    q = bf16_round(g.standard_normal((rows, heads, dqk)).astype(np.float32))
+    kv = bf16_round(g.standard_normal((n, dqk)).astype(np.float32))
+    idx = np.stack([g.choice(n, size=k, replace=False) for _ in range(rows)]).astype(np.int32)
+    return DecodeWorkload("decode", q, kv, idx, dv, float(1.0 / np.sqrt(dqk)), seed,
+                          f"{rows} rows x {heads} heads, dqk={dqk}, dv={dv}, latent cache of "
+                          f"{n:,} entries (bf16), k={k} selected positions per row")
+
+
 WORKLOADS = {
     "vocab": vocab,
     "small": small,

@@ -142,6 +142,32 @@ def test_radix_argument_errors(lib, args, status):
     assert lib.topk_select_radix(*args) == status
 
 
+def test_sparse_decode_argument_errors(lib):
+    import ctypes as C
+    f = lib.topk_sparse_decode
+    ok = dict(q=FAKE, kv=FAKE, idx=FAKE, rows=2, heads=16, n=100, k=8, dqk=64, dv=64, scale=0.5,
+              out=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["kv"], a["idx"], a["rows"], a["heads"], a["n"], a["k"], a["dqk"],
+                 a["dv"], C.c_float(a["scale"]), a["out"], None)
+
+    assert call(rows=-1) == _lib.TOPK_EINVAL
+    assert call(heads=8) == _lib.TOPK_EINVAL           # not a multiple of 16
+    assert call(n=0) == _lib.TOPK_EINVAL
+    assert call(dqk=72) == _lib.TOPK_EINVAL            # not a multiple of 16
+    assert call(dqk=2048, dv=64) == _lib.TOPK_EINVAL   # dqk above 1024
+    assert call(dv=96) == _lib.TOPK_EINVAL             # not a multiple of 64
+    assert call(dqk=64, dv=128) == _lib.TOPK_EINVAL    # dv above dqk
+    assert call(scale=float("nan")) == _lib.TOPK_EINVAL
+    assert call(k=0) == _lib.TOPK_EK_RANGE
+    assert call(k=8193) == _lib.TOPK_EK_RANGE
+    assert call(q=None) == _lib.TOPK_EINVAL
+    assert call(kv=FAKE + 8) == _lib.TOPK_EINVAL       # not 16-byte aligned
+    assert call(rows=0, q=None, kv=None, idx=None, out=None) == _lib.TOPK_OK
+
+
 def test_workspace_init_and_probe_argument_errors(lib):
     assert lib.topk_workspace_init(None, 256, None) == _lib.TOPK_EWORKSPACE
     assert lib.topk_workspace_init(FAKE + 16, 256, None) == _lib.TOPK_EWORKSPACE

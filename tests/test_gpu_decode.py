@@ -1,0 +1,117 @@
+"""GPU parity of topk_sparse_decode against the float64 oracle.
+
+Tolerance, from the arithmetic: the kernel multiplies bf16 inputs exactly
+and sums in fp32, so the scores carry errors far below 1e-4; the softmax
+weights are rounded to bf16 (relative error at most 2^-9 each) before the
+value product, and the running sum adds the rounded weights, so the output
+is a convex combination whose weights differ from the exact ones by at most
+about 2^-8 in total.  Each output therefore lies within 2^-8 * max|v| of the
+exact one, where max|v| is the largest magnitude among the selected value
+channels of that row; the test allows twice that (2^-7 * max|v|) plus 1e-6.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as H
+from oracle.decode import sparse_decode
+from sparse_attention_indexer_row_amd import api, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    H.require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def run(q, kv, idx, dv, scale, kv_dev=None):
+    qd = torch.from_numpy(q).to("cuda", dtype=torch.bfloat16)
+    kd = kv_dev if kv_dev is not None else torch.from_numpy(kv).to("cuda", dtype=torch.bfloat16)
+    out = api.topk_sparse_decode(qd, kd, torch.from_numpy(idx).to("cuda"), dv, scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(q, kv, idx, dv, scale, what="", rows=None, kv_dev=None):
+    print(f"[case] decode {what} q={q.shape} kv={kv.shape} k={idx.shape[1]} dv={dv} "
+          f"scale={scale}", flush=True)
+    got = run(q, kv, idx, dv, scale, kv_dev)
+    sample = range(q.shape[0]) if rows is None else rows
+    for r in sample:
+        want = sparse_decode(q[r:r + 1], kv, idx[r:r + 1], scale, dv)[0]
+        sel = [int(j) for j in idx[r] if 0 <= int(j) < kv.shape[0]]
+        vmax = float(np.abs(kv[sel, :dv]).max()) if sel else 0.0
+        err = float(np.abs(got[r] - want).max())
+        assert err <= 2.0 ** -7 * vmax + 1e-6, f"{what}: row {r} error {err} (max|v| {vmax})"
+
+
+def test_decode_workload_sampled_rows():
+    w = workloads.decode()
+    rows = [0, 1, 17, 64, 127]
+    check(w.q, w.kv, w.idx, w.dv, w.scale, what="decode workload", rows=rows)
+
+
+@pytest.mark.parametrize("k", [1, 2, 31, 32, 33, 100, 512, 1000, 2048])
+def test_selected_counts(k):
+    g = np.random.Generator(np.random.PCG64(k))
+    n, dqk, dv = 5000, 576, 512
+    q = workloads.bf16_round(g.standard_normal((3, 16, dqk)).astype(np.float32))
+    kv = workloads.bf16_round(g.standard_normal((n, dqk)).astype(np.float32))
+    idx = np.stack([g.choice(n, size=k, replace=False) for _ in range(3)]).astype(np.int32)
+    check(q, kv, idx, dv, 1.0 / 24.0, what=f"k={k}")
+
+
+@pytest.mark.parametrize("heads,dqk,dv", [(16, 64, 64), (32, 64, 64), (16, 128, 128),
+                                          (48, 576, 512), (16, 1024, 1024), (16, 1024, 64)])
+def test_shapes(heads, dqk, dv):
+    g = np.random.Generator(np.random.PCG64(heads * dqk + dv))
+    n = 3000
+    q = workloads.bf16_round(g.standard_normal((4, heads, dqk)).astype(np.float32))
+    kv = workloads.bf16_round(g.standard_normal((n, dqk)).astype(np.float32))
+    idx = np.stack([g.choice(n, size=200, replace=False) for _ in range(4)]).astype(np.int32)
+    check(q, kv, idx, dv, float(1.0 / np.sqrt(dqk)), what=f"heads={heads} dqk={dqk} dv={dv}")
+
+
+def test_filler_out_of_range_duplicates_and_empty_rows():
+    g = np.random.Generator(np.random.PCG64(5))
+    n, dqk, dv = 1000, 128, 64
+    q = workloads.bf16_round(g.standard_normal((5, 16, dqk)).astype(np.float32))
+    kv = workloads.bf16_round(g.standard_normal((n, dqk)).astype(np.float32))
+    idx = g.integers(0, n, size=(5, 70)).astype(np.int32)   # repeats allowed
+    idx[0, 40:] = -1                                         # the selection's filler
+    idx[1, ::3] = n + 5                                      # out of range: skipped
+    idx[2, :] = -1                                           # nothing selected: zeros
+    idx[3, :] = 7                                            # one position, 70 times
+    check(q, kv, idx, dv, 0.3, what="filler and repeats")
+    out = run(q, kv, idx, dv, 0.3)
+    assert np.all(out[2] == 0.0)
+
+
+def test_scales_flat_and_peaked():
+    g = np.random.Generator(np.random.PCG64(6))
+    n, dqk, dv = 2000, 256, 128
+    q = workloads.bf16_round(g.standard_normal((2, 16, dqk)).astype(np.float32))
+    kv = workloads.bf16_round(g.standard_normal((n, dqk)).astype(np.float32))
+    idx = np.stack([g.choice(n, size=300, replace=False) for _ in range(2)]).astype(np.int32)
+    check(q, kv, idx, dv, 0.0, what="scale 0 (mean)")
+    check(q, kv, idx, dv, 2.0, what="peaked softmax")
+
+
+def test_many_rows_and_one_row():
+    # one row spreads its positions over many splits; 600 rows use one each
+    g = np.random.Generator(np.random.PCG64(8))
+    n, dqk, dv = 4000, 576, 512
+    kv = workloads.bf16_round(g.standard_normal((n, dqk)).astype(np.float32))
+    kvd = torch.from_numpy(kv).to("cuda", dtype=torch.bfloat16)
+    q1 = workloads.bf16_round(g.standard_normal((1, 16, dqk)).astype(np.float32))
+    i1 = g.choice(n, size=2048, replace=False).astype(np.int32)[None, :]
+    check(q1, kv, i1, dv, 1.0 / 24.0, what="one row, k=2048", kv_dev=kvd)
+    qm = workloads.bf16_round(g.standard_normal((600, 16, dqk)).astype(np.float32))
+    im = np.stack([g.choice(n, size=64, replace=False) for _ in range(600)]).astype(np.int32)
+    check(qm, kv, im, dv, 1.0 / 24.0, what="600 rows", rows=[0, 299, 599], kv_dev=kvd)
