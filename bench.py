@@ -35,6 +35,7 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 SELECT_SOURCES = ["select_kernel.hip", "common.h", "wave_sort.h", "internal.h"]
 KERNEL_SOURCES = {
     "vocab": ["pool_kernel.hip", "common.h", "internal.h"],
+    "decode": ["decode_kernel.hip", "common.h", "internal.h"],
     "pool": SELECT_SOURCES + ["pool_kernel.hip"],
     "pooled": SELECT_SOURCES + ["pool_kernel.hip"],
 }
@@ -53,6 +54,11 @@ def profile_target(workload: str):
     """(summary file stem, kernels one call launches, algorithmic read bytes,
     algorithmic write bytes) of a bench workload; host only, no GPU."""
     from sparse_attention_indexer_row_amd import workloads
+    if workload == "decode":
+        w = workloads.decode()
+        rows, heads, dqk = w.q.shape
+        return (traffic_stem(workload), ["decode_partial_kernel", "decode_combine_kernel"],
+                decode_read_bytes(w), 4 * rows * heads * w.dv)
     if workload == "pooled":
         w = workloads.pooled()
         return (traffic_stem(workload),
@@ -69,8 +75,16 @@ def profile_target(workload: str):
     return (traffic_stem(workload), ["select_kernel"], 4 * w.valid_elements(), 8 * w.rows * w.k)
 
 
+def decode_read_bytes(w) -> int:
+    """Algorithmic bytes a decode call reads: each selected cache row once
+    (bf16), the queries and the indices."""
+    rows, heads, dqk = w.q.shape
+    return 2 * w.idx.size * dqk + 2 * w.q.size + 4 * w.idx.size
+
+
 def traffic_stem(workload: str) -> str:
     return {"pooled": "topk_pooled_select_pooled", "vocab": "topk_select_radix_vocab",
+            "decode": "topk_sparse_decode_decode",
             "pool": "topk_block_pool_adverse"}.get(workload, f"topk_select_{workload}")
 
 
@@ -213,6 +227,46 @@ def make_case(name, dev, np, torch, api, workloads):
         copies = max(2, -(-(3 << 29) // batch_bytes))
         return [base_list] + [[t.clone() for t in base_list] for _ in range(copies - 1)], copies
 
+    if name == "decode":
+        from oracle.decode import sparse_decode
+        w = workloads.decode()
+        rows, heads, dqk = w.q.shape
+        q = torch.from_numpy(w.q).to(dev, dtype=torch.bfloat16)
+        kv = torch.from_numpy(w.kv).to(dev, dtype=torch.bfloat16)
+        idx = torch.from_numpy(w.idx).to(dev)
+        out = torch.empty((rows, heads, w.dv), dtype=torch.float32, device=dev)
+
+        def step(i):
+            api.topk_sparse_decode(q, kv, idx, w.dv, w.scale, out=out, stream=stream)
+
+        sample = [0, 1, rows // 2, rows - 1]
+
+        def parity():
+            got = out.cpu().numpy()
+            ok = True
+            for r in sample:
+                want = sparse_decode(w.q[r:r + 1], w.kv, w.idx[r:r + 1], w.scale, w.dv)[0]
+                vmax = float(np.abs(w.kv[w.idx[r], :w.dv]).max())
+                ok = ok and float(np.abs(got[r] - want).max()) <= 2.0 ** -7 * vmax + 1e-6
+            return ok, sample
+
+        def cpu(cores):
+            t0 = time.perf_counter()
+            sparse_decode(w.q[:8], w.kv, w.idx[:8], w.scale, w.dv)
+            dt = time.perf_counter() - t0
+            return dt, decode_read_bytes(w) * 8 // rows, "8 of the rows (float64 numpy)"
+
+        c.update(rows=rows, read_bytes=decode_read_bytes(w), copies=1, step=step, parity=parity,
+                 cpu=cpu, cpu_cores=lambda cores: 1,
+                 kernel="decode_partial_kernel + decode_combine_kernel (whole call)",
+                 parity_kind="within 2^-7 max|v| of the float64 oracle",
+                 metric="effective HBM read GB/s of gathered bf16 cache rows for sparse-attention "
+                        "decode over 512 selected positions (16 heads, dqk 576, dv 512)",
+                 config={"workload": w.description, "rows": rows, "heads": heads, "dqk": dqk,
+                         "dv": w.dv, "k": int(w.idx.shape[1])})
+        c["set_copies"] = lambda m: None
+        return c
+
     if name == "pooled":
         w = workloads.pooled()
         base = [torch.from_numpy(w.pool_scores).to(dev), torch.from_numpy(w.pool_idx).to(dev)]
@@ -334,10 +388,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="adverse",
                     choices=["small", "outlier", "one_row", "adverse", "ragged", "pool", "pooled",
-                             "vocab"],
+                             "vocab", "decode"],
                     help="pool: topk_block_pool over the adverse rows (blocks of 8, keep 2,000, "
                          "16 pinned); pooled: topk_pooled_select over 2,000-block pools; "
-                         "vocab: topk_select_radix, top-4,096 of 129,000-score rows")
+                         "vocab: topk_select_radix, top-4,096 of 129,000-score rows; "
+                         "decode: topk_sparse_decode over 512 selected positions per row")
     ap.add_argument("--copies", type=int, default=0,
                     help="input copies to rotate over (0: enough for >= 1.5 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -382,7 +437,8 @@ def main() -> int:
         step(0)
         torch.cuda.synchronize()
         ok, sample = case["parity"]()
-        parity = f"bit-exact vs oracle on rows {sample}" if ok else "MISMATCH"
+        parity = (f"{case.get('parity_kind', 'bit-exact vs oracle')} on rows {sample}" if ok
+                  else "MISMATCH")
         if not ok:
             print("[bench] parity mismatch against the oracle", file=sys.stderr)
 
