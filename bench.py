@@ -32,12 +32,12 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 # Sources each bench path's kernels are built from; a traffic summary is
 # stale once any of them changes.
-SELECT_SOURCES = ["select_kernel.hip", "common.h", "wave_sort.h", "internal.h"]
+SELECT_SOURCES = ["select_kernel.hip", "common.h", "wave_sort.h", "select_args.h"]
 KERNEL_SOURCES = {
-    "vocab": ["pool_kernel.hip", "common.h", "internal.h"],
-    "decode": ["decode_kernel.hip", "common.h", "internal.h"],
-    "pool": SELECT_SOURCES + ["pool_kernel.hip"],
-    "pooled": SELECT_SOURCES + ["pool_kernel.hip"],
+    "vocab": ["pool_kernel.hip", "common.h", "internal.h", "select_args.h"],
+    "decode": ["decode_kernel.hip", "common.h", "internal.h", "select_args.h"],
+    "pool": SELECT_SOURCES + ["pool_kernel.hip", "internal.h"],
+    "pooled": SELECT_SOURCES + ["pool_kernel.hip", "internal.h"],
 }
 
 

@@ -41,7 +41,7 @@
 //     to zero (an accumulator that is never reset is the failure the
 //     kernelbench.com "DeepSeek V4.1 Flash" Kimi-Linear paragraph describes).
 #include "common.h"
-#include "internal.h"
+#include "select_args.h"
 #include "wave_sort.h"
 
 namespace topk {
