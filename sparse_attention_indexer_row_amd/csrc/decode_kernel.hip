@@ -33,8 +33,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kDecThreads = 256;
 constexpr int kDecTile = 32;       // selected positions per tile
 constexpr int kDecHeads = 16;      // heads per workgroup (MFMA rows)
-constexpr int kDecMaxSteps = kMaxDecodeDqk / 16 / 4;   // dqk steps per wave
-constexpr int kDecMaxVTiles = kMaxDecodeDv / 64;       // 16-column tiles per wave
+// Register arrays are sized per instantiation: MS dqk steps and MV
+// 16-column value tiles per wave.  The compact one covers dqk <= 576 and
+// dv <= 512 (the MLA shape); the general one the limits.
+constexpr int kDecStepsSmall = 576 / 16 / 4, kDecVTilesSmall = 512 / 64;
+constexpr int kDecStepsMax = kMaxDecodeDqk / 16 / 4, kDecVTilesMax = kMaxDecodeDv / 64;
+constexpr int kDecChunks = 8;  // 16-byte pieces per thread prefetched (the rest load at commit)
 
 __device__ __forceinline__ uint16_t to_bf16(float x) {
     // round to nearest even (weights are finite and non-negative)
@@ -44,6 +48,7 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
 
 __device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+template <int kDecMaxSteps, int kDecMaxVTiles>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int ldk = a.dqk + 8;  // padded row (16-byte multiple) against bank conflicts
@@ -53,7 +58,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs 
     float *alpha = reinterpret_cast<float *>(pw + kDecHeads * kDecTile);       // [16]
     float *mrun = alpha + kDecHeads;
     float *lrun = mrun + kDecHeads;
-    __shared__ int32_t pos[kDecTile];
+    __shared__ int32_t pos[kDecTile];       // the current tile's positions (-1: none)
+    __shared__ int32_t pos_next[kDecTile];  // the prefetched tile's
 
     const int s = blockIdx.x;
     const int h0 = blockIdx.y * kDecHeads;
@@ -84,7 +90,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs 
         lrun[tid] = 0.f;
     }
 
-    for (int tb = t0; tb < t1; tb += kDecTile) {
+    // The next tile's cache rows are loaded into registers while the
+    // current tile computes, then stored to LDS once the current tile is
+    // done with it.  A tile is 32 rows x dqk/8 16-byte pieces over 256
+    // threads; each thread prefetches up to kDecChunks of them (all of them
+    // for dqk <= 512) and loads any rest when it stores.
+    const int cpr = a.dqk / 8;
+    uint4 pre[kDecChunks];
+    int32_t pre_pos = -1;  // threads 0..31: the position of their tile row
+    auto fetch = [&](int tb) __attribute__((always_inline)) {
         if (tid < kDecTile) {
             const int t = tb + tid;
             int32_t j = -1;
@@ -92,19 +106,49 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs 
                 j = a.idx[(size_t)r * a.k + t];
                 if (j < 0 || (int64_t)j >= a.n_kv) j = -1;
             }
-            pos[tid] = j;
+            pre_pos = j;
+            pos_next[tid] = j;
         }
         __syncthreads();
-        // gather the tile's cache rows (zeros for empty slots)
-        const int cpr = a.dqk / 8;
-        for (int c = tid; c < kDecTile * cpr; c += kDecThreads) {
+#pragma unroll
+        for (int u = 0; u < kDecChunks; ++u) {
+            const int c = tid + u * kDecThreads;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (c < kDecTile * cpr) {
+                const int row = c / cpr, cc = c - row * cpr;
+                const int32_t j = pos_next[row];
+                if (j >= 0) v = *reinterpret_cast<const uint4 *>(a.kv + (size_t)j * a.dqk + cc * 8);
+            }
+            pre[u] = v;
+        }
+    };
+    auto commit = [&]() __attribute__((always_inline)) {
+        if (tid < kDecTile) pos[tid] = pre_pos;
+#pragma unroll
+        for (int u = 0; u < kDecChunks; ++u) {
+            const int c = tid + u * kDecThreads;
+            if (c < kDecTile * cpr) {
+                const int row = c / cpr, cc = c - row * cpr;
+                *reinterpret_cast<uint4 *>(kt + row * ldk + cc * 8) = pre[u];
+            }
+        }
+        for (int c = tid + kDecChunks * kDecThreads; c < kDecTile * cpr; c += kDecThreads) {
             const int row = c / cpr, cc = c - row * cpr;
-            const int32_t j = pos[row];
+            const int32_t j = pos_next[row];
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
             if (j >= 0) v = *reinterpret_cast<const uint4 *>(a.kv + (size_t)j * a.dqk + cc * 8);
             *reinterpret_cast<uint4 *>(kt + row * ldk + cc * 8) = v;
         }
-        __syncthreads();
+    };
+    if (t0 < t1) {
+        fetch(t0);
+        commit();
+    }
+    __syncthreads();
+
+    for (int tb = t0; tb < t1; tb += kDecTile) {
+        const bool more = tb + kDecTile < t1;
+        if (more) fetch(tb + kDecTile);   // loads in flight during this tile
         // partial scores over this wave's k-steps (B layout: lane holds
         // column col16 of the n-tile, k = 4 grp .. 4 grp + 3)
         f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -193,6 +237,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs 
             }
         }
         __syncthreads();
+        if (more) {
+            commit();
+            __syncthreads();
+        }
     }
     // this split's (O, max, sum) per head
 #pragma unroll
@@ -242,20 +290,27 @@ size_t decode_lds_bytes(int dqk) {
            (size_t)kDecHeads * kDecTile * 2 + 3 * kDecHeads * 4;
 }
 
-hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
-    if (a.rows <= 0) return hipSuccess;
+template <int MS, int MV>
+hipError_t launch_partial(const DecodeArgs &a, hipStream_t stream) {
     static bool raised = false;
     if (!raised) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_partial_kernel),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_partial_kernel<MS, MV>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)decode_lds_bytes(kMaxDecodeDqk));
         if (e != hipSuccess) return e;
         raised = true;
     }
     const dim3 grid((unsigned)a.splits, (unsigned)(a.heads / kDecHeads), (unsigned)a.rows);
-    hipLaunchKernelGGL(decode_partial_kernel, grid, dim3(kDecThreads), decode_lds_bytes(a.dqk),
-                       stream, a);
+    hipLaunchKernelGGL((decode_partial_kernel<MS, MV>), grid, dim3(kDecThreads),
+                       decode_lds_bytes(a.dqk), stream, a);
     return hipGetLastError();
+}
+
+hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    if (a.dqk <= 16 * 4 * kDecStepsSmall && a.dv <= 64 * kDecVTilesSmall)
+        return launch_partial<kDecStepsSmall, kDecVTilesSmall>(a, stream);
+    return launch_partial<kDecStepsMax, kDecVTilesMax>(a, stream);
 }
 
 // Combines every row of the call (a.rows is the total; row0 unused).
