@@ -221,7 +221,8 @@ int topk_select_radix(const float *scores, const int32_t *lengths, int32_t rows,
  * topk_sparse_decode -- attention over the selected positions only, the
  * consumer of the indices ("The Secret GPU Kernel Behind DeepSeek V4.1
  * Flash", transcript 1:48-2:13: the indexer chooses which positions the
- * expensive attention reads; the third page's sparse-MLA decode kernel splits
+ * expensive attention reads; "The Full-Stack Optimization of DeepSeek-V4-Flash
+ * on Blackwell GPUs", chunk 68.0 summary: a sparse-MLA decode kernel splits
  * the top-k dimension and merges the parts by log-sum-exp).
  *
  *   q:   bf16 [rows][heads][dqk] (raw bits, 16-byte aligned)

@@ -8,7 +8,8 @@ What it computes (the plain definition, in float64): the layers that
 consume the indexer's picks attend only to the selected positions
 ("The Secret GPU Kernel Behind DeepSeek V4.1 Flash", transcript 1:48-2:13:
 the indexer chooses which positions the expensive attention reads; the
-third page's sparse-MLA decode kernel, which splits the top-k dimension and
+sparse-MLA decode kernel of "The Full-Stack Optimization of DeepSeek-V4-Flash
+on Blackwell GPUs", chunk 68.0 summary, which splits the top-k dimension and
 merges the parts by their log-sum-exp).  Readings where the pages are
 silent:
   * One latent cache ``kv[n][dqk]`` is shared by every head (the MLA

@@ -1,7 +1,8 @@
 // Sparse-attention decode over the selected positions: the consumer of the
 // top-k indices ("The Secret GPU Kernel Behind DeepSeek V4.1 Flash",
 // transcript 1:48-2:13: the indexer picks which positions the expensive
-// attention reads; the third page's sparse-MLA decode kernel splits the
+// attention reads; "The Full-Stack Optimization of DeepSeek-V4-Flash on
+// Blackwell GPUs", chunk 68.0 summary: a sparse-MLA decode kernel splits the
 // top-k dimension across workgroups and merges the parts by log-sum-exp).
 //
 // Layout (the pages give none): one latent cache kv[n][dqk] in bf16 shared
