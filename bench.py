@@ -66,7 +66,7 @@ def profile_target(workload: str):
                 4 * w.pool_scores.size + 4 * w.pool_idx.size, 8 * w.rows * w.k)
     if workload == "pool":
         w = workloads.make("adverse")
-        return (traffic_stem(workload), ["block_max_kernel", "radix_select_kernel"],
+        return (traffic_stem(workload), ["block_max8_kernel", "radix_select_kernel"],
                 4 * w.valid_elements(), 8 * w.rows * POOL_KEEP)
     w = workloads.make(workload)
     if workload == "vocab":
@@ -324,7 +324,7 @@ def make_case(name, dev, np, torch, api, workloads):
         def ref(x, ln, cores):
             return oracle.block_pool(x, POOL_GROUP, POOL_KEEP, POOL_PINNED, ln)
 
-        kernel = "block_max_kernel + radix_select_kernel (whole call)"
+        kernel = "block_max8_kernel + radix_select_kernel (whole call)"
         metric = ("effective HBM read GB/s of 1M fp32 scores/row for the block-max pool "
                   f"(blocks of {POOL_GROUP}, {POOL_KEEP:,} kept, {POOL_PINNED} newest pinned)")
         config = {"workload": w.description + f"; block-max pool, blocks of {POOL_GROUP}, "

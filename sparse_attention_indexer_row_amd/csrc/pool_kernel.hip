@@ -75,6 +75,61 @@ __global__ __launch_bounds__(kPoolThreads) void block_max_kernel(PoolArgs a) {
     }
 }
 
+// Blocks of 8 on 16-byte aligned rows (n % 4 == 0): every lane reads one
+// float4, so a wave's load instruction covers 1 KiB of the row, with four
+// loads in flight per thread; the two lanes holding a block's halves
+// combine their maxima with one shuffle, and the even lane writes.  Work
+// item f is the row's f-th float4; block b = f / 2.
+constexpr int kPool8Unroll = 4;
+
+__global__ __launch_bounds__(kPoolThreads) void block_max8_kernel(PoolArgs a) {
+    const int64_t r = (int64_t)a.row0 + blockIdx.y;
+    int64_t L = a.n;
+    if (a.lengths) {
+        const int64_t l = a.lengths[r];
+        L = l < 0 ? 0 : (l > a.n ? a.n : l);
+    }
+    const int64_t nb = (L + 7) / 8;
+    const int64_t P = a.pinned < nb ? a.pinned : nb;
+    float *ov = a.out_vals + r * (int64_t)a.keep;
+    int32_t *oi = a.out_idx + r * (int64_t)a.keep;
+    const float4 *row4 = reinterpret_cast<const float4 *>(a.scores + r * a.n);
+    const int64_t base = (int64_t)blockIdx.x * (kPoolThreads * kPool8Unroll) + threadIdx.x;
+    if (base == 0) a.older[r] = (int32_t)(nb - P);
+    float4 v[kPool8Unroll];
+#pragma unroll
+    for (int u = 0; u < kPool8Unroll; ++u) {
+        const int64_t f = base + (int64_t)u * kPoolThreads;
+        v[u] = 4 * f < L ? row4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kPool8Unroll; ++u) {
+        const int64_t f = base + (int64_t)u * kPoolThreads;
+        const int64_t q = 4 * f;
+        uint32_t m = 0u;  // below every non-NaN key
+        if (q < L) m = order_key(__float_as_uint(v[u].x));
+        if (q + 1 < L) m = max(m, order_key(__float_as_uint(v[u].y)));
+        if (q + 2 < L) m = max(m, order_key(__float_as_uint(v[u].z)));
+        if (q + 3 < L) m = max(m, order_key(__float_as_uint(v[u].w)));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        const int64_t b = f >> 1;
+        if ((f & 1) == 0) {
+            if (b < nb) {
+                const float bv = __uint_as_float(key_bits(m));
+                a.bm[r * a.bm_ld + b] = bv;
+                if (b >= nb - P) {
+                    ov[nb - 1 - b] = bv;
+                    oi[nb - 1 - b] = (int32_t)b;
+                }
+            }
+            if (b >= P && b < a.pinned) {
+                ov[b] = -__builtin_inff();
+                oi[b] = -1;
+            }
+        }
+    }
+}
+
 // Bitonic sort of p2 (a power of two, >= 2) words in LDS by all THREADS
 // threads of the workgroup, ascending or descending.  A stage with stride
 // at most 64 pairs elements inside the 128-element segment of one wave
@@ -671,6 +726,13 @@ hipError_t launch_block_max(const PoolArgs &a, hipStream_t stream) {
     if (a.rows <= 0 || a.span <= 0) return hipSuccess;
     const bool vec = a.group % 4 == 0 && a.n % 4 == 0 &&
                      reinterpret_cast<uintptr_t>(a.scores) % 16 == 0;
+    if (vec && a.group == 8) {
+        const int64_t items = 2 * (int64_t)a.span;
+        const int64_t per = (int64_t)kPoolThreads * kPool8Unroll;
+        const dim3 grid8((unsigned)((items + per - 1) / per), (unsigned)a.rows);
+        hipLaunchKernelGGL(block_max8_kernel, grid8, dim3(kPoolThreads), 0, stream, a);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((a.span + kPoolThreads - 1) / kPoolThreads), (unsigned)a.rows);
     if (vec) {
         hipLaunchKernelGGL(block_max_kernel<true>, grid, dim3(kPoolThreads), 0, stream, a);
