@@ -252,9 +252,9 @@ def make_case(name, dev, np, torch, api, workloads):
 
         def cpu(cores):
             t0 = time.perf_counter()
-            sparse_decode(w.q[:8], w.kv, w.idx[:8], w.scale, w.dv)
+            sparse_decode(w.q, w.kv, w.idx, w.scale, w.dv)
             dt = time.perf_counter() - t0
-            return dt, decode_read_bytes(w) * 8 // rows, "8 of the rows (float64 numpy)"
+            return dt, decode_read_bytes(w), f"all {rows} rows (float64 numpy)"
 
         c.update(rows=rows, read_bytes=decode_read_bytes(w), copies=1, step=step, parity=parity,
                  cpu=cpu, cpu_cores=lambda cores: 1,
@@ -508,10 +508,21 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
+        # Repeat the oracle's pass over the sample until about 15 s of CPU
+        # work (wall time x threads) have run, at most 20 passes or 30 s.
         cores = host_cores()
-        dt, sample_bytes, sample = case["cpu"](cores)
-        cpu = {"value": round(sample_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": case["cpu_cores"](cores),
-               "kind": "oracle", "sample": f"{sample}, one pass, {dt:.2f} s wall"}
+        used = case["cpu_cores"](cores)
+        total, passes, done_bytes = 0.0, 0, 0
+        while True:
+            dt, sample_bytes, sample = case["cpu"](cores)
+            total += dt
+            passes += 1
+            done_bytes += sample_bytes
+            if total * used >= 15.0 or passes >= 20 or total >= 30.0:
+                break
+        cpu = {"value": round(done_bytes / total / 1e9, 3), "unit": "GB/s", "cores": used,
+               "kind": "oracle",
+               "sample": f"{sample}, {passes} pass{'es' if passes > 1 else ''}, {total:.2f} s wall"}
 
     traffic = load_traffic(args.workload)
     roofline = {
