@@ -37,7 +37,7 @@ KERNEL_SOURCES = {
     "vocab": ["pool_kernel.hip", "common.h", "internal.h", "select_args.h"],
     "decode": ["decode_kernel.hip", "common.h", "internal.h", "select_args.h"],
     "pool": SELECT_SOURCES + ["pool_kernel.hip", "internal.h"],
-    "pooled": SELECT_SOURCES + ["pool_kernel.hip", "internal.h"],
+    "pooled": ["pool_kernel.hip", "common.h", "internal.h", "select_args.h"],
 }
 
 
@@ -62,7 +62,7 @@ def profile_target(workload: str):
     if workload == "pooled":
         w = workloads.pooled()
         return (traffic_stem(workload),
-                ["pool_order_kernel", "select_kernel", "pool_positions_kernel"],
+                ["radix_select_kernel"],
                 4 * w.pool_scores.size + 4 * w.pool_idx.size, 8 * w.rows * w.k)
     if workload == "pool":
         w = workloads.make("adverse")
@@ -293,7 +293,7 @@ def make_case(name, dev, np, torch, api, workloads):
         read = 4 * w.pool_scores.size
         c.update(rows=w.rows, read_bytes=read, copies=copies, step=step, parity=parity, cpu=cpu,
                  cpu_cores=lambda cores: 1,
-                 kernel="pool_order_kernel + select_kernel + pool_positions_kernel (whole call)",
+                 kernel="radix_select_kernel",
                  metric="effective HBM read GB/s of pooled scores for top-512 inside "
                         "2,000-block pools (16,000 candidates per row)",
                  config={"workload": w.description, "rows": w.rows, "n": w.n, "k": w.k,

@@ -268,10 +268,9 @@ int topk_sparse_decode(const void *q, const void *kv, const int32_t *idx, int32_
  * (a pool never repeats a block); otherwise the output is unspecified but
  * the call stays memory-safe.  1 <= keep <= TOPK_MAX_POOL_SLOTS, group >= 1
  * (TOPK_EINVAL otherwise), 1 <= k <= TOPK_MAX_K (TOPK_EK_RANGE).
- * Work: per row, the pool's blocks are sorted into position order and their
- * scores gathered into a library-owned, grow-only device buffer; the
- * selection of topk_select runs over the gathered rows; a last step turns
- * gathered offsets into positions.  Buffer rules as for topk_block_pool.
+ * Work: one kernel, the radix selection of topk_select_radix, one workgroup
+ * per row, with each pooled score's word carrying its context position (so
+ * ties resolve by position without reordering the pool).  Allocates nothing.
  */
 int topk_pooled_select(const float *pool_scores, const int32_t *pool_idx,
                        const int32_t *lengths, int32_t rows, int32_t n, int32_t group,

@@ -31,6 +31,7 @@ hipError_t launch_block_max(const PoolArgs &a, hipStream_t stream);
 // Best `k` of each row: an exact radix selection over the rows' 64-bit
 // (key, position) words, one workgroup per row.
 constexpr int kRadixMaxK = 8192;
+constexpr int kMaxPooledSlots = 8192;
 
 struct RadixArgs {
     const float *vals;         // [rows][ld], any 4-byte alignment
@@ -42,33 +43,17 @@ struct RadixArgs {
     float *out_vals;           // [rows][out_ld], first k slots of each row written
     int32_t *out_idx;
     int64_t out_ld;
+    // Pooled rows (pool non-null): element i of row r is context position
+    // pool[r][i / group] * group + i % group; empty slots and positions at or
+    // past the row's context length are not candidates.
+    const int32_t *pool;       // [rows][pool_keep] or null
+    int32_t pool_keep;         // <= kMaxPooledSlots; pooled rows take k <= 2048
+    int32_t group;
+    int64_t n_ctx;
+    const int32_t *ctx_lengths;  // [rows] or null (n_ctx)
 };
 
 hipError_t launch_radix_select(const RadixArgs &a, hipStream_t stream);
-
-// Selection inside a block pool: the pool's blocks in position order.  The
-// order kernel sorts a row's slots in LDS (8 bytes per slot, rounded up to a
-// power of two), so keep is at most TOPK_MAX_POOL_SLOTS (64 KiB).
-
-struct PooledArgs {
-    const float *pool_scores;  // [rows][keep * group]
-    const int32_t *pool_idx;   // [rows][keep]
-    const int32_t *lengths;    // [rows] or null
-    int64_t n;                 // context length
-    int64_t ld;                // row stride of `gathered` (>= keep * group)
-    int32_t rows;              // rows handled by this launch
-    int32_t row0;
-    int32_t group;
-    int32_t keep;              // pool slots per row, <= TOPK_MAX_POOL_SLOTS
-    int32_t k;
-    float *gathered;           // [rows][ld] scores in ascending position order
-    int32_t *blocks;           // [rows][keep] block of each gathered group (ascending)
-    int32_t *valid;            // [rows] gathered scores below the row length
-    int32_t *out_idx;          // [rows][k] gathered offsets in, context positions out
-};
-
-hipError_t launch_pool_order(const PooledArgs &a, hipStream_t stream);
-hipError_t launch_pool_positions(const PooledArgs &a, hipStream_t stream);
 
 // Sparse-attention decode over selected positions.
 constexpr int kMaxDecodeDqk = 1024;

@@ -164,106 +164,6 @@ __device__ void lds_bitonic(uint64_t *x, uint32_t p2) {
     __syncthreads();
 }
 
-// Selection inside a block pool ("The Secret GPU Kernel Behind DeepSeek V4.1
-// Flash", transcript 7:46-8:00): the layers above score only the pooled
-// positions.  The selection kernel gives equal values to the earlier element
-// of its row, so the pool is first laid out in ascending position order:
-// one workgroup per row sorts the (block, slot) pairs by block with a
-// bitonic network in LDS (empty slots last), records the sorted blocks, and
-// copies each block's scores into that order.  Since the blocks are
-// distinct and ascending, the positions along the gathered row increase
-// strictly, so the scores below the row length form a prefix whose length
-// is the selection's row length.  After the selection, a map turns gathered
-// offsets back into context positions.
-constexpr int kOrderThreads = 1024;
-
-__global__ __launch_bounds__(kOrderThreads) void pool_order_kernel(PooledArgs a, int p2) {
-    extern __shared__ uint64_t sorted[];  // p2 words: block << 32 | slot
-    __shared__ int32_t count;
-    const int64_t r = (int64_t)a.row0 + blockIdx.x;
-    const int tid = threadIdx.x;
-    const int32_t *pi = a.pool_idx + r * (int64_t)a.keep;
-    for (int i = tid; i < p2; i += kOrderThreads) {
-        uint64_t w = ~0ull;
-        if (i < a.keep) {
-            const int32_t b = pi[i];
-            w = ((uint64_t)(b < 0 ? 0xFFFFFFFFu : (uint32_t)b) << 32) | (uint32_t)i;
-        }
-        sorted[i] = w;
-    }
-    if (tid == 0) count = 0;
-    __syncthreads();
-    lds_bitonic<kOrderThreads, false>(sorted, (uint32_t)p2);
-    int64_t L = a.n;
-    if (a.lengths) {
-        const int64_t l = a.lengths[r];
-        L = l < 0 ? 0 : (l > a.n ? a.n : l);
-    }
-    const int64_t g = a.group;
-    int32_t *blk = a.blocks + r * (int64_t)a.keep;
-    for (int i = tid; i < a.keep; i += kOrderThreads) {
-        const uint32_t b = (uint32_t)(sorted[i] >> 32);
-        blk[i] = b == 0xFFFFFFFFu ? -1 : (int32_t)b;
-    }
-    const float *ps = a.pool_scores + r * (int64_t)a.keep * g;
-    float *out = a.gathered + r * a.ld;
-    // keep * group < 2^31 (checked on the host): 32-bit offsets, and the
-    // (slot, lane) pair of offset c advances by a fixed step, so the loop
-    // divides nothing.  Four loads are issued before their stores.
-    constexpr uint32_t U = 4;
-    const uint32_t total = (uint32_t)a.keep * (uint32_t)a.group;
-    const uint32_t ug = (uint32_t)a.group;
-    const uint32_t di = (uint32_t)kOrderThreads / ug, dj = (uint32_t)kOrderThreads % ug;
-    uint32_t i = (uint32_t)tid / ug, j = (uint32_t)tid % ug;
-    int mine = 0;
-    for (uint32_t c0 = (uint32_t)tid; c0 < total; c0 += U * kOrderThreads) {
-        float v[U];
-        uint32_t at[U];
-#pragma unroll
-        for (uint32_t u = 0; u < U; ++u) {
-            const uint32_t c = c0 + u * kOrderThreads;
-            at[u] = 0xFFFFFFFFu;
-            v[u] = 0.f;
-            if (c < total) {
-                const uint64_t w = sorted[i];
-                const uint32_t b = (uint32_t)(w >> 32);
-                if (b != 0xFFFFFFFFu && (int64_t)b * g + j < L) {
-                    v[u] = ps[(size_t)(uint32_t)w * ug + j];
-                    at[u] = c;
-                }
-            }
-            i += di;
-            j += dj;
-            if (j >= ug) {
-                j -= ug;
-                ++i;
-            }
-        }
-#pragma unroll
-        for (uint32_t u = 0; u < U; ++u) {
-            if (at[u] != 0xFFFFFFFFu) {
-                out[at[u]] = v[u];
-                ++mine;
-            }
-        }
-    }
-    if (mine) atomicAdd(&count, mine);
-    __syncthreads();
-    if (tid == 0) a.valid[r] = count;
-}
-
-__global__ __launch_bounds__(256) void pool_positions_kernel(PooledArgs a) {
-    const int64_t r = (int64_t)a.row0 + blockIdx.y;
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= a.k) return;
-    int32_t *idx = a.out_idx + r * (int64_t)a.k;
-    const int32_t c = idx[t];
-    if (c < 0) return;
-    const uint32_t g = (uint32_t)a.group;
-    const uint32_t i = (uint32_t)c / g;
-    idx[t] = (int32_t)((uint32_t)a.blocks[r * (int64_t)a.keep + i] * g + ((uint32_t)c - i * g));
-}
-
 // Best k of a row of block maxima by radix selection.  The row is short
 // (one value per block of positions) and fully written before the selection
 // starts, so instead of streaming it through trays, one workgroup per row
@@ -302,6 +202,34 @@ __device__ __forceinline__ uint64_t radix_word(float v, uint32_t i) {
     return pack_word(order_key(__float_as_uint(v)), i);
 }
 
+// The 64-bit word of element i (value v) of a row: the order key above the
+// complemented index.
+struct PlainWords {
+    __device__ __forceinline__ uint64_t operator()(float v, uint32_t i) const {
+        return radix_word(v, i);
+    }
+};
+
+// Rows of pooled scores: element i is context position
+// pool[i / group] * group + i % group, so the word carries that position and
+// equal values go to the lower position.  Elements of empty slots or past
+// the context length get key 0 (below every score; written out as filler)
+// and stay distinct through their element index.
+struct PooledWords {
+    const int32_t *pool;  // this row's pool slots (an LDS copy)
+    uint32_t group;
+    int32_t gshift;       // log2(group) when group is a power of two, else -1
+    int64_t len;          // this row's context length
+    __device__ __forceinline__ uint64_t operator()(float v, uint32_t i) const {
+        const uint32_t s = gshift >= 0 ? i >> gshift : i / group;
+        const uint32_t j = i - s * group;
+        const int32_t b = pool[s];
+        const int64_t pos = (int64_t)b * group + j;
+        if (b < 0 || pos >= len) return (uint64_t)(0xFFFFFFFFu - i);
+        return pack_word(order_key(__float_as_uint(v)), (uint32_t)pos);
+    }
+};
+
 // A row of m floats at any 4-byte alignment: `head` scalars up to the
 // first 16-byte boundary, `n4` aligned float4s, then `tail` scalars.
 // Nothing past the row is read.
@@ -323,14 +251,14 @@ __device__ __forceinline__ RowParts row_parts(const float *row, uint32_t m) {
 
 // Calls fn(word, valid) once per thread for the head and tail scalars
 // (thread t takes the t-th of them; valid is false for the rest).
-template <class F>
-__device__ __forceinline__ void for_each_scalar(const float *row, RowParts p, F &&fn) {
+template <class W, class F>
+__device__ __forceinline__ void for_each_scalar(const float *row, RowParts p, const W &wm, F &&fn) {
     const uint32_t t = threadIdx.x;
     const uint32_t i = t < p.head ? t : p.head + 4u * p.n4 + (t - p.head);
     const bool valid = t < p.head + p.tail;
     float x = 0.f;
     if (valid) x = row[i];
-    fn(radix_word(x, i), valid);
+    fn(wm(x, i), valid);
 }
 
 // Calls fn(word, valid) for every element of a row of m floats: eight
@@ -338,8 +266,8 @@ __device__ __forceinline__ void for_each_scalar(const float *row, RowParts p, F 
 // 16 bytes, the unaligned ends one scalar per thread.  Every lane of a wave
 // makes the same calls (`valid` is false where there is no element), so fn
 // may use wave-wide ballots.
-template <class F>
-__device__ __forceinline__ void for_each_word(const float *row, uint32_t m, F &&fn) {
+template <class W, class F>
+__device__ __forceinline__ void for_each_word(const float *row, uint32_t m, const W &wm, F &&fn) {
     constexpr uint32_t U = 8;
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const RowParts p = row_parts(row, m);
@@ -355,13 +283,13 @@ __device__ __forceinline__ void for_each_word(const float *row, uint32_t m, F &&
             const uint32_t q = base + u * kRadixThreads;
             const uint32_t i = p.head + 4u * q;
             const bool ok = q < p.n4;
-            fn(radix_word(v[u].x, i), ok);
-            fn(radix_word(v[u].y, i + 1), ok);
-            fn(radix_word(v[u].z, i + 2), ok);
-            fn(radix_word(v[u].w, i + 3), ok);
+            fn(wm(v[u].x, i), ok);
+            fn(wm(v[u].y, i + 1), ok);
+            fn(wm(v[u].z, i + 2), ok);
+            fn(wm(v[u].w, i + 3), ok);
         }
     }
-    for_each_scalar(row, p, fn);
+    for_each_scalar(row, p, wm, fn);
 }
 
 // Appends every word of the row with w >= lo to buf: per group of eight
@@ -372,8 +300,10 @@ __device__ __forceinline__ void for_each_word(const float *row, uint32_t m, F &&
 __device__ __forceinline__ void wave_append(uint64_t *buf, uint32_t *counter, uint32_t cap,
                                             uint64_t w, bool take);
 
-__device__ __forceinline__ void append_at_least(const float *row, uint32_t m, uint64_t lo,
-                                                uint64_t *buf, uint32_t *counter, uint32_t cap) {
+template <class W>
+__device__ __forceinline__ void append_at_least(const float *row, uint32_t m, const W &wm,
+                                                uint64_t lo, uint64_t *buf, uint32_t *counter,
+                                                uint32_t cap) {
     constexpr uint32_t U = 8;
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const RowParts p = row_parts(row, m);
@@ -390,10 +320,10 @@ __device__ __forceinline__ void append_at_least(const float *row, uint32_t m, ui
             const uint32_t q = base + u * kRadixThreads;
             const uint32_t i = p.head + 4u * q;
             if (q < p.n4) {
-                mine += radix_word(v[u].x, i) >= lo;
-                mine += radix_word(v[u].y, i + 1) >= lo;
-                mine += radix_word(v[u].z, i + 2) >= lo;
-                mine += radix_word(v[u].w, i + 3) >= lo;
+                mine += wm(v[u].x, i) >= lo;
+                mine += wm(v[u].y, i + 1) >= lo;
+                mine += wm(v[u].z, i + 2) >= lo;
+                mine += wm(v[u].w, i + 3) >= lo;
             }
         }
         // exclusive prefix of `mine` over the wave, and the wave's total
@@ -416,7 +346,7 @@ __device__ __forceinline__ void append_at_least(const float *row, uint32_t m, ui
             const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
             for (uint32_t c = 0; c < 4; ++c) {
-                const uint64_t w = radix_word(e[c], i + c);
+                const uint64_t w = wm(e[c], i + c);
                 if (q < p.n4 && w >= lo) {
                     if (at < cap) buf[at] = w;
                     ++at;
@@ -424,7 +354,7 @@ __device__ __forceinline__ void append_at_least(const float *row, uint32_t m, ui
             }
         }
     }
-    for_each_scalar(row, p, [&](uint64_t w, bool valid) {
+    for_each_scalar(row, p, wm, [&](uint64_t w, bool valid) {
         wave_append(buf, counter, cap, w, valid && w >= lo);
     });
 }
@@ -544,7 +474,35 @@ constexpr uint32_t kSampleChunks = 128;
 constexpr uint32_t kSampleWords = kSampleChunks * kWave;
 constexpr uint32_t kEstimateMinRow = 4 * kSampleWords;
 
-template <class Cap>
+// Per-row word maker; `slots` is LDS room for a pooled row's slots.
+template <class Words>
+__device__ __forceinline__ Words row_words(const RadixArgs &a, int64_t r, int32_t *slots);
+
+template <>
+__device__ __forceinline__ PlainWords row_words<PlainWords>(const RadixArgs &, int64_t, int32_t *) {
+    return PlainWords{};
+}
+
+template <>
+__device__ __forceinline__ PooledWords row_words<PooledWords>(const RadixArgs &a, int64_t r,
+                                                              int32_t *slots) {
+    int64_t len = a.n_ctx;
+    if (a.ctx_lengths) {
+        const int64_t l = a.ctx_lengths[r];
+        len = l < 0 ? 0 : (l > a.n_ctx ? a.n_ctx : l);
+    }
+    const int32_t *pool = a.pool + r * (int64_t)a.pool_keep;
+    for (int s = threadIdx.x; s < a.pool_keep; s += kRadixThreads) slots[s] = pool[s];
+    __syncthreads();
+    const uint32_t g = (uint32_t)a.group;
+    const int32_t gshift = (g & (g - 1)) == 0 ? (int32_t)__builtin_ctz(g) : -1;
+    return PooledWords{slots, g, gshift, len};
+}
+
+// LDS a pooled launch adds for the row's slots.
+__host__ __device__ constexpr size_t pooled_slot_bytes(int keep) { return (size_t)keep * 4; }
+
+template <class Cap, class Words>
 __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a) {
     constexpr int kRadixSel = Cap::kSel;
     constexpr int kRadixCand = Cap::kCand;
@@ -562,6 +520,8 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
     const uint32_t m = (uint32_t)m64;
     const uint32_t k = (uint32_t)a.k;
     const float *row = a.vals + r * a.ld;
+    const Words wm = row_words<Words>(
+        a, r, reinterpret_cast<int32_t *>(hist + kRadixBins));
 
     if (tid == 0) {
         sh.nsel = 0;
@@ -573,7 +533,7 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
     bool done = false;
     if (m <= k) {
         // every word wins (thr = 0 admits all)
-        for_each_word(row, m, [&](uint64_t w, bool valid) {
+        for_each_word(row, m, wm, [&](uint64_t w, bool valid) {
             wave_append(sel, &sh.nsel, kRadixSel, w, valid);
         });
         done = true;
@@ -586,17 +546,22 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
         const float lam = (float)k * (float)kSampleWords / (float)m;
         const uint32_t j = (uint32_t)ceilf(lam + 4.0f * sqrtf(lam) + 4.0f);
         if (j < kSampleWords) {
+            // the sample fills the winner and candidate lists' room (both
+            // empty until the admission pass, which then overwrites it)
+            static_assert(kRadixSel + kRadixCand >= (int)kSampleWords, "sample room");
+            uint64_t *samp = lds;
             for (uint32_t q = tid; q < kSampleWords; q += kRadixThreads) {
                 const uint32_t c = q / kWave, o = q % kWave;
                 const uint32_t i = (uint32_t)(((uint64_t)c * m) / kSampleChunks) + o;
-                cand[q] = radix_word(row[i], i);
+                samp[q] = wm(row[i], i);
             }
             __syncthreads();
             int es = 0;
             uint64_t et = 0;
-            lds_radix(cand, kSampleWords, j, hist, sh, es, et);
+            lds_radix(samp, kSampleWords, j, hist, sh, es, et);
+            __syncthreads();  // the sample is read before the admission pass overwrites it
             const uint64_t est = et << es;   // words >= est: j in the sample
-            append_at_least(row, m, est, cand, &sh.ncand, kRadixCand);
+            append_at_least(row, m, wm, est, cand, &sh.ncand, kRadixCand);
             __syncthreads();
             const uint32_t nc = sh.ncand;
             if (nc >= k && nc <= (uint32_t)kRadixCand) {
@@ -625,11 +590,11 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
             for (int b = tid; b < kRadixBins; b += kRadixThreads) hist[b] = 0u;
             __syncthreads();
             if (level == 0) {
-                for_each_word(row, m, [&](uint64_t w, bool valid) {
+                for_each_word(row, m, wm, [&](uint64_t w, bool valid) {
                     hist_add(hist, (uint32_t)(w >> s) & dmask, valid);
                 });
             } else {
-                for_each_word(row, m, [&](uint64_t w, bool valid) {
+                for_each_word(row, m, wm, [&](uint64_t w, bool valid) {
                     hist_add(hist, (uint32_t)(w >> s) & dmask, valid && (w >> ps) == pfx);
                 });
             }
@@ -642,14 +607,14 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
             if (h == need || level == kRadixLevels - 1) {
                 // the whole bin wins: winners are the words at or above it
                 // (after the last level the bin is one word)
-                for_each_word(row, m, [&](uint64_t w, bool valid) {
+                for_each_word(row, m, wm, [&](uint64_t w, bool valid) {
                     wave_append(sel, &sh.nsel, kRadixSel, w, valid && (w >> s) >= pfx);
                 });
                 break;
             }
             if (h <= (uint32_t)kRadixCand) {
                 // words above the bin win; the bin goes to LDS
-                for_each_word(row, m, [&](uint64_t w, bool valid) {
+                for_each_word(row, m, wm, [&](uint64_t w, bool valid) {
                     const uint64_t top = w >> s;
                     wave_append(sel, &sh.nsel, kRadixSel, w, valid && top > pfx);
                     wave_append(cand, &sh.ncand, kRadixCand, w, valid && top == pfx);
@@ -676,50 +641,46 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
     int32_t *oi = a.out_idx + r * a.out_ld;
     for (uint32_t t = tid; t < k; t += kRadixThreads) {
         const uint64_t w = t < ns ? sel[t] : 0ull;
-        ov[t] = w != 0ull ? __uint_as_float(key_bits((uint32_t)(w >> 32))) : -__builtin_inff();
-        oi[t] = w != 0ull ? (int32_t)word_pos(w) : -1;
+        // key 0: no element (padding, or an element outside the pool's rows)
+        const bool real = (w >> 32) != 0ull;
+        ov[t] = real ? __uint_as_float(key_bits((uint32_t)(w >> 32))) : -__builtin_inff();
+        oi[t] = real ? (int32_t)word_pos(w) : -1;
     }
 }
 
 }  // namespace
 
-template <class Cap>
+template <class Cap, class Words>
 hipError_t launch_radix_cap(const RadixArgs &a, hipStream_t stream) {
+    // pooled rows also keep the row's slots in LDS, after the histogram
+    const size_t extra = a.pool ? pooled_slot_bytes(kMaxPooledSlots) : 0;
     static bool raised = false;
     if (!raised) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&radix_select_kernel<Cap>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)Cap::kLds);
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&radix_select_kernel<Cap, Words>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(Cap::kLds + extra));
         if (e != hipSuccess) return e;
         raised = true;
     }
-    hipLaunchKernelGGL(radix_select_kernel<Cap>, dim3((unsigned)a.rows), dim3(kRadixThreads),
-                       Cap::kLds, stream, a);
+    const size_t lds = Cap::kLds + (a.pool ? pooled_slot_bytes(a.pool_keep) : 0);
+    hipLaunchKernelGGL((radix_select_kernel<Cap, Words>), dim3((unsigned)a.rows),
+                       dim3(kRadixThreads), lds, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_radix_select(const RadixArgs &a, hipStream_t stream) {
+template <class Words>
+hipError_t launch_radix_words(const RadixArgs &a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
-    if (a.k <= RadixSmall::kSel) return launch_radix_cap<RadixSmall>(a, stream);
-    if (a.k <= RadixLarge::kSel) return launch_radix_cap<RadixLarge>(a, stream);
+    if (a.pool && (a.pool_keep > kMaxPooledSlots || a.k > RadixSmall::kSel))
+        return hipErrorInvalidValue;
+    if (a.k <= RadixSmall::kSel) return launch_radix_cap<RadixSmall, Words>(a, stream);
+    if (a.k <= RadixLarge::kSel) return launch_radix_cap<RadixLarge, Words>(a, stream);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_pool_order(const PooledArgs &a, hipStream_t stream) {
-    if (a.rows <= 0) return hipSuccess;
-    int p2 = 1;
-    while (p2 < a.keep) p2 <<= 1;
-    if (p2 < 2) p2 = 2;
-    hipLaunchKernelGGL(pool_order_kernel, dim3((unsigned)a.rows), dim3(kOrderThreads),
-                       (size_t)p2 * 8, stream, a, p2);
-    return hipGetLastError();
-}
-
-hipError_t launch_pool_positions(const PooledArgs &a, hipStream_t stream) {
-    if (a.rows <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((a.k + 255) / 256), (unsigned)a.rows);
-    hipLaunchKernelGGL(pool_positions_kernel, grid, dim3(256), 0, stream, a);
-    return hipGetLastError();
+hipError_t launch_radix_select(const RadixArgs &a, hipStream_t stream) {
+    return a.pool ? launch_radix_words<PooledWords>(a, stream)
+                  : launch_radix_words<PlainWords>(a, stream);
 }
 
 hipError_t launch_block_max(const PoolArgs &a, hipStream_t stream) {

@@ -507,57 +507,31 @@ int topk_pooled_select(const float *pool_scores, const int32_t *pool_idx,
         return TOPK_EINVAL;
     if (k < 1 || k > TOPK_MAX_K) return TOPK_EK_RANGE;
     const int64_t total = (int64_t)keep * group;
-    const int64_t ld = (total + kPoolRowAlign - 1) / kPoolRowAlign * kPoolRowAlign;
-    if (ld > INT32_MAX) return TOPK_EINVAL;
+    if (total > INT32_MAX) return TOPK_EINVAL;
     if (rows == 0) return TOPK_OK;
     if (!pool_scores || !pool_idx || !out_vals || !out_idx) return TOPK_EINVAL;
     if (misaligned(pool_scores, 4) || misaligned(pool_idx, 4) || misaligned(out_vals, 4) ||
         misaligned(out_idx, 4) || (lengths && misaligned(lengths, 4)))
         return TOPK_EINVAL;
-    int st = check_plan(make_plan(rows, (int32_t)ld, k, nullptr, kAssumedCUs));
-    if (st != TOPK_OK) return st;
-    int cus = 0;
-    st = device_cus(&cus);
-    if (st != TOPK_OK) return st;
-    const size_t gathered_bytes = align_up((size_t)rows * (size_t)ld * 4, kAlign);
-    const size_t blocks_bytes = align_up((size_t)rows * (size_t)keep * 4, kAlign);
-    void *scratch = nullptr;
-    st = grow_buffer(g_pool, gathered_bytes + blocks_bytes + (size_t)rows * 4, false,
-                     (hipStream_t)stream, &scratch);
-    if (st != TOPK_OK) return st;
-    char *base = static_cast<char *>(scratch);
-    topk::PooledArgs a{};
-    a.pool_scores = pool_scores;
-    a.pool_idx = pool_idx;
-    a.lengths = lengths;
-    a.n = n;
-    a.ld = ld;
-    a.group = group;
-    a.keep = keep;
-    a.k = k;
-    a.gathered = reinterpret_cast<float *>(base);
-    a.blocks = reinterpret_cast<int32_t *>(base + gathered_bytes);
-    a.valid = reinterpret_cast<int32_t *>(base + gathered_bytes + blocks_bytes);
-    a.out_idx = out_idx;
+    // One radix selection per row over the pooled scores, whose words
+    // carry context positions (so equal values go to the lower position).
+    topk::RadixArgs x{};
+    x.vals = pool_scores;
+    x.count = nullptr;
+    x.ld = total;
+    x.k = k;
+    x.out_vals = out_vals;
+    x.out_idx = out_idx;
+    x.out_ld = k;
+    x.pool = pool_idx;
+    x.pool_keep = keep;
+    x.group = group;
+    x.n_ctx = n;
+    x.ctx_lengths = lengths;
     for (int32_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
-        a.row0 = r0;
-        a.rows = std::min(kMaxGridRows, rows - r0);
-        if (topk::launch_pool_order(a, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
-    }
-    Plan pl = make_plan(rows, (int32_t)ld, k, nullptr, cus);
-    void *ws = nullptr;
-    if (pl.split > 1) {
-        st = internal_workspace(pl.ws_bytes, (hipStream_t)stream, &ws);
-        if (st != TOPK_OK) return st;
-    }
-    st = run(a.gathered, a.valid, rows, (int32_t)ld, k, out_vals, out_idx, pl, ws, 0, 0u,
-             nullptr, (hipStream_t)stream);
-    if (st != TOPK_OK) return st;
-    for (int32_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
-        a.row0 = r0;
-        a.rows = std::min(kMaxGridRows, rows - r0);
-        if (topk::launch_pool_positions(a, (hipStream_t)stream) != hipSuccess)
-            return TOPK_ELAUNCH;
+        x.row0 = r0;
+        x.rows = std::min(kMaxGridRows, rows - r0);
+        if (topk::launch_radix_select(x, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
     }
     return TOPK_OK;
 }
