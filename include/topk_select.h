@@ -67,10 +67,10 @@ extern "C" {
  * topk_select -- top-k of every row, planned automatically.
  *
  * Chooses one workgroup per row or, when rows alone cannot fill the GPU,
- * splits each row across several workgroups (transcript 5:22-5:33).  For
- * k > 1024 on rows of at most 262,144 scores, with at least a quarter as
- * many rows as compute units, it runs topk_select_radix instead (same
- * result; faster there).  A split
+ * splits each row across several workgroups (transcript 5:22-5:33).  On
+ * rows of at most 262,144 scores it runs topk_select_radix instead (same
+ * result; faster there) when k > 1024 with at least a quarter as many rows
+ * as compute units, or k > 512 with at least half as many.  A split
  * call uses a library-owned, grow-only workspace per device, allocated with
  * hipMalloc on the first call that needs a larger one (so the first such call
  * is not graph-capturable; use topk_select_split for capture).  Calls that

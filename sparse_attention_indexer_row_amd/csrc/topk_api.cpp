@@ -248,13 +248,17 @@ constexpr int64_t kPoolRowAlign = 64;
 constexpr int32_t kMaxGridRows = 65535;
 
 // Where topk_select takes the per-row radix selection instead of the
-// streaming filter: lists wider than 1,024 words, rows no longer than
-// 262,144 scores, and at least a quarter as many rows as compute units.
-// There the streaming path's 2,048-word lists spend their time sorting,
-// while one workgroup per row keeps the whole GPU busy (measured 1.2-3.9x
-// faster on such shapes; slower on million-score rows or k <= 1,024).
+// streaming filter: rows no longer than 262,144 scores with lists of 1,024
+// words (k > 512) and at least half as many rows as compute units, or
+// lists of 2,048 words (k > 1,024) and at least a quarter as many.  There
+// the streaming path's wide lists spend their time sorting, while one
+// workgroup per row keeps the GPU busy (measured 1.2-2.6x faster on such
+// shapes; slower on million-score rows, at k <= 512, or with fewer rows).
 bool prefer_radix(int32_t rows, int32_t n, int32_t k, int cus) {
-    return k > 1024 && n <= 262144 && (int64_t)rows * 4 >= cus;
+    if (n > 262144) return false;
+    if (k > 1024) return (int64_t)rows * 4 >= cus;
+    if (k > 512) return (int64_t)rows * 2 >= cus;
+    return false;
 }
 
 }  // namespace

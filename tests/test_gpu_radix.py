@@ -98,3 +98,15 @@ def test_outputs_stay_in_their_rows():
     assert torch.all(vals[3] == 7.0) and torch.all(idx[3] == 1234)
     rv, ri = oracle.topk(x, k)
     H.assert_same(vals[:3], idx[:3], rv, ri, "radix rows")
+
+
+def test_topk_select_routes_wide_lists_over_many_short_rows():
+    # 300 rows of 20,000 at k = 1,000 and k = 2,000 take the radix path
+    # inside topk_select; the result is the same selection
+    x = workloads.normal_rows(300, 20_000, seed=21)
+    for k in (1000, 2000):
+        print(f"[case] topk_select routed k={k}", flush=True)
+        v, i = api.topk_select(H.to_dev(x), k)
+        torch.cuda.synchronize()
+        rv, ri = oracle.topk(x, k)
+        H.assert_same(v, i, rv, ri, f"routed k={k}")
