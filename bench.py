@@ -202,6 +202,20 @@ def summarize_profiles(workload: str, trace_dir: str, fetch_dir: str, write_dir:
     return 0
 
 
+def host_cpu() -> dict:
+    """The host's CPU model and logical CPU count, for the baseline's context."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count()}
+
+
 def host_cores() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -356,11 +370,17 @@ def make_case(name, dev, np, torch, api, workloads):
         def ref(x, ln, cores):
             return oracle.topk(x, k, ln, threads=cores)
 
-        kernel = "select_kernel"
+        # topk_select takes the radix path on wide lists over many short
+        # rows (the library's routing rule, mirrored here for the labels)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        routed = n <= 262144 and ((k > 1024 and rows * 4 >= cus) or (k > 512 and rows * 2 >= cus))
+        kernel = "radix_select_kernel" if routed else "select_kernel"
         metric = METRIC_SELECT
         plan = api.topk_plan(rows, n, k)
         config = {"workload": w.description, "rows": rows, "n": n, "k": k,
-                  "split": plan["split"], "waves": plan["waves"]}
+                  "path": "radix" if routed else "streaming"}
+        if not routed:
+            config.update(split=plan["split"], waves=plan["waves"])
         cores_used = lambda cores: cores
 
     def parity():
@@ -375,17 +395,49 @@ def make_case(name, dev, np, torch, api, workloads):
         return (time.perf_counter() - t0, 4 * w.valid_elements(),
                 f"all {rows} rows of the batch")
 
+    def extras():
+        """Per-row counts of scores that entered a tray and of threshold-raising
+        selections (the schedule's own instrumentation, one extra call), and
+        torch.topk on the same rows for context."""
+        out = {}
+        if kernel == "select_kernel":
+            st = torch.zeros((rows, 2), dtype=torch.int64, device=dev)
+            ws = api.new_workspace(rows, n, k, plan["split"]) if plan["split"] > 1 else None
+            api.topk_select_ex(base, k, lengths, stats=st, workspace=ws, stream=stream)
+            torch.cuda.synchronize()
+            e = st.cpu().numpy().astype(np.float64)
+            out["entrants"] = {"mean": round(float(e[:, 0].mean()), 1), "max": int(e[:, 0].max()),
+                               "sorts_mean": round(float(e[:, 1].mean()), 2),
+                               "sorts_max": int(e[:, 1].max()),
+                               "per": "row (all segments of a split row)"}
+            if lengths is None:
+                tv, _ = torch.topk(base, k, dim=1)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(5):
+                    torch.topk(base, k, dim=1)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t_us = e0.elapsed_time(e1) / 5 * 1e3
+                same = bool(torch.equal(tv.cpu(), vals.cpu()))
+                out["torch_topk"] = {"us_per_call": round(t_us, 1),
+                                     "GBps": round(4 * w.valid_elements() / (t_us * 1e-6) / 1e9, 1),
+                                     "values_equal": same, "note": "context only"}
+        return out
+
     c.update(rows=rows, read_bytes=4 * w.valid_elements(), copies=copies, step=step,
              parity=parity, cpu=cpu, cpu_cores=cores_used, kernel=kernel, metric=metric,
-             config=config, set_copies=set_copies)
+             config=config, set_copies=set_copies, extras=extras)
     return c
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="adverse",
                     choices=["small", "outlier", "one_row", "adverse", "ragged", "pool", "pooled",
                              "vocab", "decode"],
@@ -524,6 +576,10 @@ def main() -> int:
                "kind": "oracle",
                "sample": f"{sample}, {passes} pass{'es' if passes > 1 else ''}, {total:.2f} s wall"}
 
+    extra = {}
+    if "extras" in case and not args.profile_run:
+        extra = case["extras"]()
+
     traffic = load_traffic(args.workload)
     roofline = {
         "kernel": case["kernel"],
@@ -551,7 +607,13 @@ def main() -> int:
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
         "kernel_us_mean": round(kern_ms * 1e3, 2),
         "kernel_us_median": round(float(np.median(per_launch_ms)) * 1e3, 2),
+        "kernel_us_p10": round(float(np.percentile(per_launch_ms, 10)) * 1e3, 2),
+        "kernel_us_p90": round(float(np.percentile(per_launch_ms, 90)) * 1e3, 2),
         "read_probe_GBps": round(probe, 1) if probe else None,
+        "frac_of_read_probe": round(achieved / probe, 4) if probe else None,
+        "entrants": extra.get("entrants"),
+        "torch_topk": extra.get("torch_topk"),
+        "host": host_cpu(),
         "parity": parity,
         "roofline": roofline,
         "cpu_baseline": cpu,
