@@ -400,6 +400,17 @@ def make_case(name, dev, np, torch, api, workloads):
         selections (the schedule's own instrumentation, one extra call), and
         torch.topk on the same rows for context."""
         out = {}
+        # the oracle single-threaded on a few rows, beside the threaded baseline
+        few = min(rows, 8)
+        t0 = time.perf_counter()
+        oracle.topk(w.scores[:few], k, w.lengths[:few] if w.lengths is not None else None,
+                    threads=1)
+        dt = time.perf_counter() - t0
+        few_bytes = 4 * (few * n if w.lengths is None
+                         else int(np.clip(w.lengths[:few], 0, n).sum()))
+        out["cpu_single_thread"] = {"value": round(few_bytes / dt / 1e9, 3), "unit": "GB/s",
+                                    "rows_per_s": round(few / dt, 1), "cores": 1,
+                                    "sample": f"{few} rows, one pass, {dt:.2f} s wall"}
         if kernel == "select_kernel":
             st = torch.zeros((rows, 2), dtype=torch.int64, device=dev)
             ws = api.new_workspace(rows, n, k, plan["split"]) if plan["split"] > 1 else None
@@ -614,6 +625,7 @@ def main() -> int:
         "entrants": extra.get("entrants"),
         "torch_topk": extra.get("torch_topk"),
         "host": host_cpu(),
+        "cpu_single_thread": extra.get("cpu_single_thread"),
         "parity": parity,
         "roofline": roofline,
         "cpu_baseline": cpu,
