@@ -58,7 +58,7 @@ extern "C" {
 #define TOPK_EDEVICE (-6)    /* no usable gfx950 device / runtime query failed */
 #define TOPK_EALLOC (-7)     /* library-owned workspace allocation failed     */
 
-/* Largest supported k (the pages' own kernel stops near 4,000). */
+/* Largest k of the streaming selection (topk_select_radix goes to 8,192). */
 #define TOPK_MAX_K 2048
 /* Largest number of workgroups one row may be split across. */
 #define TOPK_MAX_SPLIT 1024
@@ -184,10 +184,11 @@ int topk_plan(int32_t rows, int32_t n, int32_t k, const topk_options *opts, topk
  * (TOPK_EINVAL / TOPK_EK_RANGE otherwise).  out_vals: fp32 [rows][keep],
  * out_idx: int32 [rows][keep], device pointers owned by the caller.
  * Work: one pass over the scores writing ceil(n / group) block maxima per row
- * into a library-owned, grow-only device buffer, then the top-k selection of
- * topk_select over those maxima.  Like topk_select, the first call that needs
- * a larger library buffer allocates it (not graph-capturable), and calls
- * that share the library's buffers must be ordered on one stream.
+ * into a library-owned, grow-only device buffer, then the radix selection of
+ * topk_select_radix over those maxima, written behind the pinned slots.
+ * Like topk_select, the first call that needs a larger library buffer
+ * allocates it (not graph-capturable), and calls that share the library's
+ * buffers must be ordered on one stream.
  */
 int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
                     int32_t group, int32_t keep, int32_t pinned, float *out_vals,
