@@ -205,7 +205,7 @@ int topk_block_pool(const float *scores, const int32_t *lengths, int32_t rows, i
  * k = 4,000 ("The Secret GPU Kernel Behind DeepSeek V4.1 Flash", transcript
  * 5:45 and 8:00-8:14); this entry point serves larger k.
  *
- * One workgroup per row: an evenly spread 8,192-score sample gives a
+ * One workgroup per row: an evenly spread 4,096-score sample gives a
  * threshold a little below the k-th score; one pass over the row copies
  * every score at or above it into LDS; an 11-bit-digit radix selection in
  * LDS finds the k-th (value, position) word exactly, and the winners are

@@ -533,9 +533,9 @@ __device__ void lds_radix(const uint64_t *buf, uint32_t n, uint32_t need, uint32
     }
 }
 
-// Sample size of the threshold estimate: 128 chunks of 64 consecutive
+// Sample size of the threshold estimate: 64 chunks of 64 consecutive
 // elements spread evenly over the row.
-constexpr uint32_t kSampleChunks = 128;
+constexpr uint32_t kSampleChunks = 64;
 constexpr uint32_t kSampleWords = kSampleChunks * kWave;
 constexpr uint32_t kEstimateMinRow = 4 * kSampleWords;
 
