@@ -537,7 +537,7 @@ __device__ void lds_radix(const uint64_t *buf, uint32_t n, uint32_t need, uint32
 // elements spread evenly over the row.
 constexpr uint32_t kSampleChunks = 64;
 constexpr uint32_t kSampleWords = kSampleChunks * kWave;
-constexpr uint32_t kEstimateMinRow = 4 * kSampleWords;
+constexpr uint32_t kEstimateMinRow = 2 * kSampleWords;
 
 // Per-row word maker; `slots` is LDS room for a pooled row's slots.
 template <class Words>
