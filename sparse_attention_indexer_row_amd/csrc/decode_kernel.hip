@@ -293,14 +293,12 @@ size_t decode_lds_bytes(int dqk) {
 
 template <int MS, int MV>
 hipError_t launch_partial(const DecodeArgs &a, hipStream_t stream) {
-    static bool raised = false;
-    if (!raised) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_partial_kernel<MS, MV>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)decode_lds_bytes(kMaxDecodeDqk));
-        if (e != hipSuccess) return e;
-        raised = true;
-    }
+    // Set on every launch (as for the selection kernel): the attribute
+    // belongs to the current device, and calls may come on several.
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_partial_kernel<MS, MV>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)decode_lds_bytes(a.dqk));
+    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)a.splits, (unsigned)(a.heads / kDecHeads), (unsigned)a.rows);
     hipLaunchKernelGGL((decode_partial_kernel<MS, MV>), grid, dim3(kDecThreads),
                        decode_lds_bytes(a.dqk), stream, a);

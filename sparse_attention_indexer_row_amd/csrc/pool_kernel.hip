@@ -718,16 +718,13 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
 template <class Cap, class Words>
 hipError_t launch_radix_cap(const RadixArgs &a, hipStream_t stream) {
     // pooled rows also keep the row's slots in LDS, after the histogram
-    const size_t extra = a.pool ? pooled_slot_bytes(kMaxPooledSlots) : 0;
-    static bool raised = false;
-    if (!raised) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&radix_select_kernel<Cap, Words>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(Cap::kLds + extra));
-        if (e != hipSuccess) return e;
-        raised = true;
-    }
     const size_t lds = Cap::kLds + (a.pool ? pooled_slot_bytes(a.pool_keep) : 0);
+    // Set on every launch (as for the selection kernel): the attribute
+    // belongs to the current device, and calls may come on several.
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&radix_select_kernel<Cap, Words>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((radix_select_kernel<Cap, Words>), dim3((unsigned)a.rows),
                        dim3(kRadixThreads), lds, stream, a);
     return hipGetLastError();
