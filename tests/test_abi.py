@@ -161,6 +161,8 @@ def test_sparse_decode_argument_errors(lib):
     assert call(dv=96) == _lib.TOPK_EINVAL             # not a multiple of 64
     assert call(dqk=64, dv=128) == _lib.TOPK_EINVAL    # dv above dqk
     assert call(scale=float("nan")) == _lib.TOPK_EINVAL
+    assert call(scale=float("inf")) == _lib.TOPK_EINVAL
+    assert call(scale=float("-inf")) == _lib.TOPK_EINVAL
     assert call(k=0) == _lib.TOPK_EK_RANGE
     assert call(k=8193) == _lib.TOPK_EK_RANGE
     assert call(q=None) == _lib.TOPK_EINVAL
