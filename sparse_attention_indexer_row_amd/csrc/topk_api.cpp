@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 
 #include "common.h"
@@ -452,7 +453,7 @@ int topk_sparse_decode(const void *q, const void *kv, const int32_t *idx, int32_
                        float scale, float *out, void *stream) {
     if (rows < 0 || heads < 16 || heads % 16 != 0 || n_kv < 1 || dqk < 16 || dqk % 16 != 0 ||
         dqk > topk::kMaxDecodeDqk || dv < 64 || dv % 64 != 0 || dv > dqk ||
-        dv > topk::kMaxDecodeDv || !(scale == scale) || scale > 3.4e38f || scale < -3.4e38f)
+        dv > topk::kMaxDecodeDv || !std::isfinite(scale))
         return TOPK_EINVAL;
     if (k < 1 || k > TOPK_MAX_K_RADIX) return TOPK_EK_RANGE;
     if ((int64_t)rows * heads > INT32_MAX) return TOPK_EINVAL;
