@@ -43,7 +43,10 @@ KERNEL_SOURCES = {
 
 def kernel_source_hash(workload: str = "adverse") -> str:
     h = hashlib.sha256()
-    for name in sorted(KERNEL_SOURCES.get(workload, SELECT_SOURCES)):
+    names = KERNEL_SOURCES.get(workload)
+    if names is None:
+        names = KERNEL_SOURCES["vocab"] if workload == "ragged" else SELECT_SOURCES
+    for name in sorted(names):
         with open(os.path.join(ROOT, "sparse_attention_indexer_row_amd", "csrc", name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -69,10 +72,16 @@ def profile_target(workload: str):
         return (traffic_stem(workload), ["block_max8_kernel", "radix_select_kernel"],
                 4 * w.valid_elements(), 8 * w.rows * POOL_KEEP)
     w = workloads.make(workload)
-    if workload == "vocab":
+    if workload == "vocab" or routed_to_radix(w.rows, w.n, w.k, 256):
         return (traffic_stem(workload), ["radix_select_kernel"], 4 * w.valid_elements(),
                 8 * w.rows * w.k)
     return (traffic_stem(workload), ["select_kernel"], 4 * w.valid_elements(), 8 * w.rows * w.k)
+
+
+def routed_to_radix(rows: int, n: int, k: int, cus: int) -> bool:
+    """topk_select's choice of the radix path (the library's rule, mirrored
+    here to label the kernel a workload runs)."""
+    return n <= 262144 and ((k > 1024 and rows * 4 >= cus) or (k > 512 and rows * 2 >= cus))
 
 
 def decode_read_bytes(w) -> int:
@@ -373,7 +382,7 @@ def make_case(name, dev, np, torch, api, workloads):
         # topk_select takes the radix path on wide lists over many short
         # rows (the library's routing rule, mirrored here for the labels)
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        routed = n <= 262144 and ((k > 1024 and rows * 4 >= cus) or (k > 512 and rows * 2 >= cus))
+        routed = routed_to_radix(rows, n, k, cus)
         kernel = "radix_select_kernel" if routed else "select_kernel"
         metric = METRIC_SELECT
         plan = api.topk_plan(rows, n, k)
