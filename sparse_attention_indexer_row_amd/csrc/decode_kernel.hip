@@ -262,25 +262,41 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs 
     }
 }
 
-// One workgroup per (row, head): out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s.
+// One workgroup per (row, head): out = sum_s e^(m_s - M) O_s / sum_s
+// e^(m_s - M) l_s.  Wave 0 reduces the splits' maxima and sums once and
+// leaves one weight per split in LDS; every thread then sums its columns
+// over the splits with independent loads.
+constexpr int kMaxCombineSplits = kRadixMaxK / kDecTile;   // splits of >= 32 positions
+
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+    __shared__ float wgt[kMaxCombineSplits];
+    __shared__ float s_scale;
     const int64_t rh = blockIdx.x;   // r * heads + h
+    const int tid = threadIdx.x;
     const float *ml = a.part_ml + (size_t)rh * a.splits * 2;
-    float M = -__builtin_inff();
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, ml[2 * s]);
-    float *out = a.out + (size_t)rh * a.dv;
-    if (M == -__builtin_inff()) {
-        for (int c = threadIdx.x; c < a.dv; c += blockDim.x) out[c] = 0.f;
-        return;
+    if (tid < kWave) {
+        float M = -__builtin_inff();
+        for (int q = tid; q < a.splits; q += kWave) M = fmaxf(M, ml[2 * q]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        float L = 0.f;
+        for (int q = tid; q < a.splits; q += kWave) {
+            const float w = M == -__builtin_inff() ? 0.f : expf(ml[2 * q] - M);
+            wgt[q] = w;
+            L += w * ml[2 * q + 1];
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+        if (tid == 0) s_scale = L > 0.f ? 1.f / L : 0.f;
     }
-    float L = 0.f;
-    for (int s = 0; s < a.splits; ++s) L += expf(ml[2 * s] - M) * ml[2 * s + 1];
-    const float inv = 1.f / L;
+    __syncthreads();
+    const float scale = s_scale;
     const float *po = a.part_o + (size_t)rh * a.splits * a.dv;
-    for (int c = threadIdx.x; c < a.dv; c += blockDim.x) {
+    float *out = a.out + (size_t)rh * a.dv;
+    for (int c = tid; c < a.dv; c += blockDim.x) {
         float o = 0.f;
-        for (int s = 0; s < a.splits; ++s) o += expf(ml[2 * s] - M) * po[(size_t)s * a.dv + c];
-        out[c] = o * inv;
+        for (int q = 0; q < a.splits; ++q) o += wgt[q] * po[(size_t)q * a.dv + c];
+        out[c] = o * scale;
     }
 }
 
