@@ -1,19 +1,25 @@
-// Block-max pooled pre-selection, first step ("The Secret GPU Kernel Behind
-// DeepSeek V4.1 Flash", transcript 7:22-7:46): the layer that scores the
-// whole context also groups positions into blocks, scores each block by its
-// best position, and keeps the newest blocks unconditionally.
+// Kernels of the block-max pool, of the per-row radix selection, and of
+// selection inside a pool.
 //
-// One work item per block of a row.  It reduces the block's valid scores
-// with the same order-preserving keys the selection uses (IEEE total order,
-// -0.0 below +0.0), writes the block's best score to the block-maxima row,
-// and, when the block is one of the row's newest `pinned`, also writes it
-// straight to its output slot (newest first).  Work items past a short row's
-// blocks fill its unused pinned slots with (-inf, -1).  The selection kernel
-// then picks the best older blocks from the block-maxima rows and writes
-// them behind the pinned slots.
+// Block maxima ("The Secret GPU Kernel Behind DeepSeek V4.1 Flash",
+// transcript 7:22-7:46: the layer that scores the whole context also groups
+// positions into blocks, scores each block by its best position, and keeps
+// the newest blocks unconditionally).  One work item per block of a row (or,
+// for blocks of 8 on aligned rows, one float4 per lane with lane pairs
+// combining): the block's valid scores are reduced with the library's
+// order-preserving keys (IEEE total order, -0.0 below +0.0), the best is
+// written to the block-maxima row and, for the row's newest `pinned` blocks,
+// straight to its output slot (newest first); unused pinned slots of short
+// rows get (-inf, -1).  Traffic: each score read once, one 4-byte maximum
+// written per block.
 //
-// Traffic: each score is read once (coalesced: neighbouring work items read
-// neighbouring blocks), each block writes one 4-byte maximum.
+// Radix selection: the exact best k of each row by the 64-bit (key,
+// position) words, one workgroup per row (a sampled estimate, one admission
+// pass into LDS, an 11-bit-digit search in LDS, and a sort of the winners
+// in register runs).  It picks the pool's best older blocks from the
+// block-maxima rows, serves topk_select_radix, and, with words that carry
+// context positions, selection inside a pool ("The Secret GPU Kernel Behind
+// DeepSeek V4.1 Flash", transcript 7:46-8:00).
 #include <hip/hip_runtime.h>
 
 #include "common.h"
