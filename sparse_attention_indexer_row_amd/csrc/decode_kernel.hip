@@ -39,7 +39,9 @@ constexpr int kDecHeads = 16;      // heads per workgroup (MFMA rows)
 // dv <= 512 (the MLA shape); the general one the limits.
 constexpr int kDecStepsSmall = 576 / 16 / 4, kDecVTilesSmall = 512 / 64;
 constexpr int kDecStepsMax = kMaxDecodeDqk / 16 / 4, kDecVTilesMax = kMaxDecodeDv / 64;
-constexpr int kDecChunks = 8;  // 16-byte pieces per thread prefetched (the rest load at commit)
+// 16-byte pieces per thread prefetched for the next tile (the rest load at
+// commit): all nine of a dqk = 576 tile in the compact instantiation.
+constexpr int kDecChunksSmall = kDecTile * 576 / 8 / kDecThreads, kDecChunksMax = 8;
 
 __device__ __forceinline__ uint16_t to_bf16(float x) {
     // round to nearest even (weights are finite and non-negative)
@@ -49,7 +51,7 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
 
 __device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-template <int kDecMaxSteps, int kDecMaxVTiles>
+template <int kDecMaxSteps, int kDecMaxVTiles, int kDecChunks>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int ldk = a.dqk + 8;  // padded row (16-byte multiple) against bank conflicts
@@ -307,16 +309,16 @@ size_t decode_lds_bytes(int dqk) {
            (size_t)kDecHeads * kDecTile * 2 + 3 * kDecHeads * 4;
 }
 
-template <int MS, int MV>
+template <int MS, int MV, int PC>
 hipError_t launch_partial(const DecodeArgs &a, hipStream_t stream) {
     // Set on every launch (as for the selection kernel): the attribute
     // belongs to the current device, and calls may come on several.
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_partial_kernel<MS, MV>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_partial_kernel<MS, MV, PC>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)decode_lds_bytes(a.dqk));
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)a.splits, (unsigned)(a.heads / kDecHeads), (unsigned)a.rows);
-    hipLaunchKernelGGL((decode_partial_kernel<MS, MV>), grid, dim3(kDecThreads),
+    hipLaunchKernelGGL((decode_partial_kernel<MS, MV, PC>), grid, dim3(kDecThreads),
                        decode_lds_bytes(a.dqk), stream, a);
     return hipGetLastError();
 }
@@ -324,8 +326,8 @@ hipError_t launch_partial(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     if (a.dqk <= 16 * 4 * kDecStepsSmall && a.dv <= 64 * kDecVTilesSmall)
-        return launch_partial<kDecStepsSmall, kDecVTilesSmall>(a, stream);
-    return launch_partial<kDecStepsMax, kDecVTilesMax>(a, stream);
+        return launch_partial<kDecStepsSmall, kDecVTilesSmall, kDecChunksSmall>(a, stream);
+    return launch_partial<kDecStepsMax, kDecVTilesMax, kDecChunksMax>(a, stream);
 }
 
 // Combines every row of the call (a.rows is the total; row0 unused).
