@@ -51,7 +51,7 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
 
 __device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-template <int kDecMaxSteps, int kDecMaxVTiles, int kDecChunks>
+template <int kDecMaxSteps, int kDecMaxVTiles, int kDecChunks, int kExactDqk = 0, int kExactDv = 0>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int ldk = a.dqk + 8;  // padded row (16-byte multiple) against bank conflicts
@@ -71,8 +71,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs 
     const int col16 = lane & 15, grp = lane >> 4;
     const int t0 = s * a.per_split;
     const int t1 = min(a.k, t0 + a.per_split);
-    const int nks = a.dqk / 16;
-    const int nvt = a.dv / 64;
+    // exact-shape instantiations know these at compile time, so the guards
+    // in the unrolled loops fold away and operand loads can be issued early
+    const int nks = kExactDqk ? kExactDqk / 16 : a.dqk / 16;
+    const int nvt = kExactDv ? kExactDv / 64 : a.dv / 64;
 
     // This wave's query operands: k-steps ks = wv, wv + 4, ... (A layout:
     // lane holds row col16, k = 4 grp .. 4 grp + 3 of the step).
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs 
     // done with it.  A tile is 32 rows x dqk/8 16-byte pieces over 256
     // threads; each thread prefetches up to kDecChunks of them (all of them
     // for dqk <= 512) and loads any rest when it stores.
-    const int cpr = a.dqk / 8;
+    const int cpr = kExactDqk ? kExactDqk / 8 : a.dqk / 8;
     uint4 pre[kDecChunks];
     int32_t pre_pos = -1;  // threads 0..31: the position of their tile row
     auto fetch = [&](int tb) __attribute__((always_inline)) {
@@ -309,22 +311,24 @@ size_t decode_lds_bytes(int dqk) {
            (size_t)kDecHeads * kDecTile * 2 + 3 * kDecHeads * 4;
 }
 
-template <int MS, int MV, int PC>
+template <int MS, int MV, int PC, int XQ = 0, int XV = 0>
 hipError_t launch_partial(const DecodeArgs &a, hipStream_t stream) {
     // Set on every launch (as for the selection kernel): the attribute
     // belongs to the current device, and calls may come on several.
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_partial_kernel<MS, MV, PC>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_partial_kernel<MS, MV, PC, XQ, XV>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)decode_lds_bytes(a.dqk));
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)a.splits, (unsigned)(a.heads / kDecHeads), (unsigned)a.rows);
-    hipLaunchKernelGGL((decode_partial_kernel<MS, MV, PC>), grid, dim3(kDecThreads),
+    hipLaunchKernelGGL((decode_partial_kernel<MS, MV, PC, XQ, XV>), grid, dim3(kDecThreads),
                        decode_lds_bytes(a.dqk), stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_partial(const DecodeArgs &a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
+    if (a.dqk == 576 && a.dv == 512)   // the MLA shape, exactly
+        return launch_partial<kDecStepsSmall, kDecVTilesSmall, kDecChunksSmall, 576, 512>(a, stream);
     if (a.dqk <= 16 * 4 * kDecStepsSmall && a.dv <= 64 * kDecVTilesSmall)
         return launch_partial<kDecStepsSmall, kDecVTilesSmall, kDecChunksSmall>(a, stream);
     return launch_partial<kDecStepsMax, kDecVTilesMax, kDecChunksMax>(a, stream);
