@@ -115,3 +115,15 @@ def test_many_rows_and_one_row():
     qm = workloads.bf16_round(g.standard_normal((600, 16, dqk)).astype(np.float32))
     im = np.stack([g.choice(n, size=64, replace=False) for _ in range(600)]).astype(np.int32)
     check(qm, kv, im, dv, 1.0 / 24.0, what="600 rows", rows=[0, 299, 599], kv_dev=kvd)
+
+
+def test_long_splits_load_positions_per_tile():
+    # 300 rows of 16 heads fill the GPU with one split per row, so each split
+    # walks all 1,000 positions (more than a split keeps in LDS)
+    g = np.random.Generator(np.random.PCG64(9))
+    n, dqk, dv = 6000, 576, 512
+    kv = workloads.bf16_round(g.standard_normal((n, dqk)).astype(np.float32))
+    q = workloads.bf16_round(g.standard_normal((300, 16, dqk)).astype(np.float32))
+    idx = np.stack([g.choice(n, size=1000, replace=False) for _ in range(300)]).astype(np.int32)
+    idx[5, 700:] = -1
+    check(q, kv, idx, dv, 1.0 / 24.0, what="long splits", rows=[0, 5, 150, 299])
