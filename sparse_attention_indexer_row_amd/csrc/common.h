@@ -38,6 +38,10 @@ TOPK_HD uint64_t pack_word(uint32_t key, uint32_t pos) {
 
 TOPK_HD uint32_t word_pos(uint64_t w) { return 0xFFFFFFFFu - (uint32_t)w; }
 
+// Four floats as a native vector (the operand type of the buffer-load
+// builtins).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 // Largest key that is not a real number: keys at or below it are negative
 // NaN patterns, key 0x007FFFFF is -inf itself.
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;

@@ -731,7 +731,6 @@ struct RowGeom {
     uint32_t L;            // valid positions
     uint32_t vend;         // L + off0
     uint32_t nb;           // blocks
-    uint32_t last_group;   // last aligned 4-group holding a valid position
 };
 
 __device__ __forceinline__ RowGeom row_geometry(const SelectArgs &p, uint32_t r) {
@@ -747,8 +746,33 @@ __device__ __forceinline__ RowGeom row_geometry(const SelectArgs &p, uint32_t r)
     g.L = (uint32_t)L;
     g.vend = g.L + g.off0;
     g.nb = L > 0 ? (g.vend + kBlock - 1) / kBlock : 0u;
-    g.last_group = L > 0 ? ((g.vend - 1u) & ~3u) : 0u;
     return g;
+}
+
+// Buffer resource over the 4 KiB of block b (virtual positions
+// [1024 b, 1024 b + 1024)).  Its size stops at the row's valid end rounded up
+// to a whole 16-byte group, so loads beyond it return zeros; the rounding
+// reads at most three positions past the row, inside the 16-byte group that
+// holds its last score.  Positions before the row's start (its misalignment)
+// lie in the same 16-byte group as its first score.
+constexpr int kRsrcWord3 = 0x00020000;   // buffer format word for gfx9-family cores
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const RowGeom &g, uint32_t b) {
+    const uint32_t vb = b * (uint32_t)kBlock;
+    const uint32_t vend4 = (g.vend + 3u) & ~3u;
+    const uint32_t left = vend4 > vb ? vend4 - vb : 0u;
+    const uint32_t nrec = (left < (uint32_t)kBlock ? left : (uint32_t)kBlock) * 4u;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(g.abase + vb), (short)0, (int)nrec,
+                                             kRsrcWord3);
+}
+
+// One 16-byte load of scores at byte offset `off` of a block resource,
+// with the nontemporal hint (scores are read once).
+constexpr int kLoadNontemporal = 2;
+
+__device__ __forceinline__ float4 load_block4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    const f32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, kLoadNontemporal);
+    return make_float4(v.x, v.y, v.z, v.w);
 }
 
 // Sampled threshold estimate ("The Secret GPU Kernel Behind DeepSeek V4.1
@@ -835,6 +859,24 @@ __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t
                       position_bits(g.L), hist, gath, lane);
 }
 
+// A stream's bound from one block: at least 64*E >= k scores of the block
+// have keys >= kb, so (kb << 32) is at most the row's k-th best word.  Raises
+// the stream's threshold and the workgroup's (and, for split rows, the
+// row's).
+template <bool SPLIT>
+__device__ __forceinline__ void raise_stream_bound(uint64_t &T, uint32_t kb, uint64_t *sT,
+                                                   uint64_t *gT, uint32_t lane) {
+    const uint64_t lb = (uint64_t)kb << 32;
+    if (lb <= T) return;
+    T = lb;
+    if (lane == 0) {
+        __hip_atomic_fetch_max(sT, lb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if constexpr (SPLIT) {
+            __hip_atomic_fetch_max(gT, lb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 // Streams this wave's share of a row's blocks once: visit positions q, q+Q,
 // ... of the row's visit order.  Scores whose word beats max(threshold,
 // estimate) go to the tray; full trays are published to the sorter.  Returns
@@ -889,21 +931,17 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
         }
         return (uint32_t)__builtin_amdgcn_readlane((int)vis, (int)(tt - c0));
     };
+    // Each block is read through a buffer resource covering it: a load past
+    // the row's valid end returns zeros instead of touching memory, so every
+    // block, ragged or not, issues the same four loads from a scalar base
+    // and one fixed per-lane offset (no per-lane address arithmetic, which
+    // lets the loads of the blocks in flight overlap).
+    const uint32_t lane_off = lane * 16u;
     auto issue = [&](float4 (&dst)[kLoadsPerBlock], uint32_t b) __attribute__((always_inline)) {
-        const uint32_t vbase = b * (uint32_t)kBlock;
-        if (vbase >= g.off0 && vbase + (uint32_t)kBlock <= g.vend) {
-            const float *bp = g.abase + vbase;
+        const __amdgpu_buffer_rsrc_t rs = block_rsrc(g, b);
 #pragma unroll
-            for (int u = 0; u < kLoadsPerBlock; ++u) {
-                dst[u] = *reinterpret_cast<const float4 *>(bp + u * 256 + lane * 4u);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < kLoadsPerBlock; ++u) {
-                uint32_t gp = vbase + (uint32_t)u * 256u + lane * 4u;
-                gp = gp > g.last_group ? g.last_group : gp;   // stay on a valid group
-                dst[u] = *reinterpret_cast<const float4 *>(g.abase + gp);
-            }
+        for (int u = 0; u < kLoadsPerBlock; ++u) {
+            dst[u] = load_block4(rs, lane_off + (uint32_t)u * 1024u);
         }
     };
 #pragma unroll
@@ -954,19 +992,8 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                     if (!ragged && cnt - before >= (uint32_t)(kWave * E)) {
                         // This block alone filled a kept list's worth of the
                         // tray (a sorted run, say): bound the k-th best by it.
-                        const uint32_t kb = wave_min32(block_rank_key<E>(buf[d]), lane);
-                        const uint64_t lb = (uint64_t)kb << 32;
-                        if (lb > T) {
-                            T = lb;
-                            if (lane == 0) {
-                                __hip_atomic_fetch_max(sT, lb, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-                                if constexpr (SPLIT) {
-                                    __hip_atomic_fetch_max(gT, lb, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT);
-                                }
-                            }
-                        }
+                        raise_stream_bound<SPLIT>(T, wave_min32(block_rank_key<E>(buf[d]), lane),
+                                                  sT, gT, lane);
                     }
                 }
                 if (lane_bounds && cnt != before) {
