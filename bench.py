@@ -79,9 +79,32 @@ def profile_target(workload: str):
 
 
 def routed_to_radix(rows: int, n: int, k: int, cus: int) -> bool:
-    """topk_select's choice of the radix path (the library's rule, mirrored
-    here to label the kernel a workload runs)."""
-    return n <= 262144 and ((k > 1024 and rows * 4 >= cus) or (k > 512 and rows * 2 >= cus))
+    """Whether topk_select takes the radix path for this shape: the library's
+    own plan (no launch), used to label the kernel a workload runs.  `cus`
+    is kept for the callers; the plan queries the device itself."""
+    from sparse_attention_indexer_row_amd import _lib, api
+    return api.topk_plan(rows, n, k, for_select=True)["path"] == _lib.TOPK_PATH_RADIX
+
+
+def decode_bound(q, kv, idx, scale, dv):
+    """Per-element tolerance of the decode's parity check, in float64:
+    2^-7 * sum_j p_j |v_jc| + 1e-6 with p the exact softmax of the selected
+    positions -- twice what bf16-rounded softmax weights can move a convex
+    combination (the same bound as the GPU tests')."""
+    import numpy as np
+    rows, heads, _ = q.shape
+    n = kv.shape[0]
+    out = np.full((rows, heads, dv), 1e-6)
+    for r in range(rows):
+        j = idx[r][(idx[r] >= 0) & (idx[r] < n)].astype(np.int64)
+        if j.size == 0:
+            continue
+        keys = kv[j].astype(np.float64)
+        logits = scale * (q[r].astype(np.float64) @ keys.T)
+        p = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        out[r] += 2.0 ** -7 * (p @ np.abs(keys[:, :dv]))
+    return out
 
 
 def decode_read_bytes(w) -> int:
@@ -269,8 +292,8 @@ def make_case(name, dev, np, torch, api, workloads):
             ok = True
             for r in sample:
                 want = sparse_decode(w.q[r:r + 1], w.kv, w.idx[r:r + 1], w.scale, w.dv)[0]
-                vmax = float(np.abs(w.kv[w.idx[r], :w.dv]).max())
-                ok = ok and float(np.abs(got[r] - want).max()) <= 2.0 ** -7 * vmax + 1e-6
+                bound = decode_bound(w.q[r:r + 1], w.kv, w.idx[r:r + 1], w.scale, w.dv)[0]
+                ok = ok and bool(np.all(np.abs(got[r] - want) <= bound))
             return ok, sample
 
         def cpu(cores):
@@ -282,7 +305,8 @@ def make_case(name, dev, np, torch, api, workloads):
         c.update(rows=rows, read_bytes=decode_read_bytes(w), copies=1, step=step, parity=parity,
                  cpu=cpu, cpu_cores=lambda cores: 1,
                  kernel="decode_partial_kernel + decode_combine_kernel (whole call)",
-                 parity_kind="within 2^-7 max|v| of the float64 oracle",
+                 parity_kind="within 2^-7 sum_j p_j |v_jc| + 1e-6 of the float64 oracle, "
+                             "per element",
                  metric="effective HBM read GB/s of gathered bf16 cache rows for sparse-attention "
                         "decode over 512 selected positions (16 heads, dqk 576, dv 512)",
                  config={"workload": w.description, "rows": rows, "heads": heads, "dqk": dqk,

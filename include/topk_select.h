@@ -58,55 +58,84 @@ extern "C" {
 #define TOPK_EDEVICE (-6)    /* no usable gfx950 device / runtime query failed */
 #define TOPK_EALLOC (-7)     /* library-owned workspace allocation failed     */
 
-/* Largest k of the streaming selection (topk_select_radix goes to 8,192). */
-#define TOPK_MAX_K 2048
+/* Largest k of topk_select, topk_select_split and topk_select_ex: the
+ * page's own kernel stops near k = 4,000 ("The Secret GPU Kernel Behind
+ * DeepSeek V4.1 Flash", transcript 5:45).  Lists up to 2,048 words run the
+ * streaming filter; wider lists (k > 2,048) run the per-row radix selection
+ * of topk_select_radix, one workgroup per row, with the same result. */
+#define TOPK_MAX_K 4096
+/* Largest k the streaming filter itself takes (its kept lists sit in
+ * registers); above it the calls take the radix path. */
+#define TOPK_MAX_K_STREAM 2048
 /* Largest number of workgroups one row may be split across. */
 #define TOPK_MAX_SPLIT 1024
 
 /*
- * topk_select -- top-k of every row, planned automatically.
+ * topk_select -- top-k of every row, planned automatically ("The Secret GPU
+ * Kernel Behind DeepSeek V4.1 Flash", transcript 2:40-4:20: keep the best k
+ * of a row of indexer scores by one comparison per score against a rising
+ * threshold; 5:45: k up to about 4,000).
  *
- * Chooses one workgroup per row or, when rows alone cannot fill the GPU,
- * splits each row across several workgroups (transcript 5:22-5:33).  On
- * rows of at most 262,144 scores it runs topk_select_radix instead (same
- * result; faster there) when k > 1024 with at least a quarter as many rows
- * as compute units, or k > 512 with at least half as many.  A split
- * call uses a library-owned, grow-only workspace per device, allocated with
- * hipMalloc on the first call that needs a larger one (so the first such call
- * is not graph-capturable; use topk_select_split for capture).  Calls that
- * share this internal workspace must be ordered on one stream.
+ * 1 <= k <= TOPK_MAX_K (TOPK_EK_RANGE otherwise).  Chooses one workgroup
+ * per row or, when rows alone cannot fill the GPU, splits each row across
+ * several workgroups (transcript 5:22-5:33).  It runs topk_select_radix
+ * instead (same result) when k > TOPK_MAX_K_STREAM, and on rows of at most
+ * 262,144 scores when k > 1024 with at least a quarter as many rows as
+ * compute units, or k > 512 with at least half as many (measured faster
+ * there).  A split call uses a library-owned, grow-only workspace per
+ * device, allocated with hipMalloc on the first call that needs a larger one
+ * (so the first such call is not graph-capturable; use topk_select_split
+ * for capture).  Calls that share this internal workspace must be ordered
+ * on one stream.  The visit order's seed changes from call to call (a
+ * per-device counter), so the order in which a row's blocks are read cannot
+ * be predicted from the input (transcript 4:55-5:10); the result never
+ * depends on it.
  */
 int topk_select(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
                 int32_t k, float *out_vals, int32_t *out_idx, void *stream);
 
 /*
- * topk_split_workspace_bytes -- device bytes topk_select_split needs.
- * `split` == 0 means the automatic choice.  Returns 0 for invalid arguments.
- * The workspace holds per-row threshold and ticket words, one arrival ticket
- * per group of eight of a row's workgroups, and one k-list per (row, split)
- * pair.
+ * topk_split_workspace_bytes -- device bytes topk_select_split needs for
+ * the split-row mode ("The Secret GPU Kernel Behind DeepSeek V4.1 Flash",
+ * transcript 5:22-5:33: when the batch is too small to fill the chip, one
+ * row is spread over several compute units that each keep a local top-k,
+ * and a leader merges their winners).  `split` == 0 means the automatic
+ * choice.  Returns 0 when no workspace is needed (split 1, or k above
+ * TOPK_MAX_K_STREAM) and for invalid arguments.  The workspace holds per-row
+ * threshold and ticket words, one arrival ticket per group of eight of a
+ * row's workgroups, and one k-list per (row, split) pair.
  */
 size_t topk_split_workspace_bytes(int32_t rows, int32_t n, int32_t k, int32_t split);
 
 /*
- * topk_workspace_init -- zero a caller-owned workspace once, before its first
- * use, with a fill kernel on `stream` (no memset node, so it can be captured).
- * The split path leaves the workspace zeroed again at the end of every call.
- * `workspace` must be 256-byte aligned.
+ * topk_workspace_init -- zero a caller-owned split-row workspace once,
+ * before its first use, with a fill kernel on `stream` (no memset node, so it
+ * can be captured).  The split path resets its tickets and shared
+ * threshold words at the end of every call, so the workspace is all zero
+ * again between calls (kernelbench.com "DeepSeek V4.1 Flash", Kimi-Linear
+ * paragraph: an accumulator that is never reset corrupts the next launch).
+ * `workspace` must be 256-byte aligned and workspace_bytes a multiple of 16
+ * (TOPK_EWORKSPACE otherwise); workspace_bytes == 0 does nothing.
  */
 int topk_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * topk_select_split -- top-k with each row split across `split` workgroups
- * (0 = automatic, 1 = no split).  Each workgroup keeps a local top-k of its
- * share of the row's blocks; workgroups of a row share a rising threshold
- * through the workspace.  The last of each group of eight workgroups to
- * finish (elected by an atomic ticket) merges the group's lists, and the last
- * group to finish merges the groups' lists and writes the row's output.
- * `workspace` is
- * caller-owned device memory of at least topk_split_workspace_bytes(...),
- * 256-byte aligned, zeroed once by topk_workspace_init.  Allocates nothing.
- * Two calls that use one workspace must not run concurrently.
+ * (0 = automatic, 1 = no split), the split-row mode of "The Secret GPU
+ * Kernel Behind DeepSeek V4.1 Flash", transcript 5:22-5:33.  Each workgroup
+ * keeps a local top-k of its share of the row's blocks; workgroups of a row
+ * share a rising threshold through the workspace.  The last of each group of
+ * eight workgroups to finish (elected by an atomic ticket, as the split-KV
+ * decode of kernelbench.com "DeepSeek V4.1 Flash" elects its merging
+ * workgroup) merges the group's lists, and the last group to finish merges
+ * the groups' lists and writes the row's output.  `workspace` is caller-owned
+ * device memory of at least topk_split_workspace_bytes(...), 256-byte
+ * aligned, zeroed once by topk_workspace_init.  Allocates nothing.  Two calls
+ * that use one workspace must not run concurrently.  With
+ * k > TOPK_MAX_K_STREAM the rows run the radix selection, one workgroup per
+ * row: `split` is checked but not used and the workspace may be NULL (a
+ * wide list leaves no room for several segments' lists in one workgroup's
+ * registers; the radix path's own per-row time is short).
  */
 int topk_select_split(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
                       int32_t k, float *out_vals, int32_t *out_idx, int32_t split,
@@ -136,14 +165,37 @@ typedef struct {
 } topk_options;
 
 /*
- * topk_select_ex -- topk_select_split with explicit options.  `workspace`
- * may be NULL when the plan has split == 1.
+ * topk_select_ex -- topk_select_split with explicit options: the visit
+ * order's seed ("The Secret GPU Kernel Behind DeepSeek V4.1 Flash",
+ * transcript 4:55-5:10: blocks visited in a shuffled order that does not
+ * depend on the data), the split (5:22-5:33), the waves per workgroup, the
+ * tray watermark (3:55-4:08: the tray is sorted only once it passes its
+ * mark), the sampled estimate (10:57-11:09 and 11:47-12:10: start from an
+ * estimated threshold and still return the exact answer) and per-row counts
+ * of scores that entered a tray (4:45-4:55: the bound on elements that ever
+ * reach a sort).  `workspace` may be NULL when the plan has split == 1.
+ * Every option is range-checked for every k.  With k > TOPK_MAX_K_STREAM
+ * the rows run the radix selection, where seed, split, waves, watermark and
+ * the flags do not apply and `stats` is left untouched.
  */
 int topk_select_ex(const float *scores, const int32_t *lengths, int32_t rows, int32_t n,
                    int32_t k, float *out_vals, int32_t *out_idx, const topk_options *opts,
                    void *workspace, size_t workspace_bytes, void *stream);
 
-/* The plan a call would use (host only, no launch). */
+/* Paths a plan can take. */
+#define TOPK_PATH_STREAM 0   /* the streaming threshold filter (select_kernel) */
+#define TOPK_PATH_RADIX 1    /* the per-row radix selection (topk_select_radix) */
+
+/*
+ * topk_plan -- the plan a call would use (host only, no launch): the
+ * split-row choice ("The Secret GPU Kernel Behind DeepSeek V4.1 Flash",
+ * transcript 5:22-5:33), the tray and its watermark (3:55-4:08) and the
+ * LDS they take.  With opts == NULL it is topk_select's plan (including its
+ * routing to the radix path); otherwise topk_select_ex's with those options.
+ * A radix plan has split 1, waves 16, list_words = the winners' sort size
+ * (k rounded up to a power of two), watermark and tray_words 0, and no
+ * workspace.  Status codes as for topk_select_ex.
+ */
 typedef struct {
     int32_t split;           /* workgroups per row                      */
     int32_t waves;           /* waves per workgroup                     */
@@ -152,7 +204,7 @@ typedef struct {
     int32_t tray_words;      /* tray capacity per wave                  */
     int32_t lds_bytes;       /* dynamic LDS per workgroup               */
     int32_t compute_units;   /* compute units the plan assumed          */
-    int32_t reserved;
+    int32_t path;            /* TOPK_PATH_STREAM or TOPK_PATH_RADIX     */
     size_t workspace_bytes;  /* 0 when split == 1                       */
 } topk_plan_t;
 
@@ -181,7 +233,7 @@ int topk_plan(int32_t rows, int32_t n, int32_t k, const topk_options *opts, topk
  *   block count.
  *
  * group >= 1, keep >= 1, 0 <= pinned <= keep, keep - pinned <= TOPK_MAX_K
- * (TOPK_EINVAL / TOPK_EK_RANGE otherwise).  out_vals: fp32 [rows][keep],
+ * (TOPK_EINVAL / TOPK_EK_RANGE otherwise; the page keeps 2,000 blocks).  out_vals: fp32 [rows][keep],
  * out_idx: int32 [rows][keep], device pointers owned by the caller.
  * Work: one pass over the scores writing ceil(n / group) block maxima per row
  * into a library-owned, grow-only device buffer, then the radix selection of
@@ -245,8 +297,10 @@ int topk_sparse_decode(const void *q, const void *kv, const int32_t *idx, int32_
                        int32_t heads, int64_t n_kv, int32_t k, int32_t dqk, int32_t dv,
                        float scale, float *out, void *stream);
 
-/* Most pool slots topk_pooled_select takes per row. */
+/* Most pool slots topk_pooled_select takes per row, and its largest k (its
+ * radix selection keeps the pool's slots in LDS beside the winners). */
 #define TOPK_MAX_POOL_SLOTS 8192
+#define TOPK_MAX_K_POOLED 2048
 
 /*
  * topk_pooled_select -- top-k inside a block pool ("The Secret GPU Kernel
@@ -268,7 +322,7 @@ int topk_sparse_decode(const void *q, const void *kv, const int32_t *idx, int32_
  * Precondition: a row's block indices are distinct and below 2^31 / group
  * (a pool never repeats a block); otherwise the output is unspecified but
  * the call stays memory-safe.  1 <= keep <= TOPK_MAX_POOL_SLOTS, group >= 1
- * (TOPK_EINVAL otherwise), 1 <= k <= TOPK_MAX_K (TOPK_EK_RANGE).
+ * (TOPK_EINVAL otherwise), 1 <= k <= TOPK_MAX_K_POOLED (TOPK_EK_RANGE).
  * Work: one kernel, the radix selection of topk_select_radix, one workgroup
  * per row, with each pooled score's word carrying its context position (so
  * ties resolve by position without reordering the pool).  Allocates nothing.
@@ -278,18 +332,26 @@ int topk_pooled_select(const float *pool_scores, const int32_t *pool_idx,
                        int32_t keep, int32_t k, float *out_vals, int32_t *out_idx,
                        void *stream);
 
-/* Human-readable text for a status code (static storage). */
+/* Human-readable text for a status code (static storage); the codes are the
+ * argument checks every entry point above makes before any HIP call. */
 const char *topk_strerror(int status);
 
 /*
- * topk_visit_order -- host-side copy of the block visit order for row `row`
- * of a row with `nblocks` 1,024-element blocks: out[p] = block visited at
- * step p.  A diagnostic for tests; it is the same function the kernel uses.
+ * topk_visit_order -- host-side copy of the block visit order ("The Secret
+ * GPU Kernel Behind DeepSeek V4.1 Flash", transcript 3:30 and 4:55-5:10:
+ * 1,024-element blocks visited in a shuffled order drawn without looking at
+ * the data) for row `row` of a row with `nblocks` blocks: out[p] = block
+ * visited at step p.  A diagnostic for tests; it is the same function the
+ * kernel uses.  TOPK_EINVAL for negative sizes or a NULL `out`.
  */
 int topk_visit_order(uint64_t seed, int32_t row, int32_t nblocks, int32_t *out);
 
 /*
- * Streaming probes used to measure the machine, not part of the selection:
+ * Streaming probes used to measure the machine, not part of the selection
+ * (kernelbench.com "DeepSeek V4.1 Flash", split-KV decode paragraph: a
+ * bandwidth roof taken from a weak measured read sits well short of what
+ * the GPU delivers, so the roof here is measured with the selection's own
+ * load pattern):
  * topk_probe_read reads `bytes` (multiple of 16) from `src` once with the
  * selection kernel's load pattern and writes one word per workgroup into
  * `sink` (at least topk_probe_sink_words(bytes) uint32 words), so the read

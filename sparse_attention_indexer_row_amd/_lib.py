@@ -21,7 +21,11 @@ TOPK_ESPLIT = -4
 TOPK_ELAUNCH = -5
 TOPK_EDEVICE = -6
 TOPK_EALLOC = -7
-TOPK_MAX_K = 2048
+TOPK_MAX_K = 4096
+TOPK_MAX_K_STREAM = 2048
+TOPK_MAX_K_POOLED = 2048
+TOPK_PATH_STREAM = 0
+TOPK_PATH_RADIX = 1
 TOPK_FLAG_NO_ESTIMATE = 1
 TOPK_FLAG_FORCE_RERUN = 2
 TOPK_MAX_SPLIT = 1024
@@ -68,7 +72,7 @@ class TopkPlan(ctypes.Structure):
         ("tray_words", ctypes.c_int32),
         ("lds_bytes", ctypes.c_int32),
         ("compute_units", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("path", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

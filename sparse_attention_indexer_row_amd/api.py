@@ -143,11 +143,14 @@ def topk_select_ex(scores: torch.Tensor, k: int, lengths: torch.Tensor | None = 
 
 
 def topk_plan(rows: int, n: int, k: int, *, split: int = 0, waves: int = 0,
-              watermark: int = 0) -> dict:
+              watermark: int = 0, for_select: bool = False) -> dict:
+    """The launch plan.  ``for_select``: topk_select's own plan (no options,
+    its routing included); otherwise topk_select_ex's with these options."""
     o = _options(0, split, waves, watermark, None)
     p = TopkPlan()
-    _lib.check(_lib.load().topk_plan(rows, n, k, ctypes.byref(o), ctypes.byref(p)), "topk_plan")
-    return {f: getattr(p, f) for f, _ in TopkPlan._fields_ if f != "reserved"}
+    opt = None if for_select else ctypes.byref(o)
+    _lib.check(_lib.load().topk_plan(rows, n, k, opt, ctypes.byref(p)), "topk_plan")
+    return {f: getattr(p, f) for f, _ in TopkPlan._fields_}
 
 
 def topk_select_radix(scores: torch.Tensor, k: int, lengths: torch.Tensor | None = None,

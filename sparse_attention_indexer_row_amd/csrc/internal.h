@@ -54,6 +54,9 @@ struct RadixArgs {
 };
 
 hipError_t launch_radix_select(const RadixArgs &a, hipStream_t stream);
+// Dynamic LDS of the radix selection's launch for list size k (pool_keep
+// slots kept in LDS for pooled rows, 0 otherwise).
+size_t radix_lds_bytes(int k, int pool_keep);
 
 // Sparse-attention decode over selected positions.
 constexpr int kMaxDecodeDqk = 1024;

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kPoolThreads) void block_max8_kernel(PoolArgs a) {
 // LDS ordering; a workgroup barrier is needed around the wider stages.
 // The caller syncs before; the function ends with a barrier.
 template <int THREADS, bool DESC>
-__device__ void lds_bitonic(uint64_t *x, uint32_t p2) {
+__device__ __forceinline__ void lds_bitonic(uint64_t *x, uint32_t p2) {
     const uint32_t tid = threadIdx.x;
     for (uint32_t size = 2; size <= p2; size <<= 1) {
         for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
@@ -412,7 +412,7 @@ __device__ __forceinline__ void wave_append(uint64_t *buf, uint32_t *counter, ui
 // every run with a register merge.  For 4,096 words: 10 LDS stages instead
 // of the plain network's 78.  The caller syncs before; ends with a barrier.
 template <int E>
-__device__ void run_sort_desc(uint64_t *x, uint32_t p2, uint32_t nw) {
+__device__ __forceinline__ void run_sort_desc(uint64_t *x, uint32_t p2, uint32_t nw) {
     constexpr uint32_t R = 64u * E;
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     const bool active = w < nw;
@@ -510,8 +510,15 @@ __device__ __forceinline__ void radix_pick(const uint32_t *hist, uint32_t need, 
 // Exact radix search in LDS: for `need` <= n distinct words buf[0, n),
 // returns (shift, thr) such that exactly `need` of them satisfy
 // (w >> shift) >= thr.  All threads of the workgroup call it together.
-__device__ void lds_radix(const uint64_t *buf, uint32_t n, uint32_t need, uint32_t *hist,
-                          RadixShared &sh, int &thr_shift, uint64_t &thr) {
+// Inlined, with the result returned by value, so the kernel makes no calls
+// and keeps nothing on the stack.
+struct RadixCut {
+    int shift;
+    uint64_t thr;
+};
+
+__device__ __forceinline__ RadixCut lds_radix(const uint64_t *buf, uint32_t n, uint32_t need,
+                                              uint32_t *hist, RadixShared &sh) {
     const int tid = threadIdx.x;
     const uint32_t lane = (uint32_t)tid & (kWave - 1);
     uint64_t pfx = 0;
@@ -531,11 +538,7 @@ __device__ void lds_radix(const uint64_t *buf, uint32_t n, uint32_t need, uint32
         __syncthreads();  // everyone has read the pick before the next scan writes it
         need -= above;
         pfx = level == 0 ? (uint64_t)t : ((pfx << (ps - s)) | t);
-        if (h == need || level == kRadixLevels - 1) {
-            thr_shift = s;
-            thr = pfx;
-            return;
-        }
+        if (h == need || level == kRadixLevels - 1) return RadixCut{s, pfx};
     }
 }
 
@@ -627,16 +630,16 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
                 samp[q] = wm(row[i], i);
             }
             __syncthreads();
-            int es = 0;
-            uint64_t et = 0;
-            lds_radix(samp, kSampleWords, j, hist, sh, es, et);
+            const RadixCut ec = lds_radix(samp, kSampleWords, j, hist, sh);
             __syncthreads();  // the sample is read before the admission pass overwrites it
-            const uint64_t est = et << es;   // words >= est: j in the sample
+            const uint64_t est = ec.thr << ec.shift;   // words >= est: j in the sample
             append_at_least(row, m, wm, est, cand, &sh.ncand, kRadixCand);
             __syncthreads();
             const uint32_t nc = sh.ncand;
             if (nc >= k && nc <= (uint32_t)kRadixCand) {
-                lds_radix(cand, nc, k, hist, sh, thr_shift, thr);
+                const RadixCut c = lds_radix(cand, nc, k, hist, sh);
+                thr_shift = c.shift;
+                thr = c.thr;
                 for (uint32_t c = tid; c - lane < nc; c += kRadixThreads) {
                     const uint64_t w = c < nc ? cand[c] : 0ull;
                     wave_append(sel, &sh.nsel, kRadixSel, w, c < nc && (w >> thr_shift) >= thr);
@@ -692,7 +695,9 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
                 });
                 __syncthreads();
                 const uint32_t nc = sh.ncand;
-                lds_radix(cand, nc, need, hist, sh, thr_shift, thr);
+                const RadixCut c = lds_radix(cand, nc, need, hist, sh);
+                thr_shift = c.shift;
+                thr = c.thr;
                 for (uint32_t c = tid; c - lane < nc; c += kRadixThreads) {
                     const uint64_t w = c < nc ? cand[c] : 0ull;
                     wave_append(sel, &sh.nsel, kRadixSel, w, c < nc && (w >> thr_shift) >= thr);
@@ -744,6 +749,11 @@ hipError_t launch_radix_words(const RadixArgs &a, hipStream_t stream) {
     if (a.k <= RadixSmall::kSel) return launch_radix_cap<RadixSmall, Words>(a, stream);
     if (a.k <= RadixLarge::kSel) return launch_radix_cap<RadixLarge, Words>(a, stream);
     return hipErrorInvalidValue;
+}
+
+size_t radix_lds_bytes(int k, int pool_keep) {
+    const size_t slots = pool_keep > 0 ? pooled_slot_bytes(pool_keep) : 0;
+    return (k <= RadixSmall::kSel ? RadixSmall::kLds : RadixLarge::kLds) + slots;
 }
 
 hipError_t launch_radix_select(const RadixArgs &a, hipStream_t stream) {

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 
@@ -249,17 +250,67 @@ constexpr int64_t kPoolRowAlign = 64;
 constexpr int32_t kMaxGridRows = 65535;
 
 // Where topk_select takes the per-row radix selection instead of the
-// streaming filter: rows no longer than 262,144 scores with lists of 1,024
+// streaming filter: every k above the filter's widest list, and rows no
+// longer than 262,144 scores with lists of 1,024
 // words (k > 512) and at least half as many rows as compute units, or
 // lists of 2,048 words (k > 1,024) and at least a quarter as many.  There
 // the streaming path's wide lists spend their time sorting, while one
 // workgroup per row keeps the GPU busy (measured 1.2-2.6x faster on such
 // shapes; slower on million-score rows, at k <= 512, or with fewer rows).
 bool prefer_radix(int32_t rows, int32_t n, int32_t k, int cus) {
+    if (k > TOPK_MAX_K_STREAM) return true;   // wider than the streaming filter's lists
     if (n > 262144) return false;
     if (k > 1024) return (int64_t)rows * 4 >= cus;
     if (k > 512) return (int64_t)rows * 2 >= cus;
     return false;
+}
+
+// The radix selection over every row (one workgroup per row), in launches of
+// at most kMaxGridRows rows.
+int run_radix(const float *scores, const int32_t *lengths, int32_t rows, int32_t n, int32_t k,
+              float *out_vals, int32_t *out_idx, hipStream_t stream) {
+    topk::RadixArgs x{};
+    x.vals = scores;
+    x.count = lengths;
+    x.ld = n;
+    x.k = k;
+    x.out_vals = out_vals;
+    x.out_idx = out_idx;
+    x.out_ld = k;
+    for (int32_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
+        x.row0 = r0;
+        x.rows = std::min(kMaxGridRows, rows - r0);
+        if (topk::launch_radix_select(x, stream) != hipSuccess) return TOPK_ELAUNCH;
+    }
+    return TOPK_OK;
+}
+
+// A radix plan (one workgroup of 16 waves per row, no workspace).
+topk_plan_t radix_plan(int32_t k, int cus) {
+    topk_plan_t p{};
+    int32_t p2 = 2;
+    while (p2 < k) p2 <<= 1;
+    p.split = 1;
+    p.waves = 16;
+    p.list_words = p2;
+    p.watermark = 0;
+    p.tray_words = 0;
+    p.lds_bytes = (int32_t)topk::radix_lds_bytes(k, 0);
+    p.compute_units = cus;
+    p.path = TOPK_PATH_RADIX;
+    p.workspace_bytes = 0;
+    return p;
+}
+
+// topk_select's visit-order seed: a per-device call counter run through
+// splitmix64, so consecutive calls read a row's blocks in unrelated orders.
+std::atomic<uint64_t> g_calls[kMaxDevices];
+
+uint64_t next_seed() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+    const uint64_t c = g_calls[dev].fetch_add(1, std::memory_order_relaxed);
+    return topk::splitmix64(c ^ ((uint64_t)dev << 56));
 }
 
 }  // namespace
@@ -277,6 +328,10 @@ int topk_plan(int32_t rows, int32_t n, int32_t k, const topk_options *opts, topk
     int count = 0;
     if (hipGetDeviceCount(&count) == hipSuccess && count > 0 && device_cus(&dev_cus) == TOPK_OK)
         cus = dev_cus;
+    if (k > TOPK_MAX_K_STREAM || (!opts && prefer_radix(rows, n, k, cus))) {
+        *out = radix_plan(k, cus);
+        return TOPK_OK;
+    }
     Plan p = make_plan(rows, n, k, opts, cus);
     st = check_plan(p);
     if (st != TOPK_OK) return st;
@@ -287,13 +342,14 @@ int topk_plan(int32_t rows, int32_t n, int32_t k, const topk_options *opts, topk
     out->tray_words = p.tray;
     out->lds_bytes = (int32_t)p.lds;
     out->compute_units = p.cus;
-    out->reserved = 0;
+    out->path = TOPK_PATH_STREAM;
     out->workspace_bytes = p.ws_bytes;
     return TOPK_OK;
 }
 
 size_t topk_split_workspace_bytes(int32_t rows, int32_t n, int32_t k, int32_t split) {
-    if (rows < 0 || n < 1 || k < 1 || k > TOPK_MAX_K || split < 0 || split > TOPK_MAX_SPLIT)
+    if (rows < 0 || n < 1 || k < 1 || k > TOPK_MAX_K_STREAM || split < 0 ||
+        split > TOPK_MAX_SPLIT)
         return 0;
     topk_options o{};
     o.split = split;
@@ -319,6 +375,11 @@ int topk_select_ex(const float *scores, const int32_t *lengths, int32_t rows, in
     st = check_options(opts);
     if (st != TOPK_OK) return st;
     if (workspace && misaligned(workspace, kAlign)) return TOPK_EWORKSPACE;
+    if (k > TOPK_MAX_K_STREAM) {
+        // Wider than the streaming filter's lists: the radix selection.
+        if (rows == 0) return TOPK_OK;
+        return run_radix(scores, lengths, rows, n, k, out_vals, out_idx, (hipStream_t)stream);
+    }
     // Whether the launch fits does not depend on the device's CU count, so
     // it is checked with the other arguments, before any HIP call.
     st = check_plan(make_plan(rows, n, k, opts, kAssumedCUs));
@@ -353,14 +414,14 @@ int topk_select(const float *scores, const int32_t *lengths, int32_t rows, int32
     st = device_cus(&cus);
     if (st != TOPK_OK) return st;
     if (prefer_radix(rows, n, k, cus))
-        return topk_select_radix(scores, lengths, rows, n, k, out_vals, out_idx, stream);
+        return run_radix(scores, lengths, rows, n, k, out_vals, out_idx, (hipStream_t)stream);
     Plan pl = make_plan(rows, n, k, nullptr, cus);
     void *ws = nullptr;
     if (pl.split > 1) {
         st = internal_workspace(pl.ws_bytes, (hipStream_t)stream, &ws);
         if (st != TOPK_OK) return st;
     }
-    return run(scores, lengths, rows, n, k, out_vals, out_idx, pl, ws, 0, 0u, nullptr,
+    return run(scores, lengths, rows, n, k, out_vals, out_idx, pl, ws, next_seed(), 0u, nullptr,
                (hipStream_t)stream);
 }
 
@@ -432,20 +493,7 @@ int topk_select_radix(const float *scores, const int32_t *lengths, int32_t rows,
     if (misaligned(scores, 4) || misaligned(out_vals, 4) || misaligned(out_idx, 4) ||
         (lengths && misaligned(lengths, 4)))
         return TOPK_EINVAL;
-    topk::RadixArgs x{};
-    x.vals = scores;
-    x.count = lengths;
-    x.ld = n;
-    x.k = k;
-    x.out_vals = out_vals;
-    x.out_idx = out_idx;
-    x.out_ld = k;
-    for (int32_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
-        x.row0 = r0;
-        x.rows = std::min(kMaxGridRows, rows - r0);
-        if (topk::launch_radix_select(x, (hipStream_t)stream) != hipSuccess) return TOPK_ELAUNCH;
-    }
-    return TOPK_OK;
+    return run_radix(scores, lengths, rows, n, k, out_vals, out_idx, (hipStream_t)stream);
 }
 
 int topk_sparse_decode(const void *q, const void *kv, const int32_t *idx, int32_t rows,
@@ -510,7 +558,7 @@ int topk_pooled_select(const float *pool_scores, const int32_t *pool_idx,
                        void *stream) {
     if (rows < 0 || n < 1 || group < 1 || keep < 1 || keep > TOPK_MAX_POOL_SLOTS)
         return TOPK_EINVAL;
-    if (k < 1 || k > TOPK_MAX_K) return TOPK_EK_RANGE;
+    if (k < 1 || k > TOPK_MAX_K_POOLED) return TOPK_EK_RANGE;
     const int64_t total = (int64_t)keep * group;
     if (total > INT32_MAX) return TOPK_EINVAL;
     if (rows == 0) return TOPK_OK;

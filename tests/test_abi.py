@@ -39,7 +39,8 @@ def test_constants_match_header():
     text = open(HEADER).read()
     for cname in ("TOPK_OK", "TOPK_EINVAL", "TOPK_EK_RANGE", "TOPK_EWORKSPACE", "TOPK_ESPLIT",
                   "TOPK_ELAUNCH", "TOPK_EDEVICE", "TOPK_EALLOC", "TOPK_MAX_K", "TOPK_MAX_SPLIT",
-                  "TOPK_MAX_POOL_SLOTS", "TOPK_MAX_K_RADIX"):
+                  "TOPK_MAX_POOL_SLOTS", "TOPK_MAX_K_RADIX", "TOPK_MAX_K_STREAM",
+                  "TOPK_MAX_K_POOLED", "TOPK_PATH_STREAM", "TOPK_PATH_RADIX"):
         m = re.search(rf"#define {cname} \(?(-?\d+)\)?", text)
         assert m and int(m.group(1)) == getattr(_lib, cname), cname
 
@@ -56,7 +57,7 @@ FAKE = 0x10000  # a non-null, 256-aligned address that is never dereferenced
     ((FAKE, None, -1, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # rows < 0
     ((FAKE, None, 1, 0, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),        # n < 1
     ((FAKE, None, 1, 16, 0, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),     # k < 1
-    ((FAKE, None, 1, 16, 2049, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),  # k > max
+    ((FAKE, None, 1, 16, 4097, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),  # k > max
     ((None, None, 1, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),       # null scores
     ((FAKE, None, 1, 16, 4, None, FAKE, None), _lib.TOPK_EINVAL),       # null out_vals
     ((FAKE, None, 1, 16, 4, FAKE, None, None), _lib.TOPK_EINVAL),       # null out_idx
@@ -97,7 +98,7 @@ def test_split_and_ex_argument_errors(lib):
     ((FAKE, None, 1, 64, 8, 0, 0, FAKE, FAKE, None), _lib.TOPK_EINVAL),        # keep < 1
     ((FAKE, None, 1, 64, 8, 16, -1, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # pinned < 0
     ((FAKE, None, 1, 64, 8, 16, 17, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # pinned > keep
-    ((FAKE, None, 1, 64, 8, 2100, 51, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),  # keep - pinned > max
+    ((FAKE, None, 1, 64, 8, 4200, 51, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),  # keep - pinned > max
     ((None, None, 1, 64, 8, 16, 2, FAKE, FAKE, None), _lib.TOPK_EINVAL),       # null scores
     ((FAKE, None, 1, 64, 8, 16, 2, None, FAKE, None), _lib.TOPK_EINVAL),       # null out_vals
     ((FAKE, None, 1, 64, 8, 16, 2, FAKE, None, None), _lib.TOPK_EINVAL),       # null out_idx
@@ -117,7 +118,7 @@ def test_block_pool_argument_errors(lib, args, status):
     ((FAKE, FAKE, None, 1, 64, 8, 8193, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),    # keep > max
     ((FAKE, FAKE, None, 1, 64, 1 << 20, 4096, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),  # too long
     ((FAKE, FAKE, None, 1, 64, 8, 16, 0, FAKE, FAKE, None), _lib.TOPK_EK_RANGE),    # k < 1
-    ((FAKE, FAKE, None, 1, 64, 8, 16, 2049, FAKE, FAKE, None), _lib.TOPK_EK_RANGE), # k > max
+    ((FAKE, FAKE, None, 1, 64, 8, 16, 2049, FAKE, FAKE, None), _lib.TOPK_EK_RANGE), # k > pooled max
     ((None, FAKE, None, 1, 64, 8, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # null scores
     ((FAKE, None, None, 1, 64, 8, 16, 4, FAKE, FAKE, None), _lib.TOPK_EINVAL),      # null pool
     ((FAKE, FAKE, None, 1, 64, 8, 16, 4, None, FAKE, None), _lib.TOPK_EINVAL),      # null out
@@ -270,3 +271,52 @@ def test_visit_order_looks_shuffled():
     assert hist.min() > 20                  # about 50 per eighth if uniform
     # records of a uniform random order average H(1024) ~ 7.5
     assert 5.0 < np.mean(records) < 10.5
+
+
+def test_main_calls_take_k_up_to_4096(lib):
+    # The page's own kernel stops near k = 4,000 ("The Secret GPU Kernel
+    # Behind DeepSeek V4.1 Flash", transcript 5:45): the main calls accept
+    # 1 <= k <= 4096 and reject 4097 before any HIP call (rows = 0 launches
+    # nothing, after the k check).
+    assert _lib.TOPK_MAX_K == 4096
+    for k, want in [(4096, _lib.TOPK_OK), (2049, _lib.TOPK_OK), (4097, _lib.TOPK_EK_RANGE)]:
+        assert lib.topk_select(FAKE, None, 0, 1 << 20, k, FAKE, FAKE, None) == want
+        assert lib.topk_select_split(FAKE, None, 0, 1 << 20, k, FAKE, FAKE, 2, None, 0,
+                                     None) == want
+        o = _lib.TopkOptions()
+        assert lib.topk_select_ex(FAKE, None, 0, 1 << 20, k, FAKE, FAKE, ctypes.byref(o), None,
+                                  0, None) == want
+    # options are range-checked for every k
+    o = _lib.TopkOptions()
+    o.waves = 9
+    assert lib.topk_select_ex(FAKE, None, 0, 1 << 20, 3000, FAKE, FAKE, ctypes.byref(o), None, 0,
+                              None) == _lib.TOPK_EINVAL
+    o.waves, o.split = 0, 2000
+    assert lib.topk_select_ex(FAKE, None, 0, 1 << 20, 3000, FAKE, FAKE, ctypes.byref(o), None, 0,
+                              None) == _lib.TOPK_ESPLIT
+
+
+def _select_plan(lib, rows, n, k):
+    p = _lib.TopkPlan()
+    assert lib.topk_plan(rows, n, k, None, ctypes.byref(p)) == 0
+    return p
+
+
+def test_plan_paths(lib):
+    # lists wider than the streaming filter's run the radix selection, with
+    # options or without, and need no workspace
+    for k in (2049, 3000, 4096):
+        p = _plan(lib, 4, 1 << 20, k, split=4)
+        assert p.path == _lib.TOPK_PATH_RADIX and p.split == 1 and p.workspace_bytes == 0
+        assert p.list_words >= k and p.list_words & (p.list_words - 1) == 0
+        assert p.lds_bytes <= 160 * 1024
+        assert _select_plan(lib, 1, 1 << 20, k).path == _lib.TOPK_PATH_RADIX
+        assert lib.topk_split_workspace_bytes(4, 1 << 20, k, 4) == 0
+    assert _plan(lib, 4, 1 << 20, 2048).path == _lib.TOPK_PATH_STREAM
+    # topk_select's own routing (no options): wide lists over many short rows
+    # go to the radix selection, million-score rows at k <= 2048 stream
+    assert _select_plan(lib, 256, 262144, 2048).path == _lib.TOPK_PATH_RADIX
+    assert _select_plan(lib, 128, 1 << 20, 2048).path == _lib.TOPK_PATH_STREAM
+    assert _select_plan(lib, 128, 1 << 20, 512).path == _lib.TOPK_PATH_STREAM
+    # with options the streaming path is kept up to its widest list
+    assert _plan(lib, 256, 262144, 2048).path == _lib.TOPK_PATH_STREAM

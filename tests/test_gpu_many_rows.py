@@ -10,6 +10,7 @@ import torch
 
 import gpu_helpers as H
 import oracle
+from decode_tolerance import decode_error_bound, within
 from oracle.decode import sparse_decode
 from sparse_attention_indexer_row_amd import api, workloads
 
@@ -69,7 +70,6 @@ def test_decode_many_rows():
     got = out.cpu().numpy()
     for r in (0, 65_534, 65_535, 65_536, ROWS - 1):
         want = sparse_decode(q[r:r + 1], kv, idx[r:r + 1], 0.125, dv)[0]
-        sel = [int(j) for j in idx[r] if j >= 0]
-        vmax = float(np.abs(kv[sel, :dv]).max()) if sel else 0.0
-        err = float(np.abs(got[r] - want).max())
-        assert err <= 2.0 ** -7 * vmax + 1e-6, f"decode row {r}: error {err}"
+        bound = decode_error_bound(q[r:r + 1], kv, idx[r:r + 1], 0.125, dv)[0]
+        ok, worst = within(got[r], want, bound)
+        assert ok, f"decode row {r}: error / bound {worst:.3f}"

@@ -272,9 +272,11 @@ def test_large_offsets_beyond_2gib():
 
 # ---- instrumentation -------------------------------------------------------
 
-def test_entrant_counts_single_stream_bound():
-    # One streamer wave per row and no split: the visit is a single stream,
-    # the setting of the pages' bound 1.5 * buffer * H(number of blocks).
+def test_entrant_counts_with_estimate():
+    # The default schedule (sampled estimate on), one streamer wave per row
+    # and no split: the estimate keeps the count far below the pages' bound
+    # 1.5 * buffer * H(number of blocks).  The bound's own setting (threshold
+    # from minus infinity, no estimate) is tested in test_gpu_boundary.py.
     rows, n, k = 16, 1 << 20, 512
     x = workloads.normal_rows(rows, n, 41)
     s = H.to_dev(x)
