@@ -141,6 +141,30 @@ int topk_select_split(const float *scores, const int32_t *lengths, int32_t rows,
                       int32_t k, float *out_vals, int32_t *out_idx, int32_t split,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the device array behind topk_select_split_noalloc (per GPU). */
+#define TOPK_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * topk_select_split_noalloc -- topk_select_split without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The split-row workspace is a file-scope device array of
+ * TOPK_NOALLOC_SCRATCH_BYTES bytes; each GPU the library runs on holds its
+ * own copy until the process ends.  Its address is looked up, and the array
+ * zeroed with a fill kernel on `stream`, on the first call on each device;
+ * every call leaves it zero again.  Same arguments and result as
+ * topk_select_split (split 0 = automatic).  TOPK_EWORKSPACE when the plan
+ * needs more than TOPK_NOALLOC_SCRATCH_BYTES (topk_split_workspace_bytes
+ * gives the need; with split > 0 this is checked before any HIP call, with
+ * split 0 after querying the device's compute units); k above
+ * TOPK_MAX_K_STREAM needs no workspace.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams, or host
+ * threads) race and must be serialised by the caller.
+ */
+int topk_select_split_noalloc(const float *scores, const int32_t *lengths, int32_t rows,
+                              int32_t n, int32_t k, float *out_vals, int32_t *out_idx,
+                              int32_t split, void *stream);
+
 /* Flags for topk_options.flags. */
 /* Skip the sampled threshold estimate: filter with exact bounds only. */
 #define TOPK_FLAG_NO_ESTIMATE 1

@@ -31,6 +31,7 @@ TOPK_FLAG_FORCE_RERUN = 2
 TOPK_MAX_SPLIT = 1024
 TOPK_MAX_POOL_SLOTS = 8192
 TOPK_MAX_K_RADIX = 8192
+TOPK_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 # Every function the header declares, in header order.
 EXPORTS = (
@@ -38,6 +39,7 @@ EXPORTS = (
     "topk_split_workspace_bytes",
     "topk_workspace_init",
     "topk_select_split",
+    "topk_select_split_noalloc",
     "topk_select_ex",
     "topk_plan",
     "topk_block_pool",
@@ -84,6 +86,7 @@ SIGNATURES = {
     "topk_split_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "topk_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "topk_select_split": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "topk_select_split_noalloc": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
     "topk_select_ex": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp,
                                       ctypes.POINTER(TopkOptions), _vp, _sz, _vp]),
     "topk_plan": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(TopkOptions),

@@ -109,6 +109,21 @@ def topk_select_split(scores: torch.Tensor, k: int, split: int, workspace: torch
     return vals, idx
 
 
+def topk_select_split_noalloc(scores: torch.Tensor, k: int, split: int = 0,
+                              lengths: torch.Tensor | None = None, out=None, stream=None):
+    """topk_select_split whose workspace is the library's static device array
+    (no allocation in the library; calls on one GPU must not overlap)."""
+    _check_scores(scores)
+    lp = _check_lengths(lengths, scores)
+    vals, idx = _outputs(scores, k, out)
+    rows, n = scores.shape
+    st = _lib.load().topk_select_split_noalloc(
+        scores.data_ptr(), lp, rows, n, k, vals.data_ptr(), idx.data_ptr(), split,
+        _stream_handle(stream, scores.device))
+    _lib.check(st, "topk_select_split_noalloc")
+    return vals, idx
+
+
 def _options(seed=0, split=0, waves=0, watermark=0, stats=None, flags=0) -> TopkOptions:
     o = TopkOptions()
     o.seed = seed

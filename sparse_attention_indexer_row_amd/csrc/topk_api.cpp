@@ -302,6 +302,35 @@ topk_plan_t radix_plan(int32_t k, int cus) {
     return p;
 }
 
+// Device array behind topk_select_split_noalloc.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is ever passed to kernels or fills.
+static __device__ __align__(256) unsigned char scratch[TOPK_NOALLOC_SCRATCH_BYTES];
+
+struct NoAllocScratch {
+    std::mutex mutex;
+    void *ptr[kMaxDevices] = {nullptr};
+};
+NoAllocScratch g_noalloc;
+
+// The current device's copy of `scratch`, zeroed on `stream` on the
+// device's first use (a fill kernel, no allocation).
+int noalloc_scratch(hipStream_t stream, void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TOPK_EDEVICE;
+    std::lock_guard<std::mutex> g(g_noalloc.mutex);
+    if (!g_noalloc.ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TOPK_EDEVICE;
+        if (topk::launch_fill_zero(p, TOPK_NOALLOC_SCRATCH_BYTES, stream) != hipSuccess)
+            return TOPK_ELAUNCH;
+        g_noalloc.ptr[dev] = p;
+    }
+    *out = g_noalloc.ptr[dev];
+    return TOPK_OK;
+}
+
 // topk_select's visit-order seed: a per-device call counter run through
 // splitmix64, so consecutive calls read a row's blocks in unrelated orders.
 std::atomic<uint64_t> g_calls[kMaxDevices];
@@ -403,6 +432,42 @@ int topk_select_split(const float *scores, const int32_t *lengths, int32_t rows,
     o.split = split;
     return topk_select_ex(scores, lengths, rows, n, k, out_vals, out_idx, &o, workspace,
                           workspace_bytes, stream);
+}
+
+int topk_select_split_noalloc(const float *scores, const int32_t *lengths, int32_t rows,
+                              int32_t n, int32_t k, float *out_vals, int32_t *out_idx,
+                              int32_t split, void *stream) {
+    int st = check_args(scores, rows, n, k, out_vals, out_idx, lengths);
+    if (st != TOPK_OK) return st;
+    if (split < 0 || split > TOPK_MAX_SPLIT) return TOPK_ESPLIT;
+    if (k > TOPK_MAX_K_STREAM) {
+        if (rows == 0) return TOPK_OK;
+        return run_radix(scores, lengths, rows, n, k, out_vals, out_idx, (hipStream_t)stream);
+    }
+    topk_options o{};
+    o.split = split;
+    // An explicit split fixes the workspace size without the device.
+    if (split > 0) {
+        const Plan fixed = make_plan(rows, n, k, &o, kAssumedCUs);
+        st = check_plan(fixed);
+        if (st != TOPK_OK) return st;
+        if (fixed.ws_bytes > TOPK_NOALLOC_SCRATCH_BYTES) return TOPK_EWORKSPACE;
+    }
+    if (rows == 0) return TOPK_OK;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != TOPK_OK) return st;
+    const Plan pl = make_plan(rows, n, k, &o, cus);
+    st = check_plan(pl);
+    if (st != TOPK_OK) return st;
+    void *ws = nullptr;
+    if (pl.split > 1) {
+        if (pl.ws_bytes > TOPK_NOALLOC_SCRATCH_BYTES) return TOPK_EWORKSPACE;
+        st = noalloc_scratch((hipStream_t)stream, &ws);
+        if (st != TOPK_OK) return st;
+    }
+    return run(scores, lengths, rows, n, k, out_vals, out_idx, pl, ws, next_seed(), 0u, nullptr,
+               (hipStream_t)stream);
 }
 
 int topk_select(const float *scores, const int32_t *lengths, int32_t rows, int32_t n, int32_t k,

@@ -320,3 +320,19 @@ def test_plan_paths(lib):
     assert _select_plan(lib, 128, 1 << 20, 512).path == _lib.TOPK_PATH_STREAM
     # with options the streaming path is kept up to its widest list
     assert _plan(lib, 256, 262144, 2048).path == _lib.TOPK_PATH_STREAM
+
+
+def test_noalloc_entry_point_rejects_sizes_beyond_its_array(lib):
+    assert _lib.TOPK_NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert "#define TOPK_NOALLOC_SCRATCH_BYTES (8u << 20)" in open(HEADER).read()
+    # 2,000 rows x 8 segments x 2,048-word lists: 262 MB of lists, refused
+    # before any HIP call
+    need = lib.topk_split_workspace_bytes(2000, 1 << 20, 2048, 8)
+    assert need > _lib.TOPK_NOALLOC_SCRATCH_BYTES
+    assert lib.topk_select_split_noalloc(FAKE, None, 2000, 1 << 20, 2048, FAKE, FAKE, 8,
+                                         None) == _lib.TOPK_EWORKSPACE
+    assert lib.topk_select_split_noalloc(FAKE, None, 4, 1 << 20, 512, FAKE, FAKE, -1,
+                                         None) == _lib.TOPK_ESPLIT
+    assert lib.topk_select_split_noalloc(FAKE, None, 4, 1 << 20, 4097, FAKE, FAKE, 2,
+                                         None) == _lib.TOPK_EK_RANGE
+    assert lib.topk_select_split_noalloc(None, None, 0, 16, 8, None, None, 2, None) == _lib.TOPK_OK
