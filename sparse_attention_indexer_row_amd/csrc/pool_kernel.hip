@@ -29,6 +29,7 @@
 namespace topk {
 namespace {
 
+
 constexpr int kPoolThreads = 256;
 
 template <bool VEC>
@@ -307,50 +308,63 @@ __device__ __forceinline__ void for_each_word(const float *row, uint32_t m, cons
 __device__ __forceinline__ void wave_append(uint64_t *buf, uint32_t *counter, uint32_t cap,
                                             uint64_t w, bool take);
 
+// Float4s per thread in one group of the admission pass.
+constexpr uint32_t kAdmitU = 8;
+
+// Loads group `base` (thread index plus a multiple of kAdmitU * 1024) of a
+// row's aligned body.  Indices past the body read its last float4 again (no
+// per-lane branch around a load); the counting masks them.
+__device__ __forceinline__ void admit_load(float4 (&d)[kAdmitU], const RowParts &p, uint32_t base) {
+#pragma unroll
+    for (uint32_t u = 0; u < kAdmitU; ++u) {
+        const uint32_t q = base + u * kRadixThreads;
+        d[u] = load_stream4(reinterpret_cast<const float *>(p.body + (q < p.n4 ? q : p.n4 - 1u)));
+    }
+}
+
+// `first` holds the row's first group (admit_load at threadIdx.x), issued
+// early by the caller so that its memory latency overlaps other work.
 template <class W>
 __device__ __forceinline__ void append_at_least(const float *row, uint32_t m, const W &wm,
                                                 uint64_t lo, uint64_t *buf, uint32_t *counter,
-                                                uint32_t cap) {
-    constexpr uint32_t U = 8;
+                                                uint32_t cap, const float4 (&first)[kAdmitU]) {
+    constexpr uint32_t U = kAdmitU;
+    constexpr uint32_t STEP = U * kRadixThreads;
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const RowParts p = row_parts(row, m);
-    for (uint32_t base = threadIdx.x; base - lane < p.n4; base += U * kRadixThreads) {
-        float4 v[U];
-#pragma unroll
-        for (uint32_t u = 0; u < U; ++u) {
-            const uint32_t q = base + u * kRadixThreads;
-            v[u] = q < p.n4 ? p.body[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+    // Two register sets: the next group of loads is in flight while the
+    // current one is counted and written, so the pass is not one memory
+    // round trip per group.
+    float4 v[2][U];
+    auto load = [&](float4 (&d)[U], uint32_t base) __attribute__((always_inline)) {
+        admit_load(d, p, base);
+    };
+    auto consume = [&](const float4 (&d)[U], uint32_t base) __attribute__((always_inline)) {
         uint32_t mine = 0;
 #pragma unroll
         for (uint32_t u = 0; u < U; ++u) {
             const uint32_t q = base + u * kRadixThreads;
             const uint32_t i = p.head + 4u * q;
             if (q < p.n4) {
-                mine += wm(v[u].x, i) >= lo;
-                mine += wm(v[u].y, i + 1) >= lo;
-                mine += wm(v[u].z, i + 2) >= lo;
-                mine += wm(v[u].w, i + 3) >= lo;
+                mine += wm(d[u].x, i) >= lo;
+                mine += wm(d[u].y, i + 1) >= lo;
+                mine += wm(d[u].z, i + 2) >= lo;
+                mine += wm(d[u].w, i + 3) >= lo;
             }
         }
-        // exclusive prefix of `mine` over the wave, and the wave's total
-        uint32_t incl = mine;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t t = (uint32_t)__shfl_up((int)incl, off);
-            if ((int)lane >= off) incl += t;
-        }
-        const uint32_t total = (uint32_t)__shfl((int)incl, kWave - 1);
-        if (total == 0) continue;
+        // inclusive prefix of `mine` over the wave, and the wave's total
+        const uint32_t incl = wave_incl_scan(mine);
+        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+        if (total == 0) return;
         uint32_t at = 0;
         if (lane == kWave - 1) at = atomicAdd(counter, total);
-        at = (uint32_t)__shfl((int)at, kWave - 1) + incl - mine;
-        if (mine == 0) continue;
+        at = (uint32_t)__builtin_amdgcn_readlane((int)at, kWave - 1) + incl - mine;
+        if (mine == 0) return;
 #pragma unroll
         for (uint32_t u = 0; u < U; ++u) {
             const uint32_t q = base + u * kRadixThreads;
             const uint32_t i = p.head + 4u * q;
-            const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            const float e[4] = {d[u].x, d[u].y, d[u].z, d[u].w};
 #pragma unroll
             for (uint32_t c = 0; c < 4; ++c) {
                 const uint64_t w = wm(e[c], i + c);
@@ -360,6 +374,19 @@ __device__ __forceinline__ void append_at_least(const float *row, uint32_t m, co
                 }
             }
         }
+    };
+    uint32_t base = threadIdx.x;
+#pragma unroll
+    for (uint32_t u = 0; u < U; ++u) v[0][u] = first[u];
+    for (; base - lane < p.n4; base += 2u * STEP) {
+        const uint32_t b1 = base + STEP;
+        const bool more1 = b1 - lane < p.n4;
+        if (more1) load(v[1], b1);
+        consume(v[0], base);
+        if (!more1) break;
+        const uint32_t b2 = b1 + STEP;
+        if (b2 - lane < p.n4) load(v[0], b2);
+        consume(v[1], b1);
     }
     for_each_scalar(row, p, wm, [&](uint64_t w, bool valid) {
         wave_append(buf, counter, cap, w, valid && w >= lo);
@@ -378,7 +405,7 @@ __device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t bin, bool on) 
         const uint64_t act = __ballot(on);
         if (act == 0ull) return;
         const int leader = __ffsll((unsigned long long)act) - 1;
-        const uint32_t lb = (uint32_t)__shfl((int)bin, leader);
+        const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
         const uint64_t same = __ballot(on && bin == lb);
         if ((int)lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
         if (on && bin == lb) on = false;
@@ -397,7 +424,7 @@ __device__ __forceinline__ void wave_append(uint64_t *buf, uint32_t *counter, ui
     const int leader = __ffsll((unsigned long long)mask) - 1;
     uint32_t base = 0;
     if ((int)lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-    base = (uint32_t)__shfl((int)base, leader);
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
     if (take) {
         const uint32_t at = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
         if (at < cap) buf[at] = w;
@@ -484,12 +511,11 @@ __device__ __forceinline__ void radix_pick(const uint32_t *hist, uint32_t need, 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     const uint32_t h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
-    uint32_t suf = h0 + h1;  // becomes the sum of this lane's bins and every bin above
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t v = (uint32_t)__shfl_down((int)suf, off);
-        if (lane + off < kWave) suf += v;
-    }
+    // sum of this lane's bins and every bin above it in the wave: the wave's
+    // total less the inclusive prefix below this lane
+    const uint32_t own = h0 + h1;
+    const uint32_t incl = wave_incl_scan(own);
+    uint32_t suf = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1) - incl + own;
     if (lane == 0) sh.wave_sum[wv] = suf;
     __syncthreads();
     for (int u = wv + 1; u < kRadixThreads / kWave; ++u) suf += sh.wave_sum[u];
@@ -629,11 +655,16 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
                 const uint32_t i = (uint32_t)(((uint64_t)c * m) / kSampleChunks) + o;
                 samp[q] = wm(row[i], i);
             }
+            // The admission pass's first group is issued now, before the
+            // sample's selection.
+            const RowParts body = row_parts(row, m);
+            float4 first[kAdmitU];
+            if (threadIdx.x - (threadIdx.x & (kWave - 1)) < body.n4) admit_load(first, body, threadIdx.x);
             __syncthreads();
             const RadixCut ec = lds_radix(samp, kSampleWords, j, hist, sh);
             __syncthreads();  // the sample is read before the admission pass overwrites it
             const uint64_t est = ec.thr << ec.shift;   // words >= est: j in the sample
-            append_at_least(row, m, wm, est, cand, &sh.ncand, kRadixCand);
+            append_at_least(row, m, wm, est, cand, &sh.ncand, kRadixCand, first);
             __syncthreads();
             const uint32_t nc = sh.ncand;
             if (nc >= k && nc <= (uint32_t)kRadixCand) {

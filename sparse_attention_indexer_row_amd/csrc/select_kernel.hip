@@ -323,24 +323,6 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t v, uint32_t lane) {
     return uniform64(v);
 }
 
-template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
-__device__ __forceinline__ uint32_t dpp_add_src(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
-}
-
-// Inclusive prefix sum over the wave's lanes with DPP: shifts by 1, 2, 4, 8
-// inside each 16-lane row, then row_bcast:15 and row_bcast:31 carry the row
-// totals upward.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    v += dpp_add_src<0x111, 0xF, true>(v);
-    v += dpp_add_src<0x112, 0xF, true>(v);
-    v += dpp_add_src<0x114, 0xF, true>(v);
-    v += dpp_add_src<0x118, 0xF, true>(v);
-    v += dpp_add_src<0x142, 0xA, false>(v);
-    v += dpp_add_src<0x143, 0xC, false>(v);
-    return v;
-}
-
 // Tray words folded into the candidate pool per step, per lane.
 constexpr int kPiece = 16;
 // LDS passes read kBatch words per lane before using any of them, so a pass

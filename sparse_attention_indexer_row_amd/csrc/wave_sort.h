@@ -30,6 +30,24 @@ __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ uint32_t dpp_add_src(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+
+// Inclusive prefix sum over the wave's lanes with DPP: shifts by 1, 2, 4, 8
+// inside each 16-lane row, then row_bcast:15 and row_bcast:31 carry the row
+// totals upward.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += dpp_add_src<0x111, 0xF, true>(v);
+    v += dpp_add_src<0x112, 0xF, true>(v);
+    v += dpp_add_src<0x114, 0xF, true>(v);
+    v += dpp_add_src<0x118, 0xF, true>(v);
+    v += dpp_add_src<0x142, 0xA, false>(v);
+    v += dpp_add_src<0x143, 0xC, false>(v);
+    return v;
+}
+
 // Value of `v` in lane (lane ^ D), with VALU lane exchanges only:
 //   D = 1, 2     DPP quad_perm [1,0,3,2] / [2,3,0,1]
 //   D = 4        DPP row_half_mirror (l -> 7-l in 8) then quad_perm [3,2,1,0]
