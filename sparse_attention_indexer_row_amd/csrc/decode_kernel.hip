@@ -13,10 +13,12 @@
 // decode_partial_kernel: workgroup (split s, 16-head group, row r), four
 // waves.  Its share of the row's selected positions is walked in tiles of
 // 32: the tile's cache rows are gathered into LDS (16-byte loads), the
-// scores S = Q K^T (16 heads x 32 positions) come from bf16 MFMA 16x16x16
-// with the dqk dimension spread over the four waves and summed through LDS,
+// scores S = Q K^T (16 heads x 32 positions) come from gfx950's bf16 MFMA
+// 16x16x32 (16-byte operands, 32 of the dqk dimension per issue) with the
+// dqk dimension spread over the four waves and summed through LDS,
 // an online softmax updates each head's running maximum and sum, and
-// O += P V runs on MFMA with each wave owning a quarter of the dv columns
+// O += P V runs on the same MFMA, one issue per 16 value columns for the
+// tile's 32 positions, with each wave owning a quarter of the dv columns
 // (P rounded to bf16, and the running sum adds the rounded weights, so the
 // weights stay normalised).  The split writes (O, max, sum) per head.
 // decode_combine_kernel merges the splits by their log-sum-exp.
@@ -28,17 +30,36 @@
 namespace topk {
 namespace {
 
-typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 MFMA 16x16x32 (gfx950): lane l holds A[l % 16][8 (l / 16) + i] and
+// B[8 (l / 16) + i][l % 16] for i < 8, and D[4 (l / 16) + e][l % 16].
+__device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+// gfx950's transposing LDS read (ds_read_b64_tr_b16): inside each group of
+// 16 lanes, lane j receives element j % 4 of the 8-byte pieces read by lanes
+// j / 4 + 4 e, e = 0..3.  When lane L of a group reads the four columns
+// c + 4 (L % 4) .. c + 4 (L % 4) + 3 of row r0 + L / 4 of a row-major bf16
+// matrix, lane j receives rows r0 .. r0 + 3 of column c + j: a column slice,
+// which is how the MFMA's B operand wants the value rows.
+__device__ __forceinline__ bf16x4_t lds_read_tr16(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t *)(p));
+}
 
 constexpr int kDecThreads = 256;
 constexpr int kDecTile = 32;       // selected positions per tile
 constexpr int kDecHeads = 16;      // heads per workgroup (MFMA rows)
-// Register arrays are sized per instantiation: MS dqk steps and MV
+// Register arrays are sized per instantiation: MS 32-wide dqk steps and MV
 // 16-column value tiles per wave.  The compact one covers dqk <= 576 and
 // dv <= 512 (the MLA shape); the general one the limits.
-constexpr int kDecStepsSmall = 576 / 16 / 4, kDecVTilesSmall = 512 / 64;
-constexpr int kDecStepsMax = kMaxDecodeDqk / 16 / 4, kDecVTilesMax = kMaxDecodeDv / 64;
+constexpr int kDecStepsSmall = (576 / 32 + 3) / 4, kDecVTilesSmall = 512 / 64;
+constexpr int kDecStepsMax = kMaxDecodeDqk / 32 / 4, kDecVTilesMax = kMaxDecodeDv / 64;
 // 16-byte pieces per thread prefetched for the next tile (the rest load at
 // commit): all nine of a dqk = 576 tile in the compact instantiation.
 constexpr int kDecChunksSmall = kDecTile * 576 / 8 / kDecThreads, kDecChunksMax = 8;
@@ -73,18 +94,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs 
     const int t1 = min(a.k, t0 + a.per_split);
     // exact-shape instantiations know these at compile time, so the guards
     // in the unrolled loops fold away and operand loads can be issued early
-    const int nks = kExactDqk ? kExactDqk / 16 : a.dqk / 16;
+    // 32-wide dqk steps; when dqk is an odd multiple of 16 the last step's
+    // upper half (lanes with grp >= 2) is zero on both operands
+    const int dqk = kExactDqk ? kExactDqk : a.dqk;
+    const int nks = (dqk + 31) / 32;
     const int nvt = kExactDv ? kExactDv / 64 : a.dv / 64;
 
     // This wave's query operands: k-steps ks = wv, wv + 4, ... (A layout:
-    // lane holds row col16, k = 4 grp .. 4 grp + 3 of the step).
-    bf16x4_t qa[kDecMaxSteps];
+    // lane holds row col16, k = 8 grp .. 8 grp + 7 of the step).
+    bf16x8_t qa[kDecMaxSteps];
     const uint16_t *qrow = a.q + ((size_t)r * a.heads + h0 + col16) * a.dqk;
 #pragma unroll
     for (int i = 0; i < kDecMaxSteps; ++i) {
         const int ks = wv + 4 * i;
-        bf16x4_t v = {0, 0, 0, 0};
-        if (ks < nks) v = *reinterpret_cast<const bf16x4_t *>(qrow + ks * 16 + grp * 4);
+        bf16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (ks < nks && ks * 32 + grp * 8 < dqk)
+            v = *reinterpret_cast<const bf16x8_t *>(qrow + ks * 32 + grp * 8);
         qa[i] = v;
     }
     f32x4_t acc[kDecMaxVTiles];
@@ -155,17 +180,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs 
         const bool more = tb + kDecTile < t1;
         if (more) fetch(tb + kDecTile);   // loads in flight during this tile
         // partial scores over this wave's k-steps (B layout: lane holds
-        // column col16 of the n-tile, k = 4 grp .. 4 grp + 3)
+        // column col16 of the n-tile, k = 8 grp .. 8 grp + 7: one 16-byte
+        // LDS read)
         f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int i = 0; i < kDecMaxSteps; ++i) {
             const int ks = wv + 4 * i;
             if (ks < nks) {
+                const bool in = ks * 32 + grp * 8 < dqk;
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    const bf16x4_t b = *reinterpret_cast<const bf16x4_t *>(
-                        kt + (nt * 16 + col16) * ldk + ks * 16 + grp * 4);
-                    sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qa[i], b, sacc[nt], 0, 0, 0);
+                    bf16x8_t b = {0, 0, 0, 0, 0, 0, 0, 0};
+                    if (in) {
+                        b = *reinterpret_cast<const bf16x8_t *>(kt + (nt * 16 + col16) * ldk +
+                                                                ks * 32 + grp * 8);
+                    }
+                    sacc[nt] = mfma32(qa[i], b, sacc[nt]);
                 }
             }
         }
@@ -227,17 +257,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeArgs 
                 for (int e = 0; e < 4; ++e) acc[nt][e] *= al[e];
             }
         }
-#pragma unroll
-        for (int kk = 0; kk < kDecTile / 16; ++kk) {
-            const bf16x4_t pa = *reinterpret_cast<const bf16x4_t *>(pw + col16 * kDecTile + kk * 16 + grp * 4);
+        // the tile's 32 positions are one k-step: A = P (lane holds head
+        // col16, positions 8 grp .. 8 grp + 7), B = V (lane holds value
+        // column col16 of those positions, two transposing LDS reads)
+        {
+            const bf16x8_t pa = *reinterpret_cast<const bf16x8_t *>(pw + col16 * kDecTile + grp * 8);
+            const int dv4 = kExactDv ? kExactDv / 4 : a.dv / 4;
+            const uint16_t *vrow = kt + (grp * 8 + (col16 >> 2)) * ldk + 4 * (col16 & 3);
 #pragma unroll
             for (int nt = 0; nt < kDecMaxVTiles; ++nt) {
                 if (nt < nvt) {
-                    const int col = wv * (a.dv / 4) + nt * 16 + col16;
-                    const uint16_t *vp = kt + (kk * 16 + grp * 4) * ldk + col;
-                    const bf16x4_t b = {(short)vp[0], (short)vp[ldk], (short)vp[2 * ldk],
-                                        (short)vp[3 * ldk]};
-                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, b, acc[nt], 0, 0, 0);
+                    const int cb = wv * dv4 + nt * 16;
+                    const bf16x4_t lo = lds_read_tr16(vrow + cb);
+                    const bf16x4_t hi = lds_read_tr16(vrow + 4 * ldk + cb);
+                    const bf16x8_t b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    acc[nt] = mfma32(pa, b, acc[nt]);
                 }
             }
         }
