@@ -257,6 +257,126 @@ def host_cores() -> int:
 
 
 METRIC_SELECT = "effective HBM read GB/s (and rows/s) for top-512 of 1M fp32 scores/row"
+
+
+def median_us(torch, stream, call, n=30, warm=5):
+    """Median of n HIP-event-timed calls on `stream` (call(i) for i = 0, 1, ...)."""
+    import numpy as np
+    for i in range(warm):
+        call(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        call(warm + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
+
+def harmonic(n: int) -> float:
+    return sum(1.0 / i for i in range(1, n + 1))
+
+
+def headline_extras(dev, torch, api, workloads):
+    """Context measured beside the headline line: topk_select on R rows of 1M
+    N(0,1) scores for R = 64, 128, 256 (cold: two copies of each batch), and
+    the other spec configurations (4 x 16K, 64 x 128K with outliers,
+    1 x 1M, 256 ragged rows of <= 256K at k = 2,048) in microseconds per call,
+    with torch.topk on the same rows."""
+    import numpy as np
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev)
+    sweep = {}
+    for R in (64, 128, 256):
+        gen.manual_seed(1000 + R)
+        xs = [torch.randn((R, 1 << 20), generator=gen, device=dev) for _ in range(2)]
+        t = median_us(torch, stream, lambda i: api.topk_select(xs[i % 2], 512, stream=stream))
+        gbs = 4 * R * (1 << 20) / (t * 1e-6) / 1e9
+        sweep[str(R)] = {"us_per_call": round(t, 1), "GBps": round(gbs, 1),
+                         "frac_of_8TBps": round(gbs / HBM_PEAK_GBPS, 4),
+                         "plan": {k: v for k, v in api.topk_plan(R, 1 << 20, 512,
+                                                                 for_select=True).items()
+                                  if k in ("split", "waves", "path")}}
+        del xs
+    configs = {}
+    for label, name in (("C1", "small"), ("C2", "outlier"), ("C3", "one_row"), ("C5", "ragged")):
+        w = workloads.make(name)
+        base = torch.from_numpy(w.scores).to(dev)
+        ln = torch.from_numpy(w.lengths).to(dev) if w.lengths is not None else None
+        m = max(2, -(-(3 << 29) // (base.numel() * 4)))
+        xs = [base] + [base.clone() for _ in range(m - 1)]
+        t = median_us(torch, stream, lambda i: api.topk_select(xs[i % m], w.k, ln, stream=stream))
+        entry = {"workload": w.description, "us_per_call": round(t, 1),
+                 "GBps": round(4 * w.valid_elements() / (t * 1e-6) / 1e9, 1),
+                 "path": "radix" if routed_to_radix(w.rows, w.n, w.k, 256) else "streaming"}
+        if w.lengths is None:
+            tk = median_us(torch, stream, lambda i: torch.topk(xs[i % m], w.k, dim=1), n=10)
+            entry["torch_topk_us"] = round(tk, 1)
+        configs[label] = entry
+        del xs, base
+    return {"rows_sweep_1M_normal_k512": sweep, "other_configs": configs}
+
+
+def probe_sweep(torch, api, dev) -> dict:
+    """Read-probe sweep: whole-chip rate over read shapes (threads, loads in
+    flight per thread, plain or nontemporal loads, bytes per workgroup) and
+    the rate with 1..256 compute units active (one 4 MiB workgroup per unit,
+    kept alone on its unit by a 96 KiB LDS reservation).  Each rate is the
+    median of 7 event-timed reads rotating over three 1 GiB buffers."""
+    stream = torch.cuda.current_stream(dev)
+    gib = 1 << 30
+    bufs = [torch.ones(gib // 4, dtype=torch.float32, device=dev) for _ in range(3)]
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+
+    def rate(per, groups, threads, loads, nt, lds=0):
+        t = median_us(torch, stream, lambda i: api.topk_probe_read_cfg(
+            bufs[i % 3], per, groups, threads, loads, nt, lds, sink=sink, stream=stream),
+            n=7, warm=2)
+        return per * groups / (t * 1e-6) / 1e9, t
+
+    shapes = []
+    for per in (64 << 10, 4 << 20):
+        for threads in (256, 512, 1024):
+            for loads in (1, 2, 4, 8):
+                if per % (16 * threads * loads):
+                    continue
+                for nt in (False, True):
+                    gbs, t = rate(per, gib // per, threads, loads, nt)
+                    shapes.append({"bytes_per_group": per, "threads": threads, "loads": loads,
+                                   "nontemporal": nt, "GBps": round(gbs, 1)})
+    cus = []
+    for g in (1, 2, 4, 8, 16, 32, 64, 96, 128, 160, 192, 224, 256):
+        gbs, t = rate(4 << 20, g, 1024, 4, True, 96 << 10)
+        cus.append({"active_cus": g, "GBps": round(gbs, 1), "GBps_per_cu": round(gbs / g, 2)})
+    best = max(shapes, key=lambda x: x["GBps"])
+    return {"shapes": shapes, "active_cus": cus, "best": best,
+            "best_frac_of_8TBps": round(best["GBps"] / HBM_PEAK_GBPS, 4)}
+
+
+def write_probe_summary(res: dict) -> str:
+    path = os.path.join(TRAFFIC_DIR, "read_probe_sweep.md")
+    lines = ["# Streaming-read ceiling of MI355X: read-probe sweep", "",
+             "Command (from the repository root): `python bench.py --probe-sweep`", "",
+             "Whole chip, 1 GiB per read (median of 7, three rotating 1 GiB buffers):", "",
+             "| bytes per workgroup | threads | loads in flight | nontemporal | GB/s |",
+             "|---|---|---|---|---|"]
+    for x in res["shapes"]:
+        lines.append(f"| {x['bytes_per_group'] >> 10} KiB | {x['threads']} | {x['loads']} | "
+                     f"{'yes' if x['nontemporal'] else 'no'} | {x['GBps']:.0f} |")
+    b = res["best"]
+    lines += ["", f"Best: {b['GBps']:.0f} GB/s ({res['best_frac_of_8TBps']:.3f} of 8 TB/s) with "
+              f"{b['threads']} threads, {b['loads']} loads in flight, "
+              f"{'nontemporal' if b['nontemporal'] else 'plain'} loads, "
+              f"{b['bytes_per_group'] >> 10} KiB per workgroup.", "",
+              "Active compute units (one 4 MiB workgroup of 1,024 threads per unit, four "
+              "nontemporal loads in flight):", "",
+              "| active CUs | GB/s | GB/s per CU |", "|---|---|---|"]
+    for x in res["active_cus"]:
+        lines.append(f"| {x['active_cus']} | {x['GBps']:.0f} | {x['GBps_per_cu']:.1f} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
 POOL_GROUP, POOL_KEEP, POOL_PINNED = 8, 2000, 16
 
 
@@ -265,6 +385,7 @@ def make_case(name, dev, np, torch, api, workloads):
     The timed region rotates over enough input copies (>= 1.5 GiB) that
     every step reads cold HBM."""
     import oracle
+    from sparse_attention_indexer_row_amd import _lib
 
     stream = torch.cuda.current_stream(dev)
     c = {}
@@ -279,11 +400,18 @@ def make_case(name, dev, np, torch, api, workloads):
         rows, heads, dqk = w.q.shape
         q = torch.from_numpy(w.q).to(dev, dtype=torch.bfloat16)
         kv = torch.from_numpy(w.kv).to(dev, dtype=torch.bfloat16)
-        idx = torch.from_numpy(w.idx).to(dev)
+        # Each step gathers a different set of positions (the workload's and
+        # more draws of the same recipe), so the rows a step reads were not
+        # touched by the previous 23 steps (about 1.8 GB): cold HBM, not the
+        # 256 MB last-level cache.
+        sets = [w.idx] + [workloads.decode_positions(rows, w.kv.shape[0], w.idx.shape[1],
+                                                     seed=w.seed + 1 + c) for c in range(23)]
+        idx_sets = [torch.from_numpy(x).to(dev) for x in sets]
         out = torch.empty((rows, heads, w.dv), dtype=torch.float32, device=dev)
 
         def step(i):
-            api.topk_sparse_decode(q, kv, idx, w.dv, w.scale, out=out, stream=stream)
+            api.topk_sparse_decode(q, kv, idx_sets[i % len(idx_sets)], w.dv, w.scale, out=out,
+                                   stream=stream)
 
         sample = sorted({r for r in (0, 1, rows // 2, rows - 1) if r < rows})
 
@@ -302,7 +430,8 @@ def make_case(name, dev, np, torch, api, workloads):
             dt = time.perf_counter() - t0
             return dt, decode_read_bytes(w), f"all {rows} rows (float64 numpy)"
 
-        c.update(rows=rows, read_bytes=decode_read_bytes(w), copies=1, step=step, parity=parity,
+        c.update(rows=rows, read_bytes=decode_read_bytes(w), copies=len(idx_sets), step=step,
+                 parity=parity,
                  cpu=cpu, cpu_cores=lambda cores: 1,
                  kernel="decode_partial_kernel + decode_combine_kernel (whole call)",
                  parity_kind="within 2^-7 sum_j p_j |v_jc| + 1e-6 of the float64 oracle, "
@@ -452,10 +581,26 @@ def make_case(name, dev, np, torch, api, workloads):
             api.topk_select_ex(base, k, lengths, stats=st, workspace=ws, stream=stream)
             torch.cuda.synchronize()
             e = st.cpu().numpy().astype(np.float64)
+            st2 = torch.zeros((rows, 2), dtype=torch.int64, device=dev)
+            if ws is not None:
+                api.topk_workspace_init(ws)
+            api.topk_select_ex(base, k, lengths, stats=st2, workspace=ws, stream=stream,
+                               flags=_lib.TOPK_FLAG_NO_ESTIMATE)
+            torch.cuda.synchronize()
+            e2 = st2.cpu().numpy().astype(np.float64)
+            S = plan["split"]
+            nb = -(-n // 1024)
+            bound = S * 1.5 * plan["tray_words"] * harmonic(max(1, nb // S))
             out["entrants"] = {"mean": round(float(e[:, 0].mean()), 1), "max": int(e[:, 0].max()),
                                "sorts_mean": round(float(e[:, 1].mean()), 2),
                                "sorts_max": int(e[:, 1].max()),
-                               "per": "row (all segments of a split row)"}
+                               "no_estimate_mean": round(float(e2[:, 0].mean()), 1),
+                               "no_estimate_max": int(e2[:, 0].max()),
+                               "bound_1.5_B_H": round(bound, 1),
+                               "pages_bound": 29000,
+                               "per": "row (all segments of a split row); the bound sums "
+                                      "1.5 x tray capacity x H(blocks per segment) over the "
+                                      f"{S} segments"}
             if lengths is None:
                 tv, _ = torch.topk(base, k, dim=1)
                 torch.cuda.synchronize()
@@ -497,6 +642,10 @@ def main() -> int:
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the timed selection launches (for rocprofv3 counter runs)")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="sweep the streaming-read probe and write profiles/read_probe_sweep.md")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the headline's context lines (rows sweep, other configs)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from the rocprofv3 runs of PROFILE_COMMANDS")
     args = ap.parse_args()
@@ -519,6 +668,11 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.probe_sweep:
+        res = probe_sweep(torch, api, dev)
+        print(f"[bench] wrote {write_probe_summary(res)}", file=sys.stderr, flush=True)
+        print(json.dumps(res), flush=True)
+        return 0
 
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
@@ -586,7 +740,7 @@ def main() -> int:
 
     probe = None
     if not args.no_probe:
-        # plain streaming read of 2 GiB with the same per-wave access pattern
+        # the library's read probe (the sweep's best shape) over 2 GiB
         buf = torch.empty(1 << 29, dtype=torch.float32, device=dev)
         buf.fill_(1.0)
         sink = api.topk_probe_read(buf)
@@ -625,6 +779,9 @@ def main() -> int:
     extra = {}
     if "extras" in case and not args.profile_run:
         extra = case["extras"]()
+    context = None
+    if args.workload == "adverse" and not args.no_context:
+        context = headline_extras(dev, torch, api, workloads)
 
     traffic = load_traffic(args.workload)
     roofline = {
@@ -658,6 +815,7 @@ def main() -> int:
         "read_probe_GBps": round(probe, 1) if probe else None,
         "frac_of_read_probe": round(achieved / probe, 4) if probe else None,
         "entrants": extra.get("entrants"),
+        "context": context,
         "torch_topk": extra.get("torch_topk"),
         "host": host_cpu(),
         "cpu_single_thread": extra.get("cpu_single_thread"),

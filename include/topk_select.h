@@ -374,16 +374,28 @@ int topk_visit_order(uint64_t seed, int32_t row, int32_t nblocks, int32_t *out);
  * Streaming probes used to measure the machine, not part of the selection
  * (kernelbench.com "DeepSeek V4.1 Flash", split-KV decode paragraph: a
  * bandwidth roof taken from a weak measured read sits well short of what
- * the GPU delivers, so the roof here is measured with the selection's own
- * load pattern):
- * topk_probe_read reads `bytes` (multiple of 16) from `src` once with the
- * selection kernel's load pattern and writes one word per workgroup into
+ * the GPU delivers, so the roof here is measured, over a sweep of read
+ * shapes):
+ * topk_probe_read reads `src` once in whole 4 MiB workgroup shares (the
+ * floor(bytes / 4 MiB) of them; `bytes` a multiple of 16) with the best
+ * shape of the sweep on MI355X -- 1,024 threads, four nontemporal 16-byte
+ * loads in flight per thread -- and writes one word per workgroup into
  * `sink` (at least topk_probe_sink_words(bytes) uint32 words), so the read
- * cannot be elided.  topk_probe_copy copies `bytes` (multiple of 16) from src
- * to dst.  Both return TOPK_OK or an error status.
+ * cannot be elided.  topk_probe_read_cfg reads `groups` workgroup shares of
+ * `bytes_per_group` bytes (a multiple of 16 * threads * loads) with
+ * `threads` in {256, 512, 1024}, `loads` in {1, 2, 4, 8} loads in flight per
+ * thread, plain or nontemporal loads, and `lds_bytes` (<= 160 KiB) of LDS
+ * reserved per workgroup (a large reservation keeps one workgroup per
+ * compute unit, so `groups` sets the active compute units); sink: `groups`
+ * words.  topk_probe_copy copies `bytes` (multiple of 16) from src to dst.
+ * All return TOPK_OK or an error status (TOPK_EINVAL for shapes outside
+ * these sets, NULL or misaligned pointers).
  */
 size_t topk_probe_sink_words(size_t bytes);
 int topk_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+int topk_probe_read_cfg(const void *src, size_t bytes_per_group, size_t groups, int32_t threads,
+                        int32_t loads, int32_t nontemporal, size_t lds_bytes, uint32_t *sink,
+                        void *stream);
 int topk_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 #ifdef __cplusplus

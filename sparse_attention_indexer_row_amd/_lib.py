@@ -50,6 +50,7 @@ EXPORTS = (
     "topk_visit_order",
     "topk_probe_sink_words",
     "topk_probe_read",
+    "topk_probe_read_cfg",
     "topk_probe_copy",
 )
 
@@ -101,6 +102,7 @@ SIGNATURES = {
     "topk_visit_order": (ctypes.c_int, [_u64, _i32, _i32, _vp]),
     "topk_probe_sink_words": (_sz, [_sz]),
     "topk_probe_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
+    "topk_probe_read_cfg": (ctypes.c_int, [_vp, _sz, _sz, _i32, _i32, _i32, _sz, _vp, _vp]),
     "topk_probe_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
 }
 

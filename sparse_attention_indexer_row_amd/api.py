@@ -262,6 +262,22 @@ def topk_probe_read(src: torch.Tensor, sink: torch.Tensor | None = None, stream=
     return sink
 
 
+def topk_probe_read_cfg(src: torch.Tensor, bytes_per_group: int, groups: int, threads: int,
+                        loads: int, nontemporal: bool, lds_bytes: int = 0, sink=None,
+                        stream=None):
+    """One probe read of groups x bytes_per_group bytes of src (see the header)."""
+    if groups * bytes_per_group > src.numel() * src.element_size():
+        raise ValueError("the probe would read past src")
+    if sink is None:
+        sink = torch.empty(max(groups, 1), dtype=torch.int32, device=src.device)
+    _lib.check(_lib.load().topk_probe_read_cfg(src.data_ptr(), bytes_per_group, groups, threads,
+                                               loads, int(bool(nontemporal)), lds_bytes,
+                                               sink.data_ptr(),
+                                               _stream_handle(stream, src.device)),
+               "topk_probe_read_cfg")
+    return sink
+
+
 def topk_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < nbytes:

@@ -38,6 +38,9 @@ hipError_t launch_select(const SelectArgs &a, int E, int waves, size_t lds_bytes
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+hipError_t launch_probe_read_cfg(const void *src, size_t per_group, size_t groups, int threads,
+                                 int loads, bool nontemporal, size_t lds, uint32_t *sink,
+                                 hipStream_t stream);
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 size_t probe_read_groups(size_t bytes);
 

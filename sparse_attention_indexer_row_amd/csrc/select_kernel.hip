@@ -1616,32 +1616,43 @@ __global__ void fill_zero_kernel(uint4 *p, size_t n16) {
     }
 }
 
-// Streaming read with the selection kernel's access pattern (1 KiB per wave
-// per dwordx4 instruction, 4 KiB per wave per block), folded into one word
-// per workgroup so the loads cannot be removed.
-constexpr int kProbeThreads = 256;
-constexpr size_t kProbeBytesPerGroup = (size_t)64 << 10;
-
-__global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const float4 *src, size_t n16,
-                                                                   uint32_t *sink) {
-    const size_t per_group = kProbeBytesPerGroup / 16;
-    const size_t begin = (size_t)blockIdx.x * per_group;
-    size_t end = begin + per_group;
-    end = end < n16 ? end : n16;
+// Streaming read probes (measure the machine, not part of the selection).
+// Workgroup b reads bytes [b * per_group, (b + 1) * per_group) of src with
+// THREADS threads, LOADS 16-byte loads in flight per thread (consecutive
+// threads on consecutive 16 bytes), plain or nontemporal, and folds the data
+// into one word per workgroup so the loads cannot be removed.  per_group is
+// a multiple of 16 * THREADS * LOADS.
+template <int THREADS, int LOADS, bool NT>
+__global__ __launch_bounds__(THREADS) void probe_read_kernel(const float4 *src, size_t per16,
+                                                             uint32_t *sink) {
+    const float4 *p = src + (size_t)blockIdx.x * per16;
     uint32_t acc = 0;
-    for (size_t i = begin + threadIdx.x; i < end; i += kProbeThreads) {
-        const float4 v = src[i];
-        acc ^= __float_as_uint(v.x) ^ __float_as_uint(v.y) ^ __float_as_uint(v.z) ^
-               __float_as_uint(v.w);
+    for (size_t i = threadIdx.x; i < per16; i += (size_t)THREADS * LOADS) {
+        float4 v[LOADS];
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            const float4 *q = p + i + (size_t)u * THREADS;
+            if constexpr (NT) {
+                v[u] = load_stream4(reinterpret_cast<const float *>(q));
+            } else {
+                v[u] = *q;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            acc ^= __float_as_uint(v[u].x) ^ __float_as_uint(v[u].y) ^ __float_as_uint(v[u].z) ^
+                   __float_as_uint(v[u].w);
+        }
     }
-    __shared__ uint32_t red[kProbeThreads];
-    red[threadIdx.x] = acc;
+    __shared__ uint32_t red[THREADS / kWave];
+    for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = acc;
     __syncthreads();
-    for (int h = kProbeThreads / 2; h > 0; h >>= 1) {
-        if ((int)threadIdx.x < h) red[threadIdx.x] ^= red[threadIdx.x + h];
-        __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t x = 0;
+        for (int w = 0; w < THREADS / kWave; ++w) x ^= red[w];
+        sink[blockIdx.x] = x;
     }
-    if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
 }
 
 __global__ __launch_bounds__(256) void probe_copy_kernel(const float4 *src, float4 *dst, size_t n16) {
@@ -1709,16 +1720,63 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The default probe: the best full-chip read of the sweep on MI355X
+// (nontemporal loads, 1,024 threads, four loads in flight per thread, 4 MiB
+// per workgroup).
+constexpr int kProbeThreads = 1024, kProbeLoads = 4;
+constexpr size_t kProbeBytesPerGroup = (size_t)4 << 20;
+
 size_t probe_read_groups(size_t bytes) {
     return (bytes + kProbeBytesPerGroup - 1) / kProbeBytesPerGroup;
 }
 
-hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
-    const size_t groups = probe_read_groups(bytes);
-    if (groups == 0) return hipSuccess;
-    hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)groups), dim3(kProbeThreads), 0, stream,
-                       reinterpret_cast<const float4 *>(src), bytes / 16, sink);
+template <int T, int L, bool NT>
+hipError_t launch_probe_t(const void *src, size_t per_group, size_t groups, size_t lds,
+                          uint32_t *sink, hipStream_t stream) {
+    if (lds > 0) {
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&probe_read_kernel<T, L, NT>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((probe_read_kernel<T, L, NT>), dim3((unsigned)groups), dim3(T), lds, stream,
+                       reinterpret_cast<const float4 *>(src), per_group / 16, sink);
     return hipGetLastError();
+}
+
+template <int T, bool NT>
+hipError_t launch_probe_l(int loads, const void *src, size_t per_group, size_t groups, size_t lds,
+                          uint32_t *sink, hipStream_t stream) {
+    switch (loads) {
+        case 1: return launch_probe_t<T, 1, NT>(src, per_group, groups, lds, sink, stream);
+        case 2: return launch_probe_t<T, 2, NT>(src, per_group, groups, lds, sink, stream);
+        case 4: return launch_probe_t<T, 4, NT>(src, per_group, groups, lds, sink, stream);
+        case 8: return launch_probe_t<T, 8, NT>(src, per_group, groups, lds, sink, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_probe_read_cfg(const void *src, size_t per_group, size_t groups, int threads,
+                                 int loads, bool nontemporal, size_t lds, uint32_t *sink,
+                                 hipStream_t stream) {
+    if (groups == 0) return hipSuccess;
+    switch (threads * 2 + (nontemporal ? 1 : 0)) {
+        case 512: return launch_probe_l<256, false>(loads, src, per_group, groups, lds, sink, stream);
+        case 513: return launch_probe_l<256, true>(loads, src, per_group, groups, lds, sink, stream);
+        case 1024: return launch_probe_l<512, false>(loads, src, per_group, groups, lds, sink, stream);
+        case 1025: return launch_probe_l<512, true>(loads, src, per_group, groups, lds, sink, stream);
+        case 2048: return launch_probe_l<1024, false>(loads, src, per_group, groups, lds, sink, stream);
+        case 2049: return launch_probe_l<1024, true>(loads, src, per_group, groups, lds, sink, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
+    // whole 4 MiB groups; a shorter tail is not read (the caller's sizes are
+    // multiples of the group in practice, and the probe only measures)
+    const size_t groups = bytes / kProbeBytesPerGroup;
+    return launch_probe_read_cfg(src, kProbeBytesPerGroup, groups, kProbeThreads, kProbeLoads, true,
+                                 0, sink, stream);
 }
 
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t stream) {

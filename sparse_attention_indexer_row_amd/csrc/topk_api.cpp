@@ -685,6 +685,25 @@ int topk_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream)
                : TOPK_ELAUNCH;
 }
 
+int topk_probe_read_cfg(const void *src, size_t bytes_per_group, size_t groups, int32_t threads,
+                        int32_t loads, int32_t nontemporal, size_t lds_bytes, uint32_t *sink,
+                        void *stream) {
+    if (threads != 256 && threads != 512 && threads != 1024) return TOPK_EINVAL;
+    if (loads != 1 && loads != 2 && loads != 4 && loads != 8) return TOPK_EINVAL;
+    if (lds_bytes > kLdsPerWorkgroup - kStaticLdsBound || groups > (size_t)INT32_MAX)
+        return TOPK_EINVAL;
+    if (groups == 0) return TOPK_OK;
+    const size_t unit = (size_t)16 * (size_t)threads * (size_t)loads;
+    if (!src || !sink || bytes_per_group == 0 || bytes_per_group % unit != 0 ||
+        misaligned(src, 16))
+        return TOPK_EINVAL;
+    return topk::launch_probe_read_cfg(src, bytes_per_group, groups, threads, loads,
+                                       nontemporal != 0, lds_bytes, sink,
+                                       (hipStream_t)stream) == hipSuccess
+               ? TOPK_OK
+               : TOPK_ELAUNCH;
+}
+
 int topk_probe_copy(const void *src, void *dst, size_t bytes, void *stream) {
     if (bytes == 0) return TOPK_OK;
     if (!src || !dst || bytes % 16 != 0 || misaligned(src, 16) || misaligned(dst, 16))

@@ -222,6 +222,13 @@ def decode(seed: int = 108, rows: int = 128, heads: int = 16, n: int = 1 << 20, 
                           f"{n:,} entries (bf16), k={k} selected positions per row")
 
 
+def decode_positions(rows: int, n: int, k: int, seed: int) -> np.ndarray:
+    """Another draw of the decode workload's selections: k distinct
+    positions per row, uniform over [0, n), int32 [rows][k]."""
+    g = _rng(seed)
+    return np.stack([g.choice(n, size=k, replace=False) for _ in range(rows)]).astype(np.int32)
+
+
 WORKLOADS = {
     "vocab": vocab,
     "small": small,

@@ -177,6 +177,13 @@ def test_workspace_init_and_probe_argument_errors(lib):
     assert lib.topk_workspace_init(FAKE, 100, None) == _lib.TOPK_EWORKSPACE
     assert lib.topk_workspace_init(FAKE, 0, None) == _lib.TOPK_OK
     assert lib.topk_probe_read(FAKE, 100, FAKE, None) == _lib.TOPK_EINVAL
+    cfg = lib.topk_probe_read_cfg
+    assert cfg(FAKE, 1 << 20, 4, 128, 4, 1, 0, FAKE, None) == _lib.TOPK_EINVAL    # threads
+    assert cfg(FAKE, 1 << 20, 4, 256, 3, 1, 0, FAKE, None) == _lib.TOPK_EINVAL    # loads
+    assert cfg(FAKE, 1000, 4, 256, 4, 1, 0, FAKE, None) == _lib.TOPK_EINVAL       # share size
+    assert cfg(FAKE, 1 << 20, 4, 256, 4, 1, 200 << 10, FAKE, None) == _lib.TOPK_EINVAL  # LDS
+    assert cfg(FAKE + 8, 1 << 20, 4, 256, 4, 1, 0, FAKE, None) == _lib.TOPK_EINVAL  # alignment
+    assert cfg(FAKE, 1 << 20, 0, 256, 4, 1, 0, FAKE, None) == _lib.TOPK_OK        # nothing
     assert lib.topk_probe_copy(FAKE, None, 256, None) == _lib.TOPK_EINVAL
     assert lib.topk_probe_copy(FAKE, FAKE, 0, None) == _lib.TOPK_OK
 
