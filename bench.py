@@ -135,7 +135,8 @@ def load_traffic(workload: str):
 
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats -T -f csv -d {d} -o trace -- "
-             "python3 bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline --no-probe",
+             "python3 bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline --no-probe "
+             "--no-context",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -T -f csv -d {d} -o fetch -- "
              "python3 bench.py --workload {w} --profile-run --steps 5 --warmup 2",
     "write": "rocprofv3 --pmc WRITE_SIZE -T -f csv -d {d} -o write -- "
