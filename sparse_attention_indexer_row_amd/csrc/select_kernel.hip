@@ -757,55 +757,121 @@ __device__ __forceinline__ float4 load_block4(__amdgpu_buffer_rsrc_t rs, uint32_
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
-// Sampled threshold estimate ("The Secret GPU Kernel Behind DeepSeek V4.1
+// Sampled threshold estimates ("The Secret GPU Kernel Behind DeepSeek V4.1
 // Flash", transcript 10:57-11:09, on LightTopK: sample a small subset to
 // estimate a threshold, filter online, still return the exact answer; and
 // 11:47-12:10: the shipped kernel starts its scan already holding a working
-// threshold).  Lane j reads one aligned 128-byte line (32 consecutive
-// scores) at a seeded place inside stratum j of the row's 64 equal strata:
-// 2,048 scores for 64 line fetches.  Each line is cut into 4 groups of 8
-// scores, and the estimate is the j-th best of the 256 group maxima.  For a
-// row of independent scores, the sample holds about lam = 2048 k / L of the
-// row's best k, and j = ceil(lam + 6 sqrt(lam) + 6) lies far enough above
-// that for the estimate to fall below the k-th best in all but a vanishing
-// fraction of rows.  A group contributes one maximum however many of the
-// row's best scores it holds, so crowding the best scores together cannot
-// lift the estimate either.  It is not a bound: whether it was low enough is
-// checked at the end (at least k scores admitted), and the row is streamed
-// again without it otherwise.  Returns 0 (no estimate) for rows too short
-// for it to pay.
-constexpr uint32_t kSampleSpan = 32;                      // scores per lane, one 128-byte line
-constexpr uint32_t kSampleWords = kWave * kSampleSpan;    // 2,048
-constexpr int kSampleGroups = 4;                          // groups of 8 scores per lane
+// threshold).  The row's aligned 128-byte lines (32 consecutive scores) are
+// cut into 64 * n equal strata (n = 4 lines per lane on rows of at least 256
+// lines, else 1), and lane j reads one line at a seeded place inside each of
+// its strata n*j .. n*j + n-1.
+//
+//   * The first estimate uses each lane's first line only (2,048 scores
+//     spread over the whole row): each line is cut into 4 groups of 8
+//     scores, and the estimate is the j-th best of the 256 group maxima.
+//   * The second, on rows with 4 lines per lane, uses all 256 lines (8,192
+//     scores): the j-th best of the 256 line maxima.  The sorter publishes
+//     it after the first, while the streams already run, and they take it up
+//     a few blocks later.
+//
+// For a row of independent scores, a sample of m scores holds about
+// lam = m k / L of the row's best k, and j = ceil(lam + 6 sqrt(lam) + 6)
+// lies far enough above that for the estimate to fall below the k-th best in
+// all but a vanishing fraction of rows.  A group or a line contributes one
+// maximum however many of the row's best scores it holds, so crowding the
+// best scores together cannot lift an estimate either.  Neither is a bound:
+// the end of the pass checks that the k-th best admitted word is at least
+// the larger estimate (so every score an estimate turned away was below it),
+// and the row is streamed again without them otherwise.
+constexpr uint32_t kSampleSpan = 32;                      // scores per line
+constexpr int kSampleLines = 4;                           // lines per lane, long rows
+constexpr uint32_t kSampleWords = kWave * kSampleSpan;    // 2,048: the first sample
+constexpr int kSampleGroups = 4;                          // groups of 8 scores per line
 constexpr uint32_t kFlagNoEstimate = 1u;
 constexpr uint32_t kFlagForceRerun = 2u;
 
-__device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t seed, uint32_t r,
-                                                       uint32_t k, uint32_t flags, uint32_t *hist,
-                                                       uint64_t *gath, uint32_t lane) {
-    if ((flags & kFlagNoEstimate) || g.L == 0u) return 0ull;
-    const float lam = (float)k * (float)kSampleWords / (float)g.L;
-    const float jf = ceilf(lam + 6.0f * sqrtf(lam) + 6.0f);
-    if (!(jf <= (float)(kSampleGroups * kWave / 2))) return 0ull;
-    const uint32_t jn = (uint32_t)jf;
-    if (flags & kFlagForceRerun) return ~0ull;  // admits nothing: forces the rerun path
+// Where a lane's sample lines lie: n strata per lane over the row's whole
+// aligned lines; `lines` is 0 when the row is too short for a sample.
+struct SampleGeom {
+    uint32_t first;    // first whole line
+    uint32_t nlines;   // whole lines
+    uint32_t lines;    // lines per lane: 0, 1 or kSampleLines
+    uint32_t mis;      // the row start's misalignment inside a line, in floats
+    uint64_t key;
+};
+
+__device__ __forceinline__ SampleGeom sample_geometry(const RowGeom &g, uint64_t seed, uint32_t r) {
+    SampleGeom sg;
     // Line m starts at virtual position 32m - mis, 128-byte aligned in memory;
     // lines first .. last_end-1 lie wholly inside the valid positions.
-    const uint32_t mis = (uint32_t)(((uintptr_t)g.abase >> 2) & (kSampleSpan - 1u));
-    const uint32_t first = (g.off0 + mis + kSampleSpan - 1u) / kSampleSpan;
-    const uint32_t last_end = (g.vend + mis) / kSampleSpan;
-    if (last_end < first + (uint32_t)kWave) return 0ull;
-    const uint32_t nlines = last_end - first;
-    const uint32_t l0 = first + (uint32_t)((uint64_t)lane * nlines / kWave);
-    const uint32_t l1 = first + (uint32_t)((uint64_t)(lane + 1u) * nlines / kWave);
-    const uint64_t key = splitmix64(seed ^ 0x5851F42D4C957F2Dull ^ ((uint64_t)r << 20));
-    const uint32_t m = l0 + mix32((uint32_t)key ^ (lane * 0x9E3779B1u) ^ (uint32_t)(key >> 32)) %
-                                (l1 - l0);
-    const uint32_t gv = m * kSampleSpan - mis;
+    sg.mis = (uint32_t)(((uintptr_t)g.abase >> 2) & (kSampleSpan - 1u));
+    sg.first = (g.off0 + sg.mis + kSampleSpan - 1u) / kSampleSpan;
+    const uint32_t last_end = (g.vend + sg.mis) / kSampleSpan;
+    sg.nlines = last_end > sg.first ? last_end - sg.first : 0u;
+    sg.lines = g.L == 0u || sg.nlines < (uint32_t)kWave ? 0u
+               : sg.nlines >= (uint32_t)(kWave * kSampleLines) ? (uint32_t)kSampleLines : 1u;
+    sg.key = splitmix64(seed ^ 0x5851F42D4C957F2Dull ^ ((uint64_t)r << 20));
+    return sg;
+}
+
+// Loads this lane's i-th line (stratum lane*n + i) and returns the virtual
+// position of its first score.
+__device__ __forceinline__ uint32_t load_line(const RowGeom &g, const SampleGeom &sg, uint32_t i,
+                                              uint32_t lane, float4 (&x)[kSampleSpan / 4]) {
+    const uint32_t strata = (uint32_t)kWave * sg.lines;
+    const uint32_t j = lane * sg.lines + i;
+    const uint32_t l0 = sg.first + (uint32_t)((uint64_t)j * sg.nlines / strata);
+    const uint32_t l1 = sg.first + (uint32_t)((uint64_t)(j + 1u) * sg.nlines / strata);
+    const uint32_t m =
+        l0 + mix32((uint32_t)sg.key ^ (j * 0x9E3779B1u) ^ (uint32_t)(sg.key >> 32)) % (l1 - l0);
+    const uint32_t gv = m * kSampleSpan - sg.mis;
     const float4 *src = reinterpret_cast<const float4 *>(g.abase + gv);
-    float4 x[kSampleSpan / 4];
 #pragma unroll
     for (int u = 0; u < (int)(kSampleSpan / 4); ++u) x[u] = src[u];
+    return gv;
+}
+
+__device__ __forceinline__ uint32_t estimate_rank(uint32_t k, uint32_t words, uint32_t L,
+                                                  uint32_t limit) {
+    const float lam = (float)k * (float)words / (float)L;
+    const float jf = ceilf(lam + 6.0f * sqrtf(lam) + 6.0f);
+    return jf <= (float)limit ? (uint32_t)jf : 0u;
+}
+
+// The sample's lines in registers: lines 0 .. UP-1 are loaded before the
+// first estimate, the rest only for the second (so that, where registers are
+// scarce, they are not held together with the first line).
+template <int UP>
+struct SampleLines {
+    float4 x[kSampleLines][kSampleSpan / 4];
+    uint32_t gv[kSampleLines];   // virtual position of each line's first score
+};
+
+template <int UP>
+__device__ __forceinline__ void load_lines(const RowGeom &g, const SampleGeom &sg, int from,
+                                           int to, uint32_t lane, SampleLines<UP> &sl) {
+#pragma unroll
+    for (int i = 0; i < kSampleLines; ++i) {
+        if (i >= from && i < to && (uint32_t)i < sg.lines) {
+            sl.gv[i] = load_line(g, sg, (uint32_t)i, lane, sl.x[i]);
+        }
+    }
+}
+
+// The first estimate, from each lane's first line; 0 = none.  line0 receives
+// this lane's first line's best word.
+template <int UP>
+__device__ __forceinline__ uint64_t first_estimate(const RowGeom &g, const SampleGeom &sg,
+                                                   const SampleLines<UP> &sl, uint32_t k,
+                                                   uint32_t flags, uint32_t *hist, uint64_t *gath,
+                                                   uint64_t &line0, uint32_t lane) {
+    line0 = 0ull;
+    if ((flags & kFlagNoEstimate) || sg.lines == 0u) return 0ull;
+    const uint32_t jn = estimate_rank(k, kSampleWords, g.L, kSampleGroups * kWave / 2);
+    if (jn == 0u) return 0ull;
+    if (flags & kFlagForceRerun) return ~0ull;  // admits nothing: forces the rerun path
+    const float4 (&x)[kSampleSpan / 4] = sl.x[0];
+    const uint32_t gv = sl.gv[0];
     uint64_t gm[kSampleGroups];
 #pragma unroll
     for (int q = 0; q < kSampleGroups; ++q) {
@@ -831,6 +897,7 @@ __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t
         lmin = umin64(lmin, gm[q]);
         lmax = umax64(lmax, gm[q]);
     }
+    line0 = lmax;
     if (jn <= (uint32_t)kWave) {
         uint64_t v[1] = {lmax};
         wave_sort<1, false>(v, lane);
@@ -838,6 +905,55 @@ __device__ __forceinline__ uint64_t estimate_threshold(const RowGeom g, uint64_t
     }
     const uint64_t none[1] = {0ull};
     return select_rth(gm, none, jn, ~wave_max64(~lmin, lane), wave_max64(lmax, lane),
+                      position_bits(g.L), hist, gath, lane);
+}
+
+// The second estimate, from all of a lane's lines (rows with 4 per lane).
+// second_rank: its rank j among the 256 line words, 0 = none; none either
+// where the row's S segments, each reading the 8,192-score sample, would add
+// more than 1/32 of the row's own reads (S > L / 2^18).  line_words
+// loads the lines not yet loaded and gives each line one word: its largest
+// key with the line's last position, at most the line's best word, so it can
+// only lower the estimate (the first line's exact best word serves for it);
+// the words of different lines stay distinct.  second_pick selects the j-th
+// best of them.
+__device__ __forceinline__ uint32_t second_rank(const RowGeom &g, const SampleGeom &sg,
+                                                uint32_t k, uint32_t segments) {
+    if (sg.lines != (uint32_t)kSampleLines || (uint64_t)segments << 18 > g.L) return 0u;
+    constexpr uint32_t kLines = (uint32_t)(kWave * kSampleLines);
+    return estimate_rank(k, kLines * kSampleSpan, g.L, kLines / 2u);
+}
+
+template <int UP>
+__device__ __forceinline__ void line_words(const RowGeom &g, const SampleGeom &sg,
+                                           SampleLines<UP> &sl, uint64_t line0,
+                                           uint64_t (&lw)[kSampleLines], uint32_t lane) {
+    load_lines<UP>(g, sg, UP, kSampleLines, lane, sl);
+    lw[0] = line0;
+#pragma unroll
+    for (int i = 1; i < kSampleLines; ++i) {
+        uint32_t mk = 0u;
+#pragma unroll
+        for (int u = 0; u < (int)(kSampleSpan / 4); ++u) {
+            const float4 v = sl.x[i][u];
+            mk = max(mk, max(max(order_key(__float_as_uint(v.x)), order_key(__float_as_uint(v.y))),
+                             max(order_key(__float_as_uint(v.z)), order_key(__float_as_uint(v.w)))));
+        }
+        lw[i] = pack_word(mk, sl.gv[i] + kSampleSpan - 1u - g.off0);
+    }
+}
+
+__device__ __forceinline__ uint64_t second_pick(const RowGeom &g, uint32_t jn,
+                                                const uint64_t (&lw)[kSampleLines],
+                                                uint32_t *hist, uint64_t *gath, uint32_t lane) {
+    uint64_t lmin = lw[0], lmax = lw[0];
+#pragma unroll
+    for (int i = 1; i < kSampleLines; ++i) {
+        lmin = umin64(lmin, lw[i]);
+        lmax = umax64(lmax, lw[i]);
+    }
+    const uint64_t none[1] = {0ull};
+    return select_rth(lw, none, jn, ~wave_max64(~lmin, lane), wave_max64(lmax, lane),
                       position_bits(g.L), hist, gath, lane);
 }
 
@@ -865,7 +981,8 @@ __device__ __forceinline__ void raise_stream_bound(uint64_t &T, uint32_t kb, uin
 // the number of scores that entered a tray and raises *tray_kmax to the
 // largest key put in a tray; the last tray is marked final.  With tau_ready
 // set, the estimate is read from tau_src once the sorter flags it, after the
-// first loads are issued.
+// first loads are issued, and again every few blocks (the sorter raises it
+// once, to its second estimate).
 //
 // Per block the wave does little besides the loads: the visit order is
 // computed 64 blocks ahead by the vector unit (one permutation step per
@@ -940,6 +1057,10 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
     const bool lane_bounds = tau == 0ull;   // the estimate, when present, is far tighter
 
     for (uint32_t t0 = 0; t0 < mine; t0 += D) {
+        // A later, tighter estimate: read now, folded in after this round.
+        const uint64_t tau_next =
+            tau_ready ? __hip_atomic_load(tau_src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                      : 0ull;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const uint32_t t = t0 + (uint32_t)d;
@@ -1003,6 +1124,7 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                 wait_tray_free(&fill[w][cur]);
             }
         }
+        tau = umax64(tau, uniform64(tau_next));
     }
     if (cnt > 0) publish_tray(&fill[w][cur], cnt | kTrayFinal, lane);
     kmx = wave_max32(kmx, lane);
@@ -1014,13 +1136,15 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
 
 // Sorter side of one pass: folds published trays into the pool until every
 // streamer is done.  Trays still published then stay where they are: the
-// end-of-pass selection takes them with the pool.
-template <int E, bool SPLIT>
+// end-of-pass selection takes them with the pool.  When a scan finds no tray
+// published, idle() runs (deferred work; it returns whether it did any)
+// before the sorter sleeps.
+template <int E, bool SPLIT, typename Idle>
 __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_t *trays,
                                         uint32_t CW, uint32_t NS, uint32_t (*fill)[2],
                                         uint32_t *done_ctr, uint64_t *sT, uint64_t *gT,
                                         uint32_t k, uint32_t *hist, uint64_t *gath,
-                                        uint32_t lane) {
+                                        Idle &&idle, uint32_t lane) {
     for (;;) {
         uint32_t done = lds_load_u32(done_ctr);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -1045,7 +1169,7 @@ __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_
         if (done == NS) break;
         if (!worked) {
             if constexpr (SPLIT) fold_row_word(ss, sT, gT, lane);
-            __builtin_amdgcn_s_sleep(2);
+            if (!idle()) __builtin_amdgcn_s_sleep(2);
         }
     }
 }
@@ -1470,11 +1594,47 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     }
 
     // ---- sorter (wave NS) ----
-    const uint64_t tau = estimate_threshold(g, p.seed, r, k, p.flags, hist, gath, lane);
+    // Lists of at least 512 words keep over 128 registers anyway: there the
+    // sample's four lines are all loaded at once, and their words are formed
+    // right after the first estimate.  Narrower lists keep fewer registers
+    // (two workgroups can share a compute unit): they load the later lines
+    // after the first estimate.
+    constexpr int kUp = E >= 8 ? kSampleLines : 1;
+    const SampleGeom sg = sample_geometry(g, p.seed, r);
+    const uint32_t jn2_row = second_rank(g, sg, k, S);   // 0: no second estimate for this row
+    SampleLines<kUp> sl;
+    if (!(p.flags & kFlagNoEstimate)) load_lines<kUp>(g, sg, 0, jn2_row != 0u ? kUp : 1, lane, sl);
+    uint64_t line0 = 0ull;
+    uint64_t tau = first_estimate<kUp>(g, sg, sl, k, p.flags, hist, gath, line0, lane);
     if (lane == 0) {
         s_tau = tau;
         __hip_atomic_store(&s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    // With the wide lists, the second estimate waits for the sorter's first
+    // idle moment (rows of rising scores send trays from the start, and those
+    // come first); the streams take it up when it is published.  Its radix selection uses the
+    // second of the three histograms, which nothing else uses during
+    // collection.  It depends on the row and the seed only, so every segment
+    // of a split row that makes it gets the same word; each makes it by the
+    // end of its pass at the latest, so the leader's check below covers
+    // whatever estimate any segment's streams used.
+    const uint32_t jn2 = tau != 0ull && tau != ~0ull ? jn2_row : 0u;
+    uint64_t lw[kSampleLines];
+    if (jn2 != 0u) line_words<kUp>(g, sg, sl, line0, lw, lane);
+    bool second_pending = jn2 != 0u;
+    auto second_estimate = [&]() __attribute__((always_inline)) {
+        if (!second_pending) return false;
+        second_pending = false;
+        const uint64_t tau2 = second_pick(g, jn2, lw, hist + 256, gath, lane);
+        if (tau2 > tau) {
+            tau = tau2;
+            if (lane == 0) {
+                __hip_atomic_store(&s_tau, tau2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+        return true;
+    };
+    if constexpr (kUp != kSampleLines) second_estimate();
     SorterState ss;
     ss.T = 0ull;
     ss.sorts = 0u;
@@ -1488,6 +1648,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     // Starts the rerun: empty pool (every score is streamed again), the
     // threshold stays (it is a valid bound of the row's k-th best).
     auto start_rerun = [&]() __attribute__((always_inline)) {
+        second_pending = false;
         reset_sorter(ss, hist, lane);
         if (lane == 0) {
             __hip_atomic_store(&s_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1499,7 +1660,9 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     uint64_t kept_sorted[E];
     bool rerun = false;
     for (int pass = 0; pass < 2; ++pass) {
-        collect<E, SPLIT>(ss, pool, trays, CW, NS, s_fill, &s_done, &s_T, gT, k, hist, gath, lane);
+        collect<E, SPLIT>(ss, pool, trays, CW, NS, s_fill, &s_done, &s_T, gT, k, hist, gath,
+                          second_estimate, lane);
+        if constexpr (SPLIT) second_estimate();
         if constexpr (SPLIT) ss.T = umax64(ss.T, uniform64(ss.gnext));
         // Every candidate's key is at most the larger of the pool's and the
         // streamers' largest keys.
@@ -1519,9 +1682,10 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
             ++ss.sorts;
         }
         if (!SPLIT || rerun) {
-            // With an estimate in use, fewer than k admitted scores means
-            // some of the row's best k may lie below it: stream again.
-            if (!rerun && tau != 0ull && n < k) {
+            // With an estimate in use, fewer than k admitted scores at or
+            // above it means some of the row's best k may lie below it:
+            // stream again.
+            if (!rerun && tau != 0ull && (n < k || list_word_at<E>(kept_sorted, k - 1) < tau)) {
                 rerun = true;
                 start_rerun();
                 continue;
@@ -1585,7 +1749,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
             return;
         }
         const uint64_t kth = list_word_at<E>(kept_sorted, k - 1);
-        if (tau != 0ull && kth == 0ull) {
+        if (tau != 0ull && kth < tau) {
             rerun = true;
             start_rerun();
             continue;
