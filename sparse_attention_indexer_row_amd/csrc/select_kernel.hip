@@ -847,14 +847,27 @@ struct SampleLines {
     uint32_t gv[kSampleLines];   // virtual position of each line's first score
 };
 
+// Loads lines 0 .. UP-1 with no branch between them, the first line first (so
+// the first estimate waits for its own loads only); lines from `count` on
+// repeat the first line's addresses, which costs no further memory traffic.
+// The row must have a sample (sg.lines != 0).
 template <int UP>
-__device__ __forceinline__ void load_lines(const RowGeom &g, const SampleGeom &sg, int from,
-                                           int to, uint32_t lane, SampleLines<UP> &sl) {
+__device__ __forceinline__ void load_first_lines(const RowGeom &g, const SampleGeom &sg,
+                                                 uint32_t count, uint32_t lane,
+                                                 SampleLines<UP> &sl) {
 #pragma unroll
-    for (int i = 0; i < kSampleLines; ++i) {
-        if (i >= from && i < to && (uint32_t)i < sg.lines) {
-            sl.gv[i] = load_line(g, sg, (uint32_t)i, lane, sl.x[i]);
-        }
+    for (int i = 0; i < UP; ++i) {
+        sl.gv[i] = load_line(g, sg, (uint32_t)i < count ? (uint32_t)i : 0u, lane, sl.x[i]);
+    }
+}
+
+// Loads the lines not loaded up front (rows with 4 lines per lane).
+template <int UP>
+__device__ __forceinline__ void load_later_lines(const RowGeom &g, const SampleGeom &sg,
+                                                 uint32_t lane, SampleLines<UP> &sl) {
+#pragma unroll
+    for (int i = UP; i < kSampleLines; ++i) {
+        sl.gv[i] = load_line(g, sg, (uint32_t)i, lane, sl.x[i]);
     }
 }
 
@@ -928,7 +941,7 @@ template <int UP>
 __device__ __forceinline__ void line_words(const RowGeom &g, const SampleGeom &sg,
                                            SampleLines<UP> &sl, uint64_t line0,
                                            uint64_t (&lw)[kSampleLines], uint32_t lane) {
-    load_lines<UP>(g, sg, UP, kSampleLines, lane, sl);
+    load_later_lines<UP>(g, sg, lane, sl);
     lw[0] = line0;
 #pragma unroll
     for (int i = 1; i < kSampleLines; ++i) {
@@ -1505,6 +1518,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     __shared__ EndShared s_end;                   // counters of the end-of-pass selection
     __shared__ uint32_t s_kmax;                   // largest key the streamers put in a tray
     __shared__ uint64_t s_hi;                     // bound of the end-of-pass candidates
+    __shared__ uint64_t s_lo;                     // lower bound of the words selected from
 
     const uint32_t lane = lane_id();
     const uint32_t w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
@@ -1546,7 +1560,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         __syncthreads();   // pool, its count, the trays and the bounds are final
         const Candidates c = make_candidates(pool, lds_load_u32(&s_pc), trays, CW, 2u * NS,
                                              &s_fill[0][0], lane);
-        const uint64_t lo = lds_load_word(&s_T);
+        const uint64_t lo = lds_load_word(&s_lo);
         const uint64_t hi = lds_load_word(&s_hi);
         const uint32_t n = end_select(c, lo, hi, position_bits(g.L), k, &s_end, hist, gath, fin, w,
                                       NW, w == NS, lane);
@@ -1603,7 +1617,9 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     const SampleGeom sg = sample_geometry(g, p.seed, r);
     const uint32_t jn2_row = second_rank(g, sg, k, S);   // 0: no second estimate for this row
     SampleLines<kUp> sl;
-    if (!(p.flags & kFlagNoEstimate)) load_lines<kUp>(g, sg, 0, jn2_row != 0u ? kUp : 1, lane, sl);
+    if (!(p.flags & kFlagNoEstimate) && sg.lines != 0u) {
+        load_first_lines<kUp>(g, sg, jn2_row != 0u ? (uint32_t)kUp : 1u, lane, sl);
+    }
     uint64_t line0 = 0ull;
     uint64_t tau = first_estimate<kUp>(g, sg, sl, k, p.flags, hist, gath, line0, lane);
     if (lane == 0) {
@@ -1667,8 +1683,17 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         // Every candidate's key is at most the larger of the pool's and the
         // streamers' largest keys.
         const uint32_t kx = max(ss.kmax, lds_load_u32(&s_kmax));
+        // The selection starts from the threshold, and in the first pass
+        // from the estimate too: every word admitted then was above the
+        // first estimate, and if fewer than k lie at or above the final one
+        // the row is streamed again anyway.  (The threshold word itself stays
+        // a valid bound, as a rerun keeps it.)  Rows whose trays mostly come
+        // as the streams' last ones leave the threshold low, and a selection
+        // from there would spend its first digits on the exponent.
+        const uint64_t t_end = umax64(ss.T, lds_load_word(&s_T));
         if (lane == 0) {
             __hip_atomic_fetch_max(&s_T, ss.T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            s_lo = rerun ? t_end : umax64(t_end, tau);
             s_pc = ss.pc;
             s_end.gcnt = 0u;
             s_end.out = 0u;
