@@ -1187,6 +1187,15 @@ __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_
     }
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads a wave has in
+// flight stay in flight across it (a full __syncthreads() waits for them).
+// The end of a pass exchanges data through LDS only.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------
 // End of a pass, run by every wave of the workgroup: the candidates are the
 // sorter's pool and every tray buffer still holding words; the best
@@ -1301,7 +1310,7 @@ __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo,
                     atomicAdd(&h[(uint32_t)(x >> low) & dmask], 1u);
                 }
             });
-            __syncthreads();
+            lds_barrier();
             uint32_t hb[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) hb[j] = h[lane * 4 + j];
@@ -1344,20 +1353,20 @@ __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo,
                 append_shared(fin, &sh->out, x, in && xm > prefix, lane);
                 append_shared(gath, &sh->gcnt, x, in && xm == prefix, lane);
             });
-            __syncthreads();
+            lds_barrier();
             if (zeroer) {
                 uint64_t v[1] = {lane < bin_cnt ? gath[lane] : 0ull};
                 wave_sort<1, false>(v, lane);
                 if (lane < r) fin[k - r + lane] = v[0];
             }
-            __syncthreads();
+            lds_barrier();
             return n;
         }
     }
     for_my_rows(c, w, NW, lane, [&](uint64_t x) __attribute__((always_inline)) {
         append_shared(fin, &sh->out, x, x >= lo && x != 0ull, lane);
     });
-    __syncthreads();
+    lds_barrier();
     return n;
 }
 
@@ -1400,7 +1409,7 @@ __device__ __forceinline__ void wg_sort_impl(uint64_t *x, const uint64_t *pool, 
 #pragma unroll
                 for (int e = 0; e < EP; ++e) x[base + (uint32_t)e * kWave + lane] = a[e];
             }
-            __syncthreads();
+            lds_barrier();
             if (active) {
                 const bool keep_max = ((base & J) == 0u) == ((base & S) == 0u);
 #pragma unroll
@@ -1409,7 +1418,7 @@ __device__ __forceinline__ void wg_sort_impl(uint64_t *x, const uint64_t *pool, 
                     a[e] = keep_max ? umax64(a[e], y) : umin64(a[e], y);
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
         if (active) {
             if ((base & S) == 0u) {
@@ -1423,7 +1432,7 @@ __device__ __forceinline__ void wg_sort_impl(uint64_t *x, const uint64_t *pool, 
 #pragma unroll
         for (int e = 0; e < EP; ++e) x[base + (uint32_t)e * kWave + lane] = a[e];
     }
-    __syncthreads();
+    lds_barrier();
     if (sorter) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -1557,7 +1566,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     // wave: the best min(k, n) of the pool and the trays, sorted into the
     // sorter's `kept` (the trays hold the sort's exchange buffer).  Returns n.
     auto end_of_pass = [&](uint64_t (&kept)[E]) __attribute__((always_inline)) {
-        __syncthreads();   // pool, its count, the trays and the bounds are final
+        lds_barrier();   // pool, its count, the trays and the bounds are final
         const Candidates c = make_candidates(pool, lds_load_u32(&s_pc), trays, CW, 2u * NS,
                                              &s_fill[0][0], lane);
         const uint64_t lo = lds_load_word(&s_lo);
@@ -1673,6 +1682,14 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         set_verdict(kVerdictRerun);
     };
 
+    // Split rows: segments publish their lists in groups of kMergeGroup.
+    uint64_t *lists = SPLIT ? p.ws_lists + (size_t)r * S * KP : nullptr;
+    const uint32_t G = (uint32_t)kMergeGroup;
+    const uint32_t ng = (S + G - 1u) / G;
+    const uint32_t grp = s / G, g0 = grp * G;
+    const uint32_t gsz = S - g0 < G ? S - g0 : G;
+    uint32_t *gticket = SPLIT ? p.ws_groups + (size_t)r * ng + grp : nullptr;
+
     uint64_t kept_sorted[E];
     bool rerun = false;
     for (int pass = 0; pass < 2; ++pass) {
@@ -1724,12 +1741,6 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         // slot and takes the row ticket; the last group to arrive merges the
         // groups' lists.  One release fence orders each publication before
         // its ticket; only the leaders need the matching acquire.
-        uint64_t *lists = p.ws_lists + (size_t)r * S * KP;
-        const uint32_t G = (uint32_t)kMergeGroup;
-        const uint32_t ng = (S + G - 1u) / G;
-        const uint32_t grp = s / G, g0 = grp * G;
-        const uint32_t gsz = S - g0 < G ? S - g0 : G;
-        uint32_t *gticket = p.ws_groups + (size_t)r * ng + grp;
         store_list<E>(lists, s, kept_sorted, lane);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         uint32_t old = 0;
