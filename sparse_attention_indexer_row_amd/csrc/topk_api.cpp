@@ -250,18 +250,26 @@ constexpr int64_t kPoolRowAlign = 64;
 constexpr int32_t kMaxGridRows = 65535;
 
 // Where topk_select takes the per-row radix selection instead of the
-// streaming filter: every k above the filter's widest list, and rows no
-// longer than 262,144 scores with lists of 1,024
-// words (k > 512) and at least half as many rows as compute units, or
-// lists of 2,048 words (k > 1,024) and at least a quarter as many.  There
-// the streaming path's wide lists spend their time sorting, while one
-// workgroup per row keeps the GPU busy (measured 1.2-2.6x faster on such
-// shapes; slower on million-score rows, at k <= 512, or with fewer rows).
+// streaming filter: every k above the filter's widest list, and, on rows no
+// longer than 262,144 scores,
+//   k > 512         always (the streaming lists of 1,024 words and more
+//                   spend their time sorting; radix 0.18-0.87x the time),
+//   256 < k <= 512  rows up to 131,072 scores, or any such row once there
+//                   are at least half as many rows as compute units,
+//   128 < k <= 256  rows up to 65,536 scores, or up to 131,072 with at
+//                   least half as many rows as compute units.
+// Those are the shapes where one workgroup per row, the whole row read once
+// into the candidate pass, beats the streaming path's fixed chain of
+// estimate, trays and end-of-pass selection (measured on MI355X over 1 to
+// 256 rows of N(0,1) scores of 16K to 256K: radix 0.71-0.98x the time
+// there; 1.0-1.7x elsewhere, and always slower on million-score rows).
 bool prefer_radix(int32_t rows, int32_t n, int32_t k, int cus) {
     if (k > TOPK_MAX_K_STREAM) return true;   // wider than the streaming filter's lists
     if (n > 262144) return false;
-    if (k > 1024) return (int64_t)rows * 4 >= cus;
-    if (k > 512) return (int64_t)rows * 2 >= cus;
+    const bool many = (int64_t)rows * 2 >= cus;
+    if (k > 512) return true;
+    if (k > 256) return n <= 131072 || many;
+    if (k > 128) return n <= 65536 || (n <= 131072 && many);
     return false;
 }
 
