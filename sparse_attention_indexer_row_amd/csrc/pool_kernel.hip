@@ -84,11 +84,12 @@ __global__ __launch_bounds__(kPoolThreads) void block_max_kernel(PoolArgs a) {
 }
 
 // Blocks of 8 on 16-byte aligned rows (n % 4 == 0): every lane reads one
-// float4, so a wave's load instruction covers 1 KiB of the row, with four
-// loads in flight per thread; the two lanes holding a block's halves
-// combine their maxima with one shuffle, and the even lane writes.  Work
-// item f is the row's f-th float4; block b = f / 2.
-constexpr int kPool8Unroll = 4;
+// float4, so a wave's load instruction covers 1 KiB of the row, with eight
+// nontemporal loads in flight per thread (the scores are read once; 4 and
+// 16 loads, or 512 threads, measured slower); the two lanes holding a
+// block's halves combine their maxima with one shuffle, and the even lane
+// writes.  Work item f is the row's f-th float4; block b = f / 2.
+constexpr int kPool8Unroll = 8;
 
 __global__ __launch_bounds__(kPoolThreads) void block_max8_kernel(PoolArgs a) {
     const int64_t r = (int64_t)a.row0 + blockIdx.y;
@@ -108,7 +109,8 @@ __global__ __launch_bounds__(kPoolThreads) void block_max8_kernel(PoolArgs a) {
 #pragma unroll
     for (int u = 0; u < kPool8Unroll; ++u) {
         const int64_t f = base + (int64_t)u * kPoolThreads;
-        v[u] = 4 * f < L ? row4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[u] = 4 * f < L ? load_stream4(reinterpret_cast<const float *>(row4 + f))
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < kPool8Unroll; ++u) {
