@@ -42,6 +42,14 @@ TOPK_HD uint32_t word_pos(uint64_t w) { return 0xFFFFFFFFu - (uint32_t)w; }
 // builtins).
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// Workgroup barrier that orders LDS accesses only: global loads a wave has in
+// flight stay in flight across it (a full __syncthreads() waits for them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // One 16-byte load of scores that are read once, with the nontemporal hint
 // (on gfx950 a read-only sweep streams at 6.5-7.0 TB/s with it against
 // 5.8-6.1 TB/s without).  `p` is 16-byte aligned.

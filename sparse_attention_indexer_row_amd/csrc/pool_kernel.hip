@@ -395,26 +395,6 @@ __device__ __forceinline__ void append_at_least(const float *row, uint32_t m, co
     });
 }
 
-// Histogram increment with the wave's most common bins merged first: rows
-// of block maxima crowd into few bins, and LDS atomics on one address
-// serialise.  Up to two rounds add the count of the lanes that share the
-// first remaining lane's bin with one atomic; the rest add one each.  All
-// lanes of the wave must call it together.
-__device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t bin, bool on) {
-    const uint32_t lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int round = 0; round < 2; ++round) {
-        const uint64_t act = __ballot(on);
-        if (act == 0ull) return;
-        const int leader = __ffsll((unsigned long long)act) - 1;
-        const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
-        const uint64_t same = __ballot(on && bin == lb);
-        if ((int)lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
-        if (on && bin == lb) on = false;
-    }
-    if (on) atomicAdd(&hist[bin], 1u);
-}
-
 // Appends w for the lanes where `take` holds: one atomic per wave, slots
 // by lane rank.  Slots at or past `cap` are dropped (never reached when the
 // counts are exact).  All lanes of the wave must call it together.
@@ -519,7 +499,7 @@ __device__ __forceinline__ void radix_pick(const uint32_t *hist, uint32_t need, 
     const uint32_t incl = wave_incl_scan(own);
     uint32_t suf = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1) - incl + own;
     if (lane == 0) sh.wave_sum[wv] = suf;
-    __syncthreads();
+    lds_barrier();
     for (int u = wv + 1; u < kRadixThreads / kWave; ++u) suf += sh.wave_sum[u];
     // suf = S(2 tid); S(2 tid + 1) = suf - h0; S(b) counts bins >= b
     const uint32_t s1 = suf - h0;
@@ -532,21 +512,25 @@ __device__ __forceinline__ void radix_pick(const uint32_t *hist, uint32_t need, 
         sh.above = suf - h0;
         sh.h = h0;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
-// Exact radix search in LDS: for `need` <= n distinct words buf[0, n),
-// returns (shift, thr) such that exactly `need` of them satisfy
-// (w >> shift) >= thr.  All threads of the workgroup call it together.
-// Inlined, with the result returned by value, so the kernel makes no calls
-// and keeps nothing on the stack.
+// Radix search in LDS: for `need` <= n distinct words buf[0, n), returns
+// (shift, thr) such that exactly `need` of them satisfy (w >> shift) >= thr.
+// With slack > 0 it may stop early, at the first digit whose bin holding the
+// need-th word has at most `slack` words: then between need and need +
+// slack - 1 of them satisfy it (the bin's lower edge; an estimate needs no
+// more).  All threads of the workgroup call it together.  Inlined, with the
+// result returned by value, so the kernel makes no calls and keeps nothing
+// on the stack.
 struct RadixCut {
     int shift;
     uint64_t thr;
 };
 
 __device__ __forceinline__ RadixCut lds_radix(const uint64_t *buf, uint32_t n, uint32_t need,
-                                              uint32_t *hist, RadixShared &sh) {
+                                              uint32_t *hist, RadixShared &sh,
+                                              uint32_t slack = 0u) {
     const int tid = threadIdx.x;
     const uint32_t lane = (uint32_t)tid & (kWave - 1);
     uint64_t pfx = 0;
@@ -555,18 +539,21 @@ __device__ __forceinline__ RadixCut lds_radix(const uint64_t *buf, uint32_t n, u
         const int ps = level == 0 ? 64 : radix_shift(level - 1);
         const uint32_t dmask = (1u << (ps - s)) - 1u;
         for (int b = tid; b < kRadixBins; b += kRadixThreads) hist[b] = 0u;
-        __syncthreads();
+        lds_barrier();
         for (uint32_t c = tid; c - lane < n; c += kRadixThreads) {
             const uint64_t w = c < n ? buf[c] : 0ull;
-            hist_add(hist, (uint32_t)(w >> s) & dmask, c < n && (level == 0 || (w >> ps) == pfx));
+            // Plain LDS atomics: on CDNA4 they beat merging a wave's equal
+            // bins first, even where many words share a bin.
+            const bool in = c < n && (level == 0 || (w >> ps) == pfx);
+            if (in) atomicAdd(&hist[(uint32_t)(w >> s) & dmask], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         radix_pick(hist, need, sh);
         const uint32_t t = sh.t, above = sh.above, h = sh.h;
-        __syncthreads();  // everyone has read the pick before the next scan writes it
+        lds_barrier();  // everyone has read the pick before the next scan writes it
         need -= above;
         pfx = level == 0 ? (uint64_t)t : ((pfx << (ps - s)) | t);
-        if (h == need || level == kRadixLevels - 1) return RadixCut{s, pfx};
+        if (h == need || h <= slack || level == kRadixLevels - 1) return RadixCut{s, pfx};
     }
 }
 
@@ -640,11 +627,12 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
         });
         done = true;
     } else if (m >= kEstimateMinRow) {
-        // Estimate: the j-th best word of an evenly spread sample, with j
-        // about four standard deviations above its expected count, admits
-        // a little more than k words; one pass appends every word at or
-        // above it to LDS.  When at least k and at most the buffer's
-        // capacity arrive, the winners are found among them exactly.
+        // Estimate: at or a little below the j-th best word of an evenly
+        // spread sample, with j about four standard deviations above its
+        // expected count, it admits a little more than k words; one pass
+        // appends every word at or above it to LDS.  When at least k and at
+        // most the buffer's capacity arrive, the winners are found among
+        // them exactly.
         const float lam = (float)k * (float)kSampleWords / (float)m;
         const uint32_t j = (uint32_t)ceilf(lam + 4.0f * sqrtf(lam) + 4.0f);
         if (j < kSampleWords) {
@@ -662,10 +650,14 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
             const RowParts body = row_parts(row, m);
             float4 first[kAdmitU];
             if (threadIdx.x - (threadIdx.x & (kWave - 1)) < body.n4) admit_load(first, body, threadIdx.x);
-            __syncthreads();
-            const RadixCut ec = lds_radix(samp, kSampleWords, j, hist, sh);
-            __syncthreads();  // the sample is read before the admission pass overwrites it
-            const uint64_t est = ec.thr << ec.shift;   // words >= est: j in the sample
+            // The sample's selection synchronises through LDS only, so the
+            // first group stays in flight meanwhile.
+            lds_barrier();
+            const RadixCut ec = lds_radix(samp, kSampleWords, j, hist, sh, j / 4u + 1u);
+            lds_barrier();  // the sample is read before the admission pass overwrites it
+            // words >= est: j to j + j/4 of the sample (the search stops at
+            // the first digit whose bin is that small)
+            const uint64_t est = ec.thr << ec.shift;
             append_at_least(row, m, wm, est, cand, &sh.ncand, kRadixCand, first);
             __syncthreads();
             const uint32_t nc = sh.ncand;
@@ -698,11 +690,12 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
             __syncthreads();
             if (level == 0) {
                 for_each_word(row, m, wm, [&](uint64_t w, bool valid) {
-                    hist_add(hist, (uint32_t)(w >> s) & dmask, valid);
+                    if (valid) atomicAdd(&hist[(uint32_t)(w >> s) & dmask], 1u);
                 });
             } else {
                 for_each_word(row, m, wm, [&](uint64_t w, bool valid) {
-                    hist_add(hist, (uint32_t)(w >> s) & dmask, valid && (w >> ps) == pfx);
+                    const bool in = valid && (w >> ps) == pfx;
+                    if (in) atomicAdd(&hist[(uint32_t)(w >> s) & dmask], 1u);
                 });
             }
             __syncthreads();

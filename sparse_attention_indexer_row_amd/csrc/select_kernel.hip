@@ -1187,15 +1187,6 @@ __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_
     }
 }
 
-// Workgroup barrier that orders LDS accesses only: global loads a wave has in
-// flight stay in flight across it (a full __syncthreads() waits for them).
-// The end of a pass exchanges data through LDS only.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // ---------------------------------------------------------------------------
 // End of a pass, run by every wave of the workgroup: the candidates are the
 // sorter's pool and every tray buffer still holding words; the best
