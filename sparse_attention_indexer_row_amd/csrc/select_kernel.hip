@@ -1544,9 +1544,29 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         s_kmax = 0u;
     }
     if (threadIdx.x < 2 * kMaxWaves) s_fill[threadIdx.x / 2][threadIdx.x % 2] = 0u;
-    __syncthreads();
 
     const RowGeom g = row_geometry(p, r);
+    // The sorter issues its sample's loads before any stream issues a block.
+    // Every workgroup of the chip starts at once, and loads issued after the
+    // streams' first blocks wait behind them (about 30 MB across the chip),
+    // while every stream waits for the estimate.  Lists of at least 512
+    // words keep over 128 registers anyway: there the sample's four lines
+    // are all loaded at once.  Narrower lists keep fewer registers (two
+    // workgroups can share a compute unit): they load the later lines after
+    // the first estimate.
+    constexpr int kUp = E >= 8 ? kSampleLines : 1;
+    SampleGeom sg{};
+    SampleLines<kUp> sl;
+    uint32_t jn2_row = 0;   // 0: no second estimate for this row
+    if (w == NS) {
+        sg = sample_geometry(g, p.seed, r);
+        jn2_row = second_rank(g, sg, k, S);
+        if (!(p.flags & kFlagNoEstimate) && sg.lines != 0u) {
+            load_first_lines<kUp>(g, sg, jn2_row != 0u ? (uint32_t)kUp : 1u, lane, sl);
+        }
+    }
+    lds_barrier();   // the LDS state above is set; the sample's loads stay in flight
+
     const VisitOrder ord = make_visit_order(p.seed, r, g.nb);
     uint64_t *pool = trays + (size_t)(2 * NS) * CW;            // [PoolCfg<E>::cap]
     uint64_t *fin = pool + PoolCfg<E>::cap;                     // [KP]
@@ -1608,18 +1628,6 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     }
 
     // ---- sorter (wave NS) ----
-    // Lists of at least 512 words keep over 128 registers anyway: there the
-    // sample's four lines are all loaded at once, and their words are formed
-    // right after the first estimate.  Narrower lists keep fewer registers
-    // (two workgroups can share a compute unit): they load the later lines
-    // after the first estimate.
-    constexpr int kUp = E >= 8 ? kSampleLines : 1;
-    const SampleGeom sg = sample_geometry(g, p.seed, r);
-    const uint32_t jn2_row = second_rank(g, sg, k, S);   // 0: no second estimate for this row
-    SampleLines<kUp> sl;
-    if (!(p.flags & kFlagNoEstimate) && sg.lines != 0u) {
-        load_first_lines<kUp>(g, sg, jn2_row != 0u ? (uint32_t)kUp : 1u, lane, sl);
-    }
     uint64_t line0 = 0ull;
     uint64_t tau = first_estimate<kUp>(g, sg, sl, k, p.flags, hist, gath, line0, lane);
     if (lane == 0) {
