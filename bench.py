@@ -33,19 +33,23 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 # Sources each bench path's kernels are built from; a traffic summary is
 # stale once any of them changes.
 SELECT_SOURCES = ["select_kernel.hip", "common.h", "wave_sort.h", "select_args.h"]
+RADIX_SOURCES = ["pool_kernel.hip", "common.h", "internal.h", "select_args.h", "wave_sort.h"]
 KERNEL_SOURCES = {
-    "vocab": ["pool_kernel.hip", "common.h", "internal.h", "select_args.h"],
+    "vocab": RADIX_SOURCES,
     "decode": ["decode_kernel.hip", "common.h", "internal.h", "select_args.h"],
     "pool": SELECT_SOURCES + ["pool_kernel.hip", "internal.h"],
-    "pooled": ["pool_kernel.hip", "common.h", "internal.h", "select_args.h"],
+    "pooled": RADIX_SOURCES,
+    # topk_select routes these shapes to the radix selection (4 x 16K and
+    # 64 x 128K at k = 512, 256 ragged rows at k = 2,048)
+    "small": RADIX_SOURCES,
+    "outlier": RADIX_SOURCES,
+    "ragged": RADIX_SOURCES,
 }
 
 
 def kernel_source_hash(workload: str = "adverse") -> str:
     h = hashlib.sha256()
-    names = KERNEL_SOURCES.get(workload)
-    if names is None:
-        names = KERNEL_SOURCES["vocab"] if workload == "ragged" else SELECT_SOURCES
+    names = KERNEL_SOURCES.get(workload, SELECT_SOURCES)
     for name in sorted(names):
         with open(os.path.join(ROOT, "sparse_attention_indexer_row_amd", "csrc", name), "rb") as f:
             h.update(name.encode())
