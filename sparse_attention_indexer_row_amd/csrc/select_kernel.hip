@@ -1469,10 +1469,11 @@ __device__ __forceinline__ void merge_lists(uint64_t (&acc)[E], uint64_t *lists,
                                             uint32_t lane);
 
 constexpr uint32_t kVerdictExit = 1u;
-// Segment lists in flight during a leader's merge (the widest lists have
-// registers for one at a time).
+// Segment lists in flight during a leader's merge: a group's other seven
+// lists at once for lists up to 512 words (one load latency per merge
+// level instead of three); the wider lists' registers hold one at a time.
 template <int E>
-constexpr uint32_t merge_batch() { return E <= 8 ? 3u : 1u; }
+constexpr uint32_t merge_batch() { return E <= 8 ? 7u : 1u; }
 constexpr uint32_t kVerdictRerun = 2u;
 
 template <int E>
