@@ -25,9 +25,12 @@ __device__ __forceinline__ uint32_t lane_id() {
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
+// Lane permutation inside a row of 16.  Every control used with it names a
+// valid source lane for every lane, so no old value is needed (a plain DPP
+// move, without the extra register that update_dpp's old operand costs).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
 template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
@@ -117,12 +120,17 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&a)[E], uint32_t lane) {
             up = ((((lane * E) & SIZE) == 0) == ASC);
         }
         const bool take_min = (lower == up);
+        // All exchanges first, then all compares, then all selects: the E
+        // independent chains overlap instead of each waiting on its own
+        // cross-lane move.
+        uint64_t y[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const uint64_t x = a[e];
-            const uint64_t y = xor_lane64<D>(x, lane);
-            a[e] = ((x < y) == take_min) ? x : y;
-        }
+        for (int e = 0; e < E; ++e) y[e] = xor_lane64<D>(a[e], lane);
+        bool keep[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) keep[e] = (a[e] < y[e]) == take_min;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[e] = keep[e] ? a[e] : y[e];
     }
 }
 
