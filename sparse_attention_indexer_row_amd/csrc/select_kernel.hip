@@ -988,9 +988,14 @@ __device__ __forceinline__ void raise_stream_bound(uint64_t &T, uint32_t kb, uin
     }
 }
 
-// Streams this wave's share of a row's blocks once: visit positions q, q+Q,
-// ... of the row's visit order.  Scores whose word beats max(threshold,
-// estimate) go to the tray; full trays are published to the sorter.  Returns
+// Streams, with the workgroup's other streams, the workgroup's share of a
+// row's blocks once: visit positions q, q+Q, ... of the row's visit order.
+// The share is dealt a block at a time: a wave takes the next index of the
+// share from the LDS counter *next (zero at the start of the pass) whenever
+// one of its load slots frees up, so the faster waves take more blocks and
+// every wave of the workgroup ends within about one block of the others.
+// Scores whose word beats max(threshold, estimate) go to the tray; full
+// trays are published to the sorter.  Returns
 // the number of scores that entered a tray and raises *tray_kmax to the
 // largest key put in a tray; the last tray is marked final.  With tau_ready
 // set, the estimate is read from tau_src once the sorter flags it, after the
@@ -998,7 +1003,7 @@ __device__ __forceinline__ void raise_stream_bound(uint64_t &T, uint32_t kb, uin
 // once, to its second estimate).
 //
 // Per block the wave does little besides the loads: the visit order is
-// computed 64 blocks ahead by the vector unit (one permutation step per
+// computed 64 indices at a time by the vector unit (one permutation step per
 // lane) and read back with one v_readlane; interior blocks are loaded from a
 // wave-uniform base plus a fixed per-lane offset; the shared threshold is
 // read from LDS early and folded in after the block's tests.
@@ -1006,14 +1011,14 @@ constexpr uint32_t kTrayFinal = 0x80000000u;   // fill flag: the stream's last t
 
 template <int E, bool SPLIT>
 __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOrder &ord,
-                                                 uint32_t q, uint32_t Q, uint64_t tau,
-                                                 uint32_t *tau_ready,
+                                                 uint32_t q, uint32_t Q, uint32_t *next,
+                                                 uint64_t tau, uint32_t *tau_ready,
                                                  uint64_t *tau_src, uint64_t &T, uint64_t *trays,
                                                  uint32_t w, uint32_t CW, uint32_t Wm,
                                                  uint64_t *sT, uint32_t (*fill)[2], uint64_t *gT,
                                                  uint32_t *tray_kmax, uint32_t lane) {
     constexpr int D = Cfg<E>::D;
-    const uint32_t mine = q < g.nb ? (g.nb - 1u - q) / Q + 1u : 0u;
+    const uint32_t mine = q < g.nb ? (g.nb - 1u - q) / Q + 1u : 0u;   // the workgroup's blocks
     uint32_t cur = 0, cnt = 0, entered = 0;
     uint32_t kmx = 0;  // this lane's largest key put in a tray
     uint32_t lk[E];   // this lane's E best keys seen, descending (0 = none)
@@ -1022,7 +1027,7 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
     uint64_t *tray = trays + (size_t)(2 * w) * CW;
     if (mine == 0u) return 0u;
 
-    // Visit list: lane j holds the block of this stream's step c0 + j.
+    // Visit list: lane j holds the block of the share's index c0 + j.
     uint32_t c0 = 0;
     auto visit_chunk = [&](uint32_t first) __attribute__((always_inline)) {
         const uint32_t t = first + lane;
@@ -1032,7 +1037,8 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
 
     float4 buf[D][kLoadsPerBlock];
     uint32_t bid[D];
-    // Block of step u; past the stream's end the last block is read again:
+    uint32_t idx[D];   // share index of the block in each slot (>= mine: none)
+    // Block of index u; past the share's end the last block is read again:
     // every slot issues exactly one set of loads per visit, so the wait
     // before each slot is the same static count every time.
     auto block_of = [&](uint32_t u) __attribute__((always_inline)) {
@@ -1056,10 +1062,21 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
             dst[u] = load_block4(rs, lane_off + (uint32_t)u * 1024u);
         }
     };
+    // Next share index, taken by lane 0 (read back with readfirstlane as
+    // late as possible: the atomic's return is waited for there).
+    auto take = [&](uint32_t n) __attribute__((always_inline)) {
+        uint32_t i = 0u;
+        if (lane == 0) i = __hip_atomic_fetch_add(next, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return i;
+    };
+    {
+        const uint32_t i0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)take((uint32_t)D));
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        bid[d] = block_of((uint32_t)d);
-        issue(buf[d], bid[d]);
+        for (int d = 0; d < D; ++d) {
+            idx[d] = i0 + (uint32_t)d;
+            bid[d] = block_of(idx[d]);
+            issue(buf[d], bid[d]);
+        }
     }
     // The first blocks are in flight while the sorter computes the estimate.
     if (tau_ready) {
@@ -1069,17 +1086,19 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
     }
     const bool lane_bounds = tau == 0ull;   // the estimate, when present, is far tighter
 
-    for (uint32_t t0 = 0; t0 < mine; t0 += D) {
+    // Indices only grow, so slot 0 holds the round's smallest: once it is
+    // past the share's end, so is every slot.
+    while (idx[0] < mine) {
         // A later, tighter estimate: read now, folded in after this round.
         const uint64_t tau_next =
             tau_ready ? __hip_atomic_load(tau_src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
                       : 0ull;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const uint32_t t = t0 + (uint32_t)d;
+            const uint32_t taken = take(1u);
             const uint64_t shared_T = __hip_atomic_load(sT, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (t < mine) {
+            if (idx[d] < mine) {
                 const uint64_t F = umax64(T, tau);
                 const int32_t tb = prefilter_bound(F);
                 const uint32_t vbase = bid[d] * (uint32_t)kBlock;
@@ -1126,7 +1145,8 @@ __device__ __forceinline__ uint32_t stream_share(const RowGeom &g, const VisitOr
                     }
                 }
             }
-            bid[d] = block_of(t + (uint32_t)D);
+            idx[d] = (uint32_t)__builtin_amdgcn_readfirstlane((int)taken);
+            bid[d] = block_of(idx[d]);
             issue(buf[d], bid[d]);
             T = umax64(T, uniform64(shared_T));
             if (cnt >= Wm) {
@@ -1513,6 +1533,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     __shared__ uint64_t s_tau;                    // sampled estimate (0 = none)
     __shared__ uint32_t s_fill[kMaxWaves][2];     // published tray word counts
     __shared__ uint32_t s_done;                   // streamers finished with the current pass
+    __shared__ uint32_t s_next;                   // next share index to stream
     __shared__ uint32_t s_ready;                  // estimate published
     __shared__ uint32_t s_verdict;                // after the first pass: exit or rerun
     __shared__ uint32_t s_pc;                     // pool words at the end of a pass
@@ -1540,6 +1561,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         s_T = 0ull;
         s_tau = 0ull;
         s_done = 0u;
+        s_next = 0u;
         s_ready = 0u;
         s_verdict = 0u;
         s_kmax = 0u;
@@ -1596,12 +1618,13 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     if (w < NS) {
         // ---- streamer ----
         uint64_t T = 0ull;
-        uint32_t q = s * NS + w, Q = S * NS;
+        uint32_t q = s, Q = S;   // the segment's blocks: visit positions s, s+S, ...
         uint32_t entered = 0;
         for (int pass = 0; pass < 2; ++pass) {
             // Pass 0 reads the estimate once its first loads are issued; a
             // rerun streams the whole row without it.
-            entered += stream_share<E, SPLIT>(g, ord, q, Q, 0ull, pass == 0 ? &s_ready : nullptr,
+            entered += stream_share<E, SPLIT>(g, ord, q, Q, &s_next, 0ull,
+                                              pass == 0 ? &s_ready : nullptr,
                                               &s_tau, T, trays, w, CW,
                                               (uint32_t)p.watermark, &s_T, s_fill, gT, &s_kmax,
                                               lane);
@@ -1619,8 +1642,8 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
             if (verdict != kVerdictRerun) break;
             // Stream the whole row again, without the estimate.
-            q = w;
-            Q = NS;
+            q = 0u;
+            Q = 1u;
         }
         if (p.stats && lane == 0 && entered > 0) {
             atomicAdd(p.stats + 2 * (size_t)r, (unsigned long long)entered);
@@ -1677,6 +1700,7 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         reset_sorter(ss, hist, lane);
         if (lane == 0) {
             __hip_atomic_store(&s_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(&s_next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __hip_atomic_store(&s_kmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         set_verdict(kVerdictRerun);
