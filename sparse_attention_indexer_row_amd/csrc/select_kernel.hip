@@ -53,7 +53,11 @@ constexpr int kLoadsPerBlock = kBlock / (kWave * 4);  // dwordx4 loads per lane 
 template <int E>
 struct Cfg {
     static constexpr int KP = kWave * E;       // kept-list words
-    static constexpr int D = E <= 8 ? 4 : 2;   // blocks in flight per wave
+    // Blocks in flight per wave.  Two beat one, three and four at every
+    // list width on gfx950 (seven streams per compute unit each reading
+    // 4 KB blocks at random places in the row): fewer blocks open at once
+    // across the chip reads faster.
+    static constexpr int D = 2;
     // Largest workgroup: the widest lists need more than half a SIMD's
     // registers per wave, so they run at most one wave per SIMD.
     static constexpr int kMaxThreads = kWave * (E >= 32 ? 4 : kMaxWaves);
