@@ -110,6 +110,16 @@ __device__ __forceinline__ void store_list(uint64_t *lists, uint32_t slot, const
     for (int e = 0; e < E; ++e) lists[off + (uint32_t)(e * kWave) + lane] = a[e];
 }
 
+// Loads a descending transposed list, as it is, into the blocked register
+// layout.
+template <int E>
+__device__ __forceinline__ void load_list(uint64_t (&a)[E], const uint64_t *lists, uint32_t slot,
+                                          uint32_t lane) {
+    const uint32_t off = list_offset<E>(slot);
+#pragma unroll
+    for (int e = 0; e < E; ++e) a[e] = lists[off + (uint32_t)(e * kWave) + lane];
+}
+
 // Loads a descending transposed list reversed, i.e. ascending, into the
 // blocked register layout.
 template <int E>
@@ -1499,6 +1509,7 @@ constexpr uint32_t kVerdictExit = 1u;
 template <int E>
 constexpr uint32_t merge_batch() { return E <= 8 ? 7u : 1u; }
 constexpr uint32_t kVerdictRerun = 2u;
+constexpr uint32_t kVerdictMerge = 3u;   // join the leader's merge, then wait again
 
 template <int E>
 __device__ __forceinline__ void merge_lists(uint64_t (&acc)[E], uint64_t *lists, uint32_t first,
@@ -1528,6 +1539,52 @@ __device__ __forceinline__ void merge_lists(uint64_t (&acc)[E], uint64_t *lists,
     }
 }
 
+// A leader's merge of three or more kept lists by all waves of its
+// workgroup: the `count` lists at workspace slots first + t*stride.  Worker j
+// (wave NS - j, so the sorter is worker 0) of P = min(NW, ceil(count/2))
+// folds lists j, j+P, ... from the workspace, clearing each behind it; then
+// each round halves the number of partial lists: the upper half's workers
+// pass theirs through LDS `x` (two buffers in turn, floor(P/2) lists each) to
+// the lower half's, which merge them.  The sorter ends with the result in
+// acc.  Every wave of the workgroup calls this with the same arguments and
+// meets the same barriers.  With 64*E <= 1024 the buffers fit in the tray
+// buffers (2 * floor(P/2) * 64*E <= NW * 1024 <= 2 * NS * tray words).
+template <int E>
+__device__ __forceinline__ void tree_merge(uint64_t (&acc)[E], uint64_t *lists, uint32_t first,
+                                           uint32_t count, uint32_t stride, uint64_t *x,
+                                           uint32_t j, uint32_t NW, uint32_t lane) {
+    static_assert(E <= 16, "the exchange buffers must fit in the trays");
+    uint64_t zero[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) zero[e] = 0ull;
+    const uint32_t half = (count + 1u) / 2u;
+    const uint32_t P = NW < half ? NW : half;
+    if (j < P) {
+        load_list<E>(acc, lists, first + j * stride, lane);
+        store_list<E>(lists, first + j * stride, zero, lane);
+        for (uint32_t t = j + P; t < count; t += P) {
+            uint64_t b[E];
+            load_list_reversed<E>(b, lists, first + t * stride, lane);
+            store_list<E>(lists, first + t * stride, zero, lane);
+            keep_best<E>(acc, b, lane);
+        }
+    }
+    const uint32_t slots = P / 2u;
+    uint32_t m = P;
+    for (uint32_t buf = 0; m > 1u; buf ^= 1u) {
+        const uint32_t h = (m + 1u) / 2u;
+        uint64_t *xb = x + (size_t)buf * slots * (uint32_t)(kWave * E);
+        if (j >= h && j < m) store_list<E>(xb, j - h, acc, lane);
+        lds_barrier();
+        if (j < m - h) {
+            uint64_t b[E];
+            load_list_reversed<E>(b, xb, j, lane);
+            keep_best<E>(acc, b, lane);
+        }
+        m = h;
+    }
+}
+
 template <int E, bool SPLIT>
 __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs p) {
     constexpr int KP = Cfg<E>::KP;
@@ -1539,7 +1596,8 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     __shared__ uint32_t s_done;                   // streamers finished with the current pass
     __shared__ uint32_t s_next;                   // next share index to stream
     __shared__ uint32_t s_ready;                  // estimate published
-    __shared__ uint32_t s_verdict;                // after the first pass: exit or rerun
+    __shared__ uint32_t s_verdict;                // after the first pass: exit, rerun or merge
+    __shared__ uint32_t s_mrg[3];                 // a merge's first slot, count and stride
     __shared__ uint32_t s_pc;                     // pool words at the end of a pass
     __shared__ EndShared s_end;                   // counters of the end-of-pass selection
     __shared__ uint32_t s_kmax;                   // largest key the streamers put in a tray
@@ -1619,6 +1677,27 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         return n;
     };
 
+    // Split rows with lists up to 512 words (wider ones would spill
+    // registers): a leader merging five or more lists (fewer gain less than
+    // the call costs) calls on every wave
+    // (kVerdictMerge) and runs tree_merge with the parameters in s_mrg.  The
+    // first barrier means every wave has read the verdict, so the sorter
+    // clears it there; the last one publishes that.
+    constexpr bool kTree = SPLIT && E <= 8;
+    uint64_t *lists = SPLIT ? p.ws_lists + (size_t)r * S * KP : nullptr;
+    auto team_merge = [&](uint64_t (&acc)[E]) __attribute__((always_inline)) {
+        lds_barrier();
+        if (w == NS && lane == 0) {
+            __hip_atomic_store(&s_verdict, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the published lists
+        if constexpr (kTree) {
+            tree_merge<E>(acc, lists, lds_load_u32(&s_mrg[0]), lds_load_u32(&s_mrg[1]),
+                          lds_load_u32(&s_mrg[2]), trays, NS - w, NW, lane);
+        }
+        lds_barrier();
+    };
+
     if (w < NS) {
         // ---- streamer ----
         uint64_t T = 0ull;
@@ -1642,8 +1721,13 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
             }
             if (pass == 1) break;
             uint32_t verdict;
-            while ((verdict = lds_load_u32(&s_verdict)) == 0u) __builtin_amdgcn_s_sleep(2);
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            for (;;) {
+                while ((verdict = lds_load_u32(&s_verdict)) == 0u) __builtin_amdgcn_s_sleep(2);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+                if (verdict != kVerdictMerge) break;
+                uint64_t unused[E];
+                team_merge(unused);
+            }
             if (verdict != kVerdictRerun) break;
             // Stream the whole row again, without the estimate.
             q = 0u;
@@ -1711,7 +1795,6 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
     };
 
     // Split rows: segments publish their lists in groups of kMergeGroup.
-    uint64_t *lists = SPLIT ? p.ws_lists + (size_t)r * S * KP : nullptr;
     const uint32_t G = (uint32_t)kMergeGroup;
     const uint32_t ng = (S + G - 1u) / G;
     const uint32_t grp = s / G, g0 = grp * G;
@@ -1783,11 +1866,21 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
         uint32_t first = g0, count = gsz, stride = 1u, own = s;
         for (int level = 0; lead; ++level) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            uint64_t zero[E];
+            if (kTree && count >= 5u) {
+                if (lane == 0) {
+                    s_mrg[0] = first;
+                    s_mrg[1] = count;
+                    s_mrg[2] = stride;
+                }
+                set_verdict(kVerdictMerge);
+                team_merge(kept_sorted);
+            } else {
+                uint64_t zero[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) zero[e] = 0ull;
-            store_list<E>(lists, own, zero, lane);
-            merge_lists<E>(kept_sorted, lists, first, count, stride, own, lane);
+                for (int e = 0; e < E; ++e) zero[e] = 0ull;
+                store_list<E>(lists, own, zero, lane);
+                merge_lists<E>(kept_sorted, lists, first, count, stride, own, lane);
+            }
             if (level == 1 || ng == 1u) break;
             if (lane == 0) __hip_atomic_store(gticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             store_list<E>(lists, g0, kept_sorted, lane);
