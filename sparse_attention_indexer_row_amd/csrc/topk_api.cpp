@@ -144,18 +144,23 @@ Plan make_plan(int32_t rows, int32_t n, int32_t k, const topk_options *o, int cu
         p.split = o->split;
     } else {
         // Enough workgroups to fill every compute unit once (as many per
-        // unit as its LDS holds), but at least six blocks per wave: every
-        // segment adds a list to the leader's merge, and on one to four rows
-        // of 256K-1M scores six blocks per wave measured 1-4 us faster than
-        // four (24 segments instead of 36 on a million-score row).
+        // unit as its LDS holds), each segment at least max(16, nb/24)
+        // blocks: every segment adds a list to the leader's merge, and on
+        // 128K-1M-score rows smaller segments measured slower (1-4 rows of
+        // 1M scores: 24 segments; of 256K: 16; of 128K: 8).  Past half the
+        // chip's compute units, segments keep at least 32 blocks (16 rows of
+        // 256K scores: 8 segments each beat 16 by 2 us).
         const int64_t nb = ((int64_t)n + 3 + kBlock - 1) / kBlock;
         const int64_t per_cu = std::max<int64_t>(
             1, (int64_t)((kLdsPerWorkgroup - kStaticLdsBound) / std::max<size_t>(p.lds, 1)));
         const int64_t target = per_cu * (int64_t)cus;
         int64_t s = rows > 0 ? (target + rows - 1) / rows : 1;
-        int64_t cap = nb / (6 * (int64_t)(p.waves - 1));
+        int64_t cap = nb / std::max<int64_t>(16, nb / 24);
         if (cap < 1) cap = 1;
         if (s > cap) s = cap;
+        if ((int64_t)rows * s * 2 > (int64_t)cus && s > 1 && nb / s < 32) {
+            s = std::max<int64_t>(1, nb / 32);
+        }
         if (s > TOPK_MAX_SPLIT) s = TOPK_MAX_SPLIT;
         if (s < 1) s = 1;
         p.split = (int)s;
@@ -255,23 +260,26 @@ constexpr int32_t kMaxGridRows = 65535;
 // streaming filter: every k above the filter's widest list, and, on rows no
 // longer than 262,144 scores,
 //   k > 512         always (the streaming lists of 1,024 words and more
-//                   spend their time sorting; radix 0.18-0.87x the time),
-//   256 < k <= 512  rows up to 131,072 scores, or any such row once there
-//                   are at least half as many rows as compute units,
-//   128 < k <= 256  rows up to 65,536 scores, or up to 131,072 with at
-//                   least half as many rows as compute units.
+//                   spend their time sorting; radix 0.7-0.9x the time),
+//   256 < k <= 512  rows up to 65,536 scores; rows up to 131,072 once there
+//                   are more than an eighth as many rows as compute units;
+//                   any such row once there are half as many,
+//   128 < k <= 256  rows up to 65,536 scores once there are more than a
+//                   64th as many rows as compute units, or up to 131,072
+//                   with half as many.
 // Those are the shapes where one workgroup per row, the whole row read once
 // into the candidate pass, beats the streaming path's fixed chain of
-// estimate, trays and end-of-pass selection (measured on MI355X over 1 to
-// 256 rows of N(0,1) scores of 16K to 256K: radix 0.71-0.98x the time
-// there; 1.0-1.7x elsewhere, and always slower on million-score rows).
+// estimate, trays, end-of-pass selection and merge (measured on MI355X over
+// 1 to 256 rows of N(0,1) scores of 64K to 256K: radix 4-9 us faster there;
+// on 1-16 rows of 131,072 scores at k = 384-512 the split streaming path is
+// 2-6 us faster, and it always is on million-score rows).
 bool prefer_radix(int32_t rows, int32_t n, int32_t k, int cus) {
     if (k > TOPK_MAX_K_STREAM) return true;   // wider than the streaming filter's lists
     if (n > 262144) return false;
     const bool many = (int64_t)rows * 2 >= cus;
     if (k > 512) return true;
-    if (k > 256) return n <= 131072 || many;
-    if (k > 128) return n <= 65536 || (n <= 131072 && many);
+    if (k > 256) return n <= 65536 || (n <= 131072 && (int64_t)rows * 8 > cus) || many;
+    if (k > 128) return (n <= 65536 && (int64_t)rows * 64 > cus) || (n <= 131072 && many);
     return false;
 }
 

@@ -326,14 +326,17 @@ def test_plan_paths(lib):
     assert _select_plan(lib, 128, 1 << 20, 2048).path == _lib.TOPK_PATH_STREAM
     assert _select_plan(lib, 128, 1 << 20, 512).path == _lib.TOPK_PATH_STREAM
     # short rows: the radix selection from k = 129 up (longer rows and more
-    # of them raise the bar), the streaming filter below
+    # of them raise the bar, a few rows of 128K go to the split stream), the
+    # streaming filter below
     cus = _select_plan(lib, 1, 1 << 20, 512).compute_units
     for rows, n, k, radix in ((4, 16384, 512, True), (64, 131072, 512, True),
                               (64, 262144, 512, False), (cus, 262144, 512, True),
                               (1, 16384, 1024, True), (1, 262144, 1000, True),
                               (16, 65536, 256, True), (16, 131072, 256, False),
                               (cus, 131072, 256, True), (cus, 262144, 256, False),
-                              (1, 16384, 128, False), (cus, 65536, 64, False)):
+                              (1, 16384, 128, False), (cus, 65536, 64, False),
+                              (1, 131072, 512, False), (16, 131072, 384, False),
+                              (4, 65536, 512, True), (1, 65536, 256, False)):
         want = _lib.TOPK_PATH_RADIX if radix else _lib.TOPK_PATH_STREAM
         assert _select_plan(lib, rows, n, k).path == want, (rows, n, k)
     # with options the streaming path is kept up to its widest list
