@@ -7,9 +7,11 @@ The timed region rotates over several copies of the batch (more bytes than
 the 256 MB last-level cache) so every step reads cold HBM.
 
 Prints one JSON line.  `value` is effective HBM read GB/s = 4 * (valid
-scores) / (wall time per step).  `roofline` compares the selection kernel's
-average duration (HIP events on the launch stream) with the 8 TB/s HBM peak.
-`cpu_baseline` times the CPU oracle on the host cores over the same batch.
+scores) / (time per step), the K steps timed back to back between two events
+on the launch stream.  `roofline` compares the selection kernel's average
+launch duration (each of K further launches between its own pair of events)
+with the 8 TB/s HBM peak.  `cpu_baseline` times the CPU oracle on the host
+cores over the same batch.
 """
 
 from __future__ import annotations
@@ -703,28 +705,37 @@ def main() -> int:
         step(i + 1)
     torch.cuda.synchronize()
 
+    # The timed region: K steps back to back, events only at its two ends (an
+    # event pair around every launch would hold each launch until the one
+    # before has ended and cost several microseconds a step).
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_all0.record(stream)
     for i in range(K):
-        starts[i].record(stream)
         step(args.warmup + 1 + i)
-        ends[i].record(stream)
     t_all1.record(stream)
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
     total_ms = t_all0.elapsed_time(t_all1)
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = total_ms / K
+    # Launch durations (the roofline's): the same K steps once more, each
+    # bracketed by its own pair of events on the launch stream.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        starts[i].record(stream)
+        step(args.warmup + 1 + K + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     kern_ms = float(np.mean(per_launch_ms))
-    print(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step, kernel avg {kern_ms * 1e3:.1f} us, "
-          f"median {np.median(per_launch_ms) * 1e3:.1f} us, wall {1e3 * (wall1 - wall0) / K:.1f} ms/step",
-          file=sys.stderr, flush=True)
+    print(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step, wall {1e3 * (wall1 - wall0) / K:.3f} "
+          f"ms/step; launch durations over {K} more: mean {kern_ms * 1e3:.1f} us, median "
+          f"{np.median(per_launch_ms) * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     if args.profile_run:
         # Counter calibration: a plain copy of a known size (1 GiB read, 1 GiB
