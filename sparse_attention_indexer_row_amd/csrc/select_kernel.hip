@@ -789,9 +789,13 @@ __device__ __forceinline__ float4 load_block4(__amdgpu_buffer_rsrc_t rs, uint32_
 //     a few blocks later.
 //
 // For a row of independent scores, a sample of m scores holds about
-// lam = m k / L of the row's best k, and j = ceil(lam + 6 sqrt(lam) + 6)
+// lam = m k / L of the row's best k, and j = ceil(lam + c sqrt(lam) + c)
 // lies far enough above that for the estimate to fall below the k-th best in
-// all but a vanishing fraction of rows.  A group or a line contributes one
+// all but a vanishing fraction of rows: c = 4 for the first estimate (at
+// lam = 1, a row's best k hold 9 or more of the sample in about one row in a
+// million) and c = 6 for the second, where a tighter rank measured slower on
+// split rows of N(0,1) scores.  The first's tighter rank took 0.6-2.9 us off
+// rows of 64K-1M scores at k = 64-512 (256 x 1M: 180.6 -> 177.8 us).  A group or a line contributes one
 // maximum however many of the row's best scores it holds, so crowding the
 // best scores together cannot lift an estimate either.  Neither is a bound:
 // the end of the pass checks that the k-th best admitted word is at least
@@ -846,9 +850,9 @@ __device__ __forceinline__ uint32_t load_line(const RowGeom &g, const SampleGeom
 }
 
 __device__ __forceinline__ uint32_t estimate_rank(uint32_t k, uint32_t words, uint32_t L,
-                                                  uint32_t limit) {
+                                                  uint32_t limit, float margin) {
     const float lam = (float)k * (float)words / (float)L;
-    const float jf = ceilf(lam + 6.0f * sqrtf(lam) + 6.0f);
+    const float jf = ceilf(lam + margin * sqrtf(lam) + margin);
     return jf <= (float)limit ? (uint32_t)jf : 0u;
 }
 
@@ -894,7 +898,7 @@ __device__ __forceinline__ uint64_t first_estimate(const RowGeom &g, const Sampl
                                                    uint64_t &line0, uint32_t lane) {
     line0 = 0ull;
     if ((flags & kFlagNoEstimate) || sg.lines == 0u) return 0ull;
-    const uint32_t jn = estimate_rank(k, kSampleWords, g.L, kSampleGroups * kWave / 2);
+    const uint32_t jn = estimate_rank(k, kSampleWords, g.L, kSampleGroups * kWave / 2, 4.0f);
     if (jn == 0u) return 0ull;
     if (flags & kFlagForceRerun) return ~0ull;  // admits nothing: forces the rerun path
     const float4 (&x)[kSampleSpan / 4] = sl.x[0];
@@ -948,7 +952,7 @@ __device__ __forceinline__ uint32_t second_rank(const RowGeom &g, const SampleGe
                                                 uint32_t k, uint32_t segments) {
     if (sg.lines != (uint32_t)kSampleLines || (uint64_t)segments << 18 > g.L) return 0u;
     constexpr uint32_t kLines = (uint32_t)(kWave * kSampleLines);
-    return estimate_rank(k, kLines * kSampleSpan, g.L, kLines / 2u);
+    return estimate_rank(k, kLines * kSampleSpan, g.L, kLines / 2u, 6.0f);
 }
 
 template <int UP>
