@@ -1318,7 +1318,13 @@ __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo,
     // The counters in *sh and hist3[0] are zero and the candidates final
     // (the caller's barrier).
     uint32_t n = 0;
-    if (hi >= lo) {
+    // With at most k candidate slots (pool words plus busy trays' words),
+    // every candidate at or above lo is kept: the counting pass is skipped
+    // and n is the number appended (segments of rows split many ways).
+    const uint32_t slots =
+        c.pc + (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(c.lane_cnt), kWave - 1);
+    const bool few = slots <= k;
+    if (!few && hi >= lo) {
         int top = hi == lo ? 0 : 63 - __clzll(lo ^ hi);
         uint64_t fmask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
         uint64_t prefix = hi & fmask;
@@ -1396,6 +1402,7 @@ __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo,
         append_shared(fin, &sh->out, x, x >= lo && x != 0ull, lane);
     });
     lds_barrier();
+    if (few) n = lds_load_u32(&sh->out);
     return n;
 }
 
