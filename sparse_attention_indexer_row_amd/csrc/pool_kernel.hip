@@ -413,67 +413,185 @@ __device__ __forceinline__ void wave_append(uint64_t *buf, uint32_t *counter, ui
     }
 }
 
-// Descending sort of p2 (a power of two) words in LDS with the waves'
-// registers doing most of the work.  Runs of R = 64 E words (one per wave,
+// Descending sort of p2 <= 1,024 words (a power of two) in LDS with the
+// waves' registers doing most of the work.  Runs of R = 64 E words (one per wave,
 // E per lane) are sorted in registers, alternately descending and
 // ascending; each further level of the bitonic network then needs LDS only
-// for its stages of stride >= R (a workgroup barrier each), and finishes
-// every run with a register merge.  For 4,096 words: 10 LDS stages instead
-// of the plain network's 78.  The caller syncs before; ends with a barrier.
+// for its stages of stride >= R, and finishes every run with a register
+// merge.  Between the register phases a run is kept transposed in LDS (its
+// word lane*E + e at e*64 + lane), so a wave moves it with conflict-free
+// 64-lane accesses; only the first load and the last store use the plain
+// layout.  Every run is permuted the same way and the LDS stages (stride >=
+// R) pair equal offsets of different runs, with a direction set by a bit
+// above the run, so they index the transposed words directly, consecutive
+// threads on consecutive words.  They go two strides at a time where they
+// can: each
+// thread takes the four words {b, b+h, b+2h, b+3h} and does both
+// compare-exchange stages (strides 2h and h) in registers, one barrier for
+// the pair.  For 4,096 words: 6 barriers for the LDS stages instead of 10
+// (and 78 for the plain network).  The caller syncs before; ends with a
+// barrier.
 template <int E>
-__device__ __forceinline__ void run_sort_desc(uint64_t *x, uint32_t p2, uint32_t nw) {
+__device__ __forceinline__ void run_sort_bitonic(uint64_t *x, uint32_t p2, uint32_t nw) {
     constexpr uint32_t R = 64u * E;
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     const bool active = w < nw;
+    // Compare-exchange of the words held for positions lo < hi: the larger
+    // first when the pair lies in a descending part (bit `size` clear).
+    auto cx = [](uint64_t &u, uint64_t &v, bool first_big) __attribute__((always_inline)) {
+        const uint64_t big = u > v ? u : v, small = u > v ? v : u;
+        u = first_big ? big : small;
+        v = first_big ? small : big;
+    };
     uint64_t a[E];
     if (active) {
 #pragma unroll
         for (int e = 0; e < E; ++e) a[e] = x[w * R + lane * E + e];
         if ((w & 1u) == 0u) wave_sort<E, false>(a, lane);
         else wave_sort<E, true>(a, lane);
+        if (p2 == R) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) x[w * R + lane * E + e] = a[e];
+            for (int e = 0; e < E; ++e) x[w * R + lane * E + e] = a[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[w * R + (uint32_t)e * kWave + lane] = a[e];
+        }
     }
     __syncthreads();
     for (uint32_t size = 2 * R; size <= p2; size <<= 1) {
-        for (uint32_t stride = size >> 1; stride >= R; stride >>= 1) {
+        uint32_t stride = size >> 1;
+        for (; stride >= 2u * R; stride >>= 2) {
+            // strides `stride` and stride/2 together, over groups of four
+            const uint32_t h = stride >> 1;
+            for (uint32_t t = tid; t < (p2 >> 2); t += kRadixThreads) {
+                const uint32_t b = ((t / h) * (stride << 1)) + (t % h);
+                const bool first_big = (b & size) == 0u;
+                uint64_t v0 = x[b], v1 = x[b + h], v2 = x[b + stride], v3 = x[b + stride + h];
+                cx(v0, v2, first_big);
+                cx(v1, v3, first_big);
+                cx(v0, v1, first_big);
+                cx(v2, v3, first_big);
+                x[b] = v0;
+                x[b + h] = v1;
+                x[b + stride] = v2;
+                x[b + stride + h] = v3;
+            }
+            __syncthreads();
+        }
+        if (stride >= R) {
             for (uint32_t t = tid; t < (p2 >> 1); t += kRadixThreads) {
                 const uint32_t lo = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
                 const uint32_t hi = lo + stride;
-                const uint64_t u = x[lo], v = x[hi];
-                const bool first_big = (lo & size) == 0;
-                if (first_big ? u < v : u > v) {
-                    x[lo] = v;
-                    x[hi] = u;
-                }
+                uint64_t u = x[lo], v = x[hi];
+                cx(u, v, (lo & size) == 0u);
+                x[lo] = u;
+                x[hi] = v;
             }
             __syncthreads();
         }
         if (active) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) a[e] = x[w * R + lane * E + e];
+            for (int e = 0; e < E; ++e) a[e] = x[w * R + (uint32_t)e * kWave + lane];
             if (((w * R) & size) == 0u) wave_merge<E, false>(a, lane);
             else wave_merge<E, true>(a, lane);
+            if (size == p2) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) x[w * R + lane * E + e] = a[e];
+                for (int e = 0; e < E; ++e) x[w * R + lane * E + e] = a[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) x[w * R + (uint32_t)e * kWave + lane] = a[e];
+            }
         }
         __syncthreads();
     }
 }
 
-// Descending sort of the p2 <= 8,192 winners: runs of 64 E words over up
-// to 16 waves, the plain LDS network below 64 words.
-__device__ __forceinline__ void sort_winners_desc(uint64_t *x, uint32_t p2) {
+// One merge-path level: pairs of descending runs of length L in src become
+// descending runs of 2L in dst.  Each thread writes c = p2 / threads
+// consecutive outputs (at least one): it finds how many of the first i
+// outputs of its pair come from the first run by a binary search along the
+// diagonal i, then merges its c outputs one at a time.  Equal words go to the
+// first run first, in the search and the merge alike (only the zero padding
+// repeats).
+__device__ __forceinline__ void merge_level_desc(const uint64_t *src, uint64_t *dst, uint32_t p2,
+                                                 uint32_t L) {
+    const uint32_t c = p2 > (uint32_t)kRadixThreads ? p2 / (uint32_t)kRadixThreads : 1u;
+    for (uint32_t o = threadIdx.x * c; o < p2; o += (uint32_t)kRadixThreads * c) {
+        const uint32_t base = o & ~(2u * L - 1u), i = o - base;
+        const uint64_t *A = src + base, *B = A + L;
+        uint32_t lo = i > L ? i - L : 0u, hi = i < L ? i : L;
+        while (lo < hi) {
+            const uint32_t m = (lo + hi + 1u) >> 1;
+            if (A[m - 1u] >= B[i - m]) lo = m;
+            else hi = m - 1u;
+        }
+        uint32_t a = lo, b = i - lo;
+        uint64_t va = a < L ? A[a] : 0ull, vb = b < L ? B[b] : 0ull;
+        for (uint32_t j = 0; j < c; ++j) {
+            const bool take_a = b >= L || (a < L && va >= vb);
+            dst[o + j] = take_a ? va : vb;
+            if (take_a) {
+                ++a;
+                va = a < L ? A[a] : 0ull;
+            } else {
+                ++b;
+                vb = b < L ? B[b] : 0ull;
+            }
+        }
+    }
+}
+
+// Descending sort of p2 >= 2,048 words (a power of two) in LDS: runs of
+// R = 64 E words (one per wave, E per lane) are sorted in registers by the
+// bitonic network, then merged pairwise level by level by merge path,
+// between x and the scratch buffer tmp (p2 words).  The bitonic network's
+// own merge levels cost several times the VALU work of these merges at that
+// size (68 register stages per word for 4,096 words, with four waves sharing
+// each SIMD: vocabulary rows at k = 4,096 56.3 -> 51.8 us per call); up to
+// 1,024 words they are the faster of the two.  The caller syncs before; ends
+// with a barrier.
+template <int E>
+__device__ __forceinline__ void run_sort_merge(uint64_t *x, uint64_t *tmp, uint32_t p2,
+                                               uint32_t nw) {
+    constexpr uint32_t R = 64u * E;
+    const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    if (w < nw) {
+        uint64_t a[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[e] = x[w * R + lane * E + e];
+        wave_sort<E, false>(a, lane);
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[w * R + lane * E + e] = a[e];
+    }
+    __syncthreads();
+    uint64_t *src = x, *dst = tmp;
+    for (uint32_t L = R; L < p2; L <<= 1) {
+        merge_level_desc(src, dst, p2, L);
+        __syncthreads();
+        uint64_t *t = src;
+        src = dst;
+        dst = t;
+    }
+    if (src != x) {
+        for (uint32_t i = tid; i < p2; i += (uint32_t)kRadixThreads) x[i] = src[i];
+        __syncthreads();
+    }
+}
+
+// Descending sort of the p2 <= 8,192 winners (tmp: p2 words of scratch):
+// runs of 64 E words over up to 16 waves, the plain LDS network below 64
+// words.
+__device__ __forceinline__ void sort_winners_desc(uint64_t *x, uint64_t *tmp, uint32_t p2) {
     if (p2 < 64u) {
         lds_bitonic<kRadixThreads, true>(x, p2);
     } else if (p2 <= 1024u) {
-        run_sort_desc<1>(x, p2, p2 / 64u);
+        run_sort_bitonic<1>(x, p2, p2 / 64u);
     } else if (p2 == 2048u) {
-        run_sort_desc<2>(x, p2, 16u);
+        run_sort_merge<2>(x, tmp, p2, 16u);
     } else if (p2 == 4096u) {
-        run_sort_desc<4>(x, p2, 16u);
+        run_sort_merge<4>(x, tmp, p2, 16u);
     } else {
-        run_sort_desc<8>(x, p2, 16u);
+        run_sort_merge<8>(x, tmp, p2, 16u);
     }
 }
 
@@ -738,7 +856,8 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
     while (p2 < ns) p2 <<= 1;
     for (uint32_t c = ns + tid; c < p2; c += kRadixThreads) sel[c] = 0ull;
     __syncthreads();
-    sort_winners_desc(sel, p2);
+    static_assert(kRadixCand >= kRadixSel, "the sort's scratch");
+    sort_winners_desc(sel, cand, p2);
     float *ov = a.out_vals + r * a.out_ld;
     int32_t *oi = a.out_idx + r * a.out_ld;
     for (uint32_t t = tid; t < k; t += kRadixThreads) {
