@@ -605,12 +605,16 @@ struct RadixShared {
 // Each thread holds two neighbouring bins; suffix sums run from the top
 // bin down: a shuffle scan inside each wave, then the totals of the waves
 // above.  The one thread whose bin crosses `need` publishes it; everyone
-// reads it after the barrier.
-__device__ __forceinline__ void radix_pick(const uint32_t *hist, uint32_t need, RadixShared &sh) {
+// reads it after the barrier.  The histogram is left all zero.
+__device__ __forceinline__ void radix_pick(uint32_t *hist, uint32_t need, RadixShared &sh) {
     static_assert(kRadixBins == 2 * kRadixThreads, "two bins per thread");
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     const uint32_t h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
+    // Each thread reads only its own two bins: it clears them for the next
+    // count (the barriers below order that before any later increment).
+    hist[2 * tid] = 0u;
+    hist[2 * tid + 1] = 0u;
     // sum of this lane's bins and every bin above it in the wave: the wave's
     // total less the inclusive prefix below this lane
     const uint32_t own = h0 + h1;
@@ -652,12 +656,13 @@ __device__ __forceinline__ RadixCut lds_radix(const uint64_t *buf, uint32_t n, u
     const int tid = threadIdx.x;
     const uint32_t lane = (uint32_t)tid & (kWave - 1);
     uint64_t pfx = 0;
+    // radix_pick leaves the histogram zero for the next level.
+    for (int b = tid; b < kRadixBins; b += kRadixThreads) hist[b] = 0u;
+    lds_barrier();
     for (int level = 0;; ++level) {
         const int s = radix_shift(level);
         const int ps = level == 0 ? 64 : radix_shift(level - 1);
         const uint32_t dmask = (1u << (ps - s)) - 1u;
-        for (int b = tid; b < kRadixBins; b += kRadixThreads) hist[b] = 0u;
-        lds_barrier();
         for (uint32_t c = tid; c - lane < n; c += kRadixThreads) {
             const uint64_t w = c < n ? buf[c] : 0ull;
             // Plain LDS atomics: on CDNA4 they beat merging a wave's equal
@@ -668,10 +673,14 @@ __device__ __forceinline__ RadixCut lds_radix(const uint64_t *buf, uint32_t n, u
         lds_barrier();
         radix_pick(hist, need, sh);
         const uint32_t t = sh.t, above = sh.above, h = sh.h;
-        lds_barrier();  // everyone has read the pick before the next scan writes it
         need -= above;
         pfx = level == 0 ? (uint64_t)t : ((pfx << (ps - s)) | t);
-        if (h == need || h <= slack || level == kRadixLevels - 1) return RadixCut{s, pfx};
+        if (h == need || h <= slack || level == kRadixLevels - 1) {
+            lds_barrier();  // everyone has read the pick before the caller goes on
+            return RadixCut{s, pfx};
+        }
+        // The next level's pick is written two barriers from here, after
+        // every thread has read this one.
     }
 }
 
