@@ -310,15 +310,22 @@ __device__ __forceinline__ void for_each_word(const float *row, uint32_t m, cons
 __device__ __forceinline__ void wave_append(uint64_t *buf, uint32_t *counter, uint32_t cap,
                                             uint64_t w, bool take);
 
-// Float4s per thread in one group of the admission pass.
+// Float4s per thread in one group of the admission pass (two groups are in
+// flight): eight on rows above kAdmitShortRow scores, four on shorter ones.
+// Rows of 16K-64K scores read faster with fewer loads outstanding (pooled
+// rows of 16,000: 27.6 -> 24.5 us per call; 4 x 16K 20.2 -> 18.8), rows of
+// 128K and more slower (vocabulary rows: 51.1 -> 52.0).
 constexpr uint32_t kAdmitU = 8;
+constexpr uint32_t kAdmitUShort = 4;
+constexpr uint32_t kAdmitShortRow = 65536;
 
-// Loads group `base` (thread index plus a multiple of kAdmitU * 1024) of a
-// row's aligned body.  Indices past the body read its last float4 again (no
+// Loads group `base` (thread index plus a multiple of U * 1024) of a row's
+// aligned body.  Indices past the body read its last float4 again (no
 // per-lane branch around a load); the counting masks them.
-__device__ __forceinline__ void admit_load(float4 (&d)[kAdmitU], const RowParts &p, uint32_t base) {
+template <uint32_t U>
+__device__ __forceinline__ void admit_load(float4 (&d)[U], const RowParts &p, uint32_t base) {
 #pragma unroll
-    for (uint32_t u = 0; u < kAdmitU; ++u) {
+    for (uint32_t u = 0; u < U; ++u) {
         const uint32_t q = base + u * kRadixThreads;
         d[u] = load_stream4(reinterpret_cast<const float *>(p.body + (q < p.n4 ? q : p.n4 - 1u)));
     }
@@ -326,11 +333,10 @@ __device__ __forceinline__ void admit_load(float4 (&d)[kAdmitU], const RowParts 
 
 // `first` holds the row's first group (admit_load at threadIdx.x), issued
 // early by the caller so that its memory latency overlaps other work.
-template <class W>
+template <uint32_t U, class W>
 __device__ __forceinline__ void append_at_least(const float *row, uint32_t m, const W &wm,
                                                 uint64_t lo, uint64_t *buf, uint32_t *counter,
-                                                uint32_t cap, const float4 (&first)[kAdmitU]) {
-    constexpr uint32_t U = kAdmitU;
+                                                uint32_t cap, const float4 (&first)[U]) {
     constexpr uint32_t STEP = U * kRadixThreads;
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const RowParts p = row_parts(row, m);
@@ -776,7 +782,12 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
             // sample's selection.
             const RowParts body = row_parts(row, m);
             float4 first[kAdmitU];
-            if (threadIdx.x - (threadIdx.x & (kWave - 1)) < body.n4) admit_load(first, body, threadIdx.x);
+            float4 (&first_short)[kAdmitUShort] = *reinterpret_cast<float4 (*)[kAdmitUShort]>(first);
+            const bool short_row = m <= kAdmitShortRow;
+            if (threadIdx.x - (threadIdx.x & (kWave - 1)) < body.n4) {
+                if (short_row) admit_load(first_short, body, threadIdx.x);
+                else admit_load(first, body, threadIdx.x);
+            }
             // The sample's selection synchronises through LDS only, so the
             // first group stays in flight meanwhile.
             lds_barrier();
@@ -785,7 +796,12 @@ __global__ __launch_bounds__(kRadixThreads) void radix_select_kernel(RadixArgs a
             // words >= est: j to j + j/4 of the sample (the search stops at
             // the first digit whose bin is that small)
             const uint64_t est = ec.thr << ec.shift;
-            append_at_least(row, m, wm, est, cand, &sh.ncand, kRadixCand, first);
+            if (short_row) {
+                append_at_least<kAdmitUShort>(row, m, wm, est, cand, &sh.ncand, kRadixCand,
+                                              first_short);
+            } else {
+                append_at_least<kAdmitU>(row, m, wm, est, cand, &sh.ncand, kRadixCand, first);
+            }
             __syncthreads();
             const uint32_t nc = sh.ncand;
             if (nc >= k && nc <= (uint32_t)kRadixCand) {
