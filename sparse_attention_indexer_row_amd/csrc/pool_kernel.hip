@@ -84,12 +84,16 @@ __global__ __launch_bounds__(kPoolThreads) void block_max_kernel(PoolArgs a) {
 }
 
 // Blocks of 8 on 16-byte aligned rows (n % 4 == 0): every lane reads one
-// float4, so a wave's load instruction covers 1 KiB of the row, with eight
-// nontemporal loads in flight per thread (the scores are read once; 4 and
-// 16 loads, or 512 threads, measured slower); the two lanes holding a
-// block's halves combine their maxima with one shuffle, and the even lane
+// float4, so a wave's load instruction covers 1 KiB of the row, with two
+// nontemporal loads per thread (the scores are read once); a workgroup
+// covers 8 KiB and the chip keeps many small workgroups in flight.  On 128
+// rows of 1M scores the block-max pass plus selection took 147.9 us with
+// eight loads per thread, 143.9 with four, 139.8 with two and 152.9 with
+// one: fewer loads outstanding per compute unit read faster, down to the
+// point where the workgroups' fixed costs take over.  The two lanes holding
+// a block's halves combine their maxima with one shuffle, and the even lane
 // writes.  Work item f is the row's f-th float4; block b = f / 2.
-constexpr int kPool8Unroll = 8;
+constexpr int kPool8Unroll = 2;
 
 __global__ __launch_bounds__(kPoolThreads) void block_max8_kernel(PoolArgs a) {
     const int64_t r = (int64_t)a.row0 + blockIdx.y;
