@@ -252,15 +252,16 @@ __device__ __forceinline__ uint32_t admit_block(uint64_t *tray, uint32_t cnt, ui
         const uint32_t g0 = vbase + (uint32_t)u * 256u + lane * 4u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const bool pre = v[u][c] >= tb;
-            if (__ballot(pre) == 0ull) continue;
+            const uint64_t pm = __ballot(v[u][c] >= tb);
+            if (pm == 0ull) continue;
             const uint32_t g = g0 + (uint32_t)c;
             uint64_t w = pack_word(order_key((uint32_t)v[u][c]), g - off0);
             if constexpr (RAGGED) w = ((g >= off0) & (g < vend)) ? w : 0ull;
-            const bool pass = pre & (w > T);
-            const uint64_t mk = __ballot(pass);
+            // The masks are combined in scalar registers (a ballot of a
+            // combined lane predicate would go through a vector register).
+            const uint64_t mk = pm & __ballot(w > T);
             if (mk != 0ull) {
-                if (pass) {
+                if ((mk >> lane) & 1ull) {
                     tray[cnt + mbcnt64(mk)] = w;
                     kmx = max(kmx, (uint32_t)(w >> 32));
                 }
