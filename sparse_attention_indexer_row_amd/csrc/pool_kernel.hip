@@ -196,8 +196,9 @@ constexpr int kRadixBins = 2048;
 constexpr int kRadixLevels = 6;
 
 // LDS capacities: SEL winners (>= k) and CAND candidates.  Lists up to
-// 2,048 take 72 KiB (two workgroups per compute unit); lists up to 8,192
-// take 158 KiB, the most one workgroup may have.
+// 2,048 take 72 KiB; lists up to 8,192 take 158 KiB, the most one
+// workgroup may have.  (The smaller size's LDS would admit two workgroups
+// per compute unit, but the kernel's register count admits one.)
 template <int SEL, int CAND>
 struct RadixCap {
     static constexpr int kSel = SEL;

@@ -11,10 +11,10 @@
 // Mapping to CDNA4:
 //   * One workgroup is one selection stream over its share of a row, run by
 //     two kinds of waves.  Streamer waves only read, test and compact: each
-//     walks its own blocks of the shuffled order with four 1 KiB dwordx4
-//     loads per 4 KiB block, several blocks in flight (the order does not
-//     depend on the data, so future addresses are known), and appends
-//     survivors to a double-buffered tray in LDS.  When a tray passes the
+//     takes the next block of the workgroup's share of the shuffled order
+//     from an LDS counter whenever one of its two load slots frees up (four
+//     1 KiB dwordx4 loads per 4 KiB block), and appends survivors to a
+//     double-buffered tray in LDS.  When a tray passes the
 //     watermark the streamer publishes it and keeps streaming into the other
 //     buffer.  One sorter wave owns the candidate pool (in LDS).  It folds
 //     each published tray in, keeps a key histogram whose bound raises the
@@ -36,10 +36,13 @@
 //     back into its workgroup's threshold (any stale value is still a lower
 //     bound of the row's k-th word, so it is safe; the streams themselves make
 //     no device-scope access).  Each sorter writes its kept list to the
-//     workspace and takes an atomic ticket; the last to arrive merges all
-//     lists, writes the row and resets the row's ticket and threshold words
-//     to zero (an accumulator that is never reset is the failure the
-//     kernelbench.com "DeepSeek V4.1 Flash" Kimi-Linear paragraph describes).
+//     workspace and takes an atomic ticket of its group of eight; the last
+//     of a group merges the group's lists (with all its waves, in a tree,
+//     when there are five or more), and the last group's leader merges the
+//     groups' lists, writes the row and resets the row's ticket and
+//     threshold words to zero (an accumulator that is never reset is the
+//     failure the kernelbench.com "DeepSeek V4.1 Flash" Kimi-Linear
+//     paragraph describes).
 #include "common.h"
 #include "select_args.h"
 #include "wave_sort.h"
