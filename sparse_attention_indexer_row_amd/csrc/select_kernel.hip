@@ -381,6 +381,36 @@ __device__ __forceinline__ void skip_fixed_bits(int &top, uint64_t &fmask, uint6
     }
 }
 
+// Bitwise OR over the wave (uniform).
+__device__ __forceinline__ uint64_t wave_or64(uint64_t v, uint32_t lane) {
+    v |= xor_lane64<32>(v, lane);
+    v |= xor_lane64<16>(v, lane);
+    v |= xor_lane64<8>(v, lane);
+    v |= xor_lane64<4>(v, lane);
+    v |= xor_lane64<2>(v, lane);
+    v |= xor_lane64<1>(v, lane);
+    return uniform64(v);
+}
+
+// After a digit pass that left more than one word in the chosen bin: `top`
+// is the bit below that digit, and any1 / any0 are the ORs of the words the
+// pass counted and of their complements.  Every bit below the digit on which
+// those words agree is fixed at once (the bin's words agree there too), so
+// the next digit starts at the highest bit where two of them differ.  Rows
+// whose scores sit on a few levels (ties filled by positions) otherwise spend
+// passes on bits that every candidate shares.
+__device__ __forceinline__ void skip_common_bits(int &top, uint64_t &fmask, uint64_t &prefix,
+                                                 uint64_t any1, uint64_t any0) {
+    const uint64_t below = (2ull << top) - 1ull;   // top <= 62 here
+    const uint64_t diff = any1 & any0 & below;
+    if (diff == 0ull) return;   // not reached: a bin of distinct words differs somewhere
+    const int nt = 63 - __clzll(diff);
+    const uint64_t ones = below & ~((2ull << nt) - 1ull);
+    fmask |= ones;
+    prefix |= any1 & ones;
+    top = nt;
+}
+
 template <int N>
 __device__ __forceinline__ void count_digits(const uint64_t (&a)[N], uint64_t fmask,
                                              uint64_t prefix, int low, uint32_t dmask,
@@ -1235,13 +1265,15 @@ __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_
 // min(k, n) of the n candidates >= lo go to `fin` (unordered).  Rows of 64
 // candidate words are dealt to the waves in turn.  The k-th best is found by
 // the same most-significant-digit radix selection as select_rth, with one
-// shared LDS histogram per digit pass (three in rotation, so a single
-// barrier per pass separates counting from reading), then a 64-word sort of
+// shared LDS histogram and one pair of ORs per digit pass (three of each in
+// rotation, so a single barrier per pass separates counting from reading),
+// then a 64-word sort of
 // the words in the final digit's bin.  `hi` bounds every candidate from
 // above, so the first pass counts all n of them.  Returns n in every wave.
 struct EndShared {
     uint32_t gcnt;    // words gathered for the last digit
     uint32_t out;     // words written to fin
+    uint64_t any[3][2];   // per digit pass: OR of the counted words, OR of their complements
 };
 
 struct Candidates {
@@ -1319,8 +1351,8 @@ __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo,
                                                uint32_t *hist3,
                                                uint64_t *gath, uint64_t *fin, uint32_t w,
                                                uint32_t NW, bool zeroer, uint32_t lane) {
-    // The counters in *sh and hist3[0] are zero and the candidates final
-    // (the caller's barrier).
+    // The counters in *sh, sh->any[0] and hist3[0] are zero and the
+    // candidates final (the caller's barrier).
     uint32_t n = 0;
     // With at most k candidate slots (pool words plus busy trays' words),
     // every candidate at or above lo is kept: the counting pass is skipped
@@ -1340,15 +1372,26 @@ __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo,
             uint32_t *hz = hist3 + 256u * ((pass + 1u) % 3u);
             const int low = top >= 7 ? top - 7 : 0;
             const uint32_t dmask = (2u << (top - low)) - 1u;
+            uint64_t *any = sh->any[pass % 3u];
             if (zeroer) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) hz[lane * 4 + j] = 0u;
+                if (lane < 2u) sh->any[(pass + 1u) % 3u][lane] = 0ull;
             }
+            uint64_t any1 = 0ull, any0 = 0ull;
             for_my_rows(c, w, NW, lane, [&](uint64_t x) __attribute__((always_inline)) {
                 if (x >= lo && (x & fmask) == prefix && x != 0ull) {
                     atomicAdd(&h[(uint32_t)(x >> low) & dmask], 1u);
+                    any1 |= x;
+                    any0 |= ~x;
                 }
             });
+            any1 = wave_or64(any1, lane);
+            any0 = wave_or64(any0, lane);
+            if (lane == 0 && (any1 | any0) != 0ull) {
+                __hip_atomic_fetch_or(&any[0], any1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_or(&any[1], any0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
             lds_barrier();
             uint32_t hb[4];
 #pragma unroll
@@ -1382,6 +1425,7 @@ __device__ __forceinline__ uint32_t end_select(const Candidates &c, uint64_t lo,
             fmask |= (uint64_t)dmask << low;
             if (bin_cnt <= (uint32_t)kWave) break;
             top = low - 1;
+            skip_common_bits(top, fmask, prefix, lds_load_word(&any[0]), lds_load_word(&any[1]));
         }
         if (n > k) {
             // Words above the final bin are kept (k - r of them); the bin's
@@ -1840,6 +1884,8 @@ __global__ __launch_bounds__(Cfg<E>::kMaxThreads) void select_kernel(SelectArgs 
             s_pc = ss.pc;
             s_end.gcnt = 0u;
             s_end.out = 0u;
+            s_end.any[0][0] = 0ull;
+            s_end.any[0][1] = 0ull;
             s_hi = ((uint64_t)kx << 32) | 0xFFFFFFFFull;
         }
 #pragma unroll
