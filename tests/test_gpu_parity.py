@@ -144,6 +144,26 @@ def test_ties_across_segments(opts):
         check(x, k, what=f"ties across segments k={k}", **opts)
 
 
+@pytest.mark.parametrize("opts", [dict(), dict(split=1), dict(split=4), dict(split=1, flags=1)],
+                         ids=lambda o: "-".join(f"{k}{v}" for k, v in o.items()) or "default")
+def test_candidates_sharing_bit_runs(opts):
+    # Candidate words that agree on long runs of bits: values on coarse grids
+    # (only a few mantissa bits vary, the rest are zero in every word), with
+    # the k-th value tied hundreds or thousands of times, so the end-of-pass
+    # selection skips the shared bits on its way to the positions.  One row
+    # mixes two exponents, one has a small top tie group holding the k-th
+    # word, one is all negative.
+    g = np.random.default_rng(31)
+    n = 300_000
+    x = np.empty((4, n), dtype=np.float32)
+    x[0] = (g.integers(0, 8, n) / 4 + 1).astype(np.float32)
+    x[1] = np.ldexp(1 + g.integers(0, 4, n) / 4, g.integers(0, 2, n)).astype(np.float32)
+    x[2] = np.where(g.random(n) < 0.002, np.float32(3.0), g.integers(0, 2, n).astype(np.float32))
+    x[3] = (-0.5 * g.integers(0, 16, n)).astype(np.float32)
+    for k in (512, 1024):
+        check(x, k, what=f"shared bit runs k={k}", **opts)
+
+
 def test_denormals_and_extremes():
     g = np.random.default_rng(10)
     b = g.integers(0, 1 << 23, size=(3, 20_000), dtype=np.uint32)
