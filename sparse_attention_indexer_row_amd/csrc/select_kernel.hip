@@ -1267,9 +1267,9 @@ __device__ __forceinline__ void collect(SorterState &ss, uint64_t *pool, uint64_
 // the same most-significant-digit radix selection as select_rth, with one
 // shared LDS histogram and one pair of ORs per digit pass (three of each in
 // rotation, so a single barrier per pass separates counting from reading),
-// then a 64-word sort of
-// the words in the final digit's bin.  `hi` bounds every candidate from
-// above, so the first pass counts all n of them.  Returns n in every wave.
+// then a 64-word sort of the words in the final digit's bin.  `hi` bounds
+// every candidate from above, so the first pass counts all n of them.
+// Returns n in every wave.
 struct EndShared {
     uint32_t gcnt;    // words gathered for the last digit
     uint32_t out;     // words written to fin
